@@ -1,0 +1,198 @@
+/*
+ * poetx.h - C ABI of libpoetx.so: the POET-X reparameterized linear layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (zhichai.net digest of arXiv:2603.05500, sections
+ * "1. 输入中心化架构", "2. 块随机正交变换", "3. Cayley-Neumann 参数化优化"):
+ *
+ *   z = P^T (W0^T (R^T x)),  R = Psi^T Diag(G_1..G_ceil(m/b)) Psi,
+ *                            P = Phi^T Diag(H_1..H_ceil(n/b)) Phi,
+ *   G_j = (I + Q_j)(I + Q_j + Q_j^2 + Q_j^3),  Q_j skew, stored as its packed
+ *   strict upper triangle (b(b-1)/2 floats per block).
+ *
+ * Row form used throughout: a batch X (T tokens x m features, row-major) maps
+ * to Z = X R W0 P (T x n). W0 is m x n and frozen; only the packed q_R, q_P
+ * are trained. Psi[i, perm_r[i]] = 1, i.e. (X Psi^T)[:, i] = X[:, perm_r[i]].
+ * Block j covers permuted indices [j*b, min((j+1)*b, dim)); only the last
+ * block can be shorter. Block j's packed parameters start at j*b(b-1)/2 and
+ * list Q_j[i][l], i < l, in row-major order (Q_j[l][i] = -Q_j[i][l]).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is a device pointer owned by the caller (hipMalloc or a
+ *    torch CUDA tensor). The library allocates no device memory and keeps no
+ *    state between calls apart from the optional timing log below; scratch
+ *    memory is the caller's workspace `ws`.
+ *  - Everything is asynchronous and stream-ordered on `stream`; no entry point
+ *    synchronises the host. Inputs are read-only unless stated otherwise.
+ *  - Arguments are validated before any launch: on any error nothing is
+ *    launched and no output is touched. POETX_EHIP reports a failed launch.
+ *  - Element types: `act_dtype` (x, z, dz, dx, saved activations, the CNP
+ *    block buffers) is POETX_F32 or POETX_BF16. `w_dtype` is POETX_F32 with
+ *    F32 activations, POETX_BF16 or POETX_I8 with BF16 activations (I8 = int8
+ *    weight with one float scale per output column: W0[r][c] = s[c] * q[r][c],
+ *    the quantised-base-weight variant POET-XQ of section "POET-XQ").
+ *  - Shapes: m, n, b_r, b_p multiples of 8; 8 <= b <= 1024; T >= 0.
+ *  - Permutations must be permutations of [0, dim). Out-of-range entries are
+ *    not reported, but every index is clamped, so a bad permutation gives
+ *    wrong values, never an access outside the buffers.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define POETX_API __attribute__((visibility("default")))
+#else
+#define POETX_API
+#endif
+
+#define POETX_ABI_VERSION 1
+
+enum {
+  POETX_OK = 0,
+  POETX_EINVAL = 1,        /* bad pointer, shape, dtype or size */
+  POETX_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+  POETX_EHIP = 3,          /* a HIP launch failed */
+  POETX_EWORKSPACE = 4     /* ws_bytes smaller than poetx_workspace_bytes() */
+};
+
+enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 };
+
+enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 };
+
+enum {
+  POETX_OP_CNP_BUILD = 0,
+  POETX_OP_WEIGHT_PREPARE = 1,
+  POETX_OP_FORWARD = 2,
+  POETX_OP_BACKWARD = 3,
+  POETX_OP_MERGE = 4
+};
+
+typedef struct poetx_layer {
+  int64_t m;          /* input features (rows of W0) */
+  int64_t n;          /* output features (columns of W0) */
+  int32_t b_r;        /* block size of R: ceil(m / b_r) blocks */
+  int32_t b_p;        /* block size of P: ceil(n / b_p) blocks */
+  int32_t act_dtype;  /* POETX_F32 or POETX_BF16 */
+  int32_t w_dtype;    /* POETX_F32, POETX_BF16 or POETX_I8 (see above) */
+} poetx_layer;
+
+/* Version of this ABI (POETX_ABI_VERSION). */
+POETX_API int poetx_abi_version(void);
+
+/* Static message for a status code; never NULL. */
+POETX_API const char* poetx_strerror(int status);
+
+/* Number of packed float parameters of one side: sum over its blocks of
+ * r(r-1)/2 (section "3. Cayley-Neumann 参数化优化"). 0 for an invalid layer. */
+POETX_API size_t poetx_packed_len(const poetx_layer* L, int side);
+
+/* Bytes of one side's CNP block buffer (output of poetx_cnp_build): two
+ * planes of nblk x b x b elements of act_dtype. Plane 0 holds G_j - I
+ * row-major, plane 1 holds (G_j - I)^T row-major; for a short last block of
+ * size r, entries with a row or column >= r are zero. 0 for an invalid layer. */
+POETX_API size_t poetx_gbuf_bytes(const poetx_layer* L, int side);
+
+/* Bytes of the activations poetx_forward saves for poetx_backward:
+ * X1 = X Psi^T (T x m) followed by Y1 = X R W0 Phi^T (T x n), act_dtype,
+ * row-major. */
+POETX_API size_t poetx_saved_bytes(const poetx_layer* L, int64_t T);
+
+/* Bytes of permuted-frame weight (each of wp and wpt in poetx_weight_prepare):
+ * m x n elements of w_dtype. */
+POETX_API size_t poetx_wbuf_bytes(const poetx_layer* L);
+
+/* Workspace bytes an operation needs for T tokens (T ignored by CNP build,
+ * weight preparation and merge). 0 means none. */
+POETX_API size_t poetx_workspace_bytes(const poetx_layer* L, int64_t T, int op);
+
+/* CNP build (section "3. Cayley-Neumann 参数化优化": G = (I+Q)(I+Q+Q^2+Q^3),
+ * every higher term formed from Q and Q^2).
+ *   q_r [poetx_packed_len(L, R)] float, q_p likewise: packed skew parameters.
+ *   g_r, g_p: CNP block buffers (poetx_gbuf_bytes), overwritten.
+ * Either side may be skipped by passing NULL for both its q and g. */
+POETX_API int poetx_cnp_build(const poetx_layer* L, const float* q_r, const float* q_p,
+                    void* g_r, void* g_p, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Permuted-frame base weight: wp = Psi W0 Phi^T (wp[i][c] =
+ * w0[perm_r[i]][perm_p[c]], m x n) and wpt = its transpose (n x m), both in
+ * w_dtype; for I8 also wscale_p[c] = w_scale[perm_p[c]] (n floats; w_scale
+ * and wscale_p are ignored otherwise and may be NULL). This is the weight
+ * poetx_forward (wpt) and poetx_backward (wp) consume; rebuild it whenever W0
+ * or a permutation changes (after poetx_merge and resampling). */
+POETX_API int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_scale,
+                         const int32_t* perm_r, const int32_t* perm_p,
+                         void* wp, void* wpt, float* wscale_p,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Forward, input-centric (section "1. 输入中心化架构"): Z = X R W0 P without
+ * forming R W0 P.
+ *   x [T][m], act_dtype. z [T][n], act_dtype, overwritten.
+ *   g_r, g_p: CNP block buffers from poetx_cnp_build.
+ *   wpt: permuted-frame transposed weight from poetx_weight_prepare;
+ *   wscale_p: its permuted scales (I8 only, else ignored).
+ *   saved: poetx_saved_bytes(L, T) bytes, overwritten with X1 and Y1.
+ * T == 0 launches nothing. */
+POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
+                  const int32_t* perm_r, const int32_t* perm_p,
+                  const void* g_r, const void* g_p,
+                  const void* wpt, const float* wscale_p,
+                  void* z, void* saved, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* Backward of L = <dz, z> for the forward that wrote `saved`:
+ *   dq_r, dq_p: packed gradients (float, poetx_packed_len), overwritten.
+ *   dx [T][m], act_dtype, overwritten.
+ *   q_r, q_p: the packed parameters the CNP buffers were built from.
+ *   wp: permuted-frame weight from poetx_weight_prepare (m x n).
+ * No W0 gradient exists (W0 is frozen). Outputs are overwritten, not
+ * accumulated; T == 0 writes zero gradients. */
+POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const void* dz,
+                   const int32_t* perm_r, const int32_t* perm_p,
+                   const float* q_r, const float* q_p,
+                   const void* g_r, const void* g_p,
+                   const void* wp, const float* wscale_p,
+                   float* dq_r, float* dq_p, void* dx,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Merge (section "代码与部署", merge_if_needed): W0 <- R W0 P with the current
+ * permutations and blocks, then q_r, q_p <- 0.
+ *   wp: poetx_weight_prepare's wp for the current W0 and permutations.
+ *   w0 [m][n], w_dtype: overwritten with R W0 P (original frame).
+ * The caller then resamples the permutations (the function no longer depends
+ * on them once q = 0) and calls poetx_weight_prepare again.
+ * POETX_I8 weights return POETX_EUNSUPPORTED. */
+POETX_API int poetx_merge(const poetx_layer* L, const void* wp,
+                const int32_t* perm_r, const int32_t* perm_p,
+                const void* g_r, const void* g_p,
+                void* w0, float* q_r, float* q_p,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Kernel timing log (tracing). poetx_profile_enable(1) clears the log and
+ * starts recording: from then on every step of every entry point (e.g.
+ * "gemm_dense_fwd", "apply_p_bwd", "grad_h", "cnp_build_r") is bracketed by a
+ * pair of HIP events recorded on the caller's stream. poetx_profile_enable(0)
+ * stops recording (the log is kept). The log is process-wide and guarded by a
+ * mutex; it is the only state the library keeps between calls. */
+POETX_API int poetx_profile_enable(int enable);
+
+/* Number of steps recorded since the last poetx_profile_enable call. */
+POETX_API int poetx_profile_count(void);
+
+/* Name (static string) and elapsed milliseconds of recorded step i; waits
+ * for that step's stop event. POETX_EINVAL for i out of range. */
+POETX_API int poetx_profile_get(int i, const char** name, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

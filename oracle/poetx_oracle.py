@@ -39,7 +39,7 @@ __all__ = [
     "project_to_packed", "cnp", "cnp_adjoint", "cnp_blocks", "gather_cols",
     "scatter_cols", "block_diag_right", "block_diag_left", "permutation_matrix",
     "dense_block_orthogonal", "dequantize", "permuted_weight", "forward",
-    "backward", "merge", "weight_centric_forward", "inner",
+    "backward", "backward_blocks", "merge", "weight_centric_forward", "inner",
 ]
 
 
@@ -275,6 +275,46 @@ def backward(X, dZ, W0, q_r, q_p, perm_r, perm_p, b_r, b_p):
     dq_p = _packed_grad(q_p, n, b_p, dH)
     return dict(dq_r=dq_r, dq_p=dq_p, dX=dX, dG=dG, dH=dH, dY2=dY2, dY1=dY1,
                 dX2=dX2, dX1=dX1, fwd=f)
+
+
+def backward_blocks(X, dZ, W0, q_r, q_p, perm_r, perm_p, b_r, b_p, blocks_r, blocks_p):
+    """Packed gradients of chosen blocks only, for sizes where backward() is
+    too costly. Same steps as backward(), restricted to the needed columns:
+    dH_k = Y1_K^T dY2_K with Y1_K = X3 W0[:, perm_p[K]], and
+    dG_j = X1_J^T dX2_J with dX2_J = dY W0[perm_r[J], :]^T.
+    Returns ({j: dq_r block j}, {k: dq_p block k})."""
+    X = np.asarray(X, dtype=np.float64)
+    dZ = np.asarray(dZ, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    perm_r, perm_p = np.asarray(perm_r), np.asarray(perm_p)
+    m, n = W0.shape
+    offs_r, sizes_r = packed_offsets(m, b_r)
+    offs_p, sizes_p = packed_offsets(n, b_p)
+    G = cnp_blocks(q_r, m, b_r)
+    H = cnp_blocks(q_p, n, b_p)
+    q_r = np.asarray(q_r, np.float64)
+    q_p = np.asarray(q_p, np.float64)
+    X1 = gather_cols(X, perm_r)
+    dY2 = gather_cols(dZ, perm_p)
+    out_p = {}
+    if len(blocks_p):
+        X3 = scatter_cols(block_diag_right(X1, G, b_r), perm_r)
+        for k in blocks_p:
+            s, r = k * b_p, sizes_p[k]
+            Y1K = X3 @ W0[:, perm_p[s:s + r]]
+            dHk = Y1K.T @ dY2[:, s:s + r]
+            Q = skew_from_packed(q_p[offs_p[k]:offs_p[k] + r * (r - 1) // 2], r)
+            out_p[k] = project_to_packed(cnp_adjoint(Q, dHk))
+    out_r = {}
+    if len(blocks_r):
+        dY = scatter_cols(block_diag_right(dY2, [Hk.T for Hk in H], b_p), perm_p)
+        for j in blocks_r:
+            s, r = j * b_r, sizes_r[j]
+            dX2J = dY @ W0[perm_r[s:s + r], :].T
+            dGj = X1[:, s:s + r].T @ dX2J
+            Q = skew_from_packed(q_r[offs_r[j]:offs_r[j] + r * (r - 1) // 2], r)
+            out_r[j] = project_to_packed(cnp_adjoint(Q, dGj))
+    return out_r, out_p
 
 
 def _packed_grad(q, dim, b, dblocks):

@@ -1,0 +1,310 @@
+// Bandwidth kernels around the matrix products: column permutations of
+// row-major matrices (full rows staged in LDS, so both the HBM reads and the
+// HBM writes are 16-byte coalesced and only the permuted accesses hit LDS),
+// transposes, the element-wise steps of the Cayley-Neumann map and its
+// adjoint, and fixed-order reductions of split-K partial sums.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace poetx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kRowLdsBudget = 64 * 1024;     // bytes of rows staged per workgroup
+constexpr int64_t kRowLdsMax = 64 * 1024;        // wider rows use the direct kernel
+
+template <typename T> struct Pack8;
+template <> struct Pack8<uint8_t> { typedef uint2 type; };
+template <> struct Pack8<uint16_t> { typedef uint4 type; };
+
+__device__ __forceinline__ uint2 pack8(const uint8_t (&v)[8]) {
+  return make_uint2(v[0] | (v[1] << 8) | (v[2] << 16) | (static_cast<uint32_t>(v[3]) << 24),
+                    v[4] | (v[5] << 8) | (v[6] << 16) | (static_cast<uint32_t>(v[7]) << 24));
+}
+__device__ __forceinline__ uint4 pack8(const uint16_t (&v)[8]) {
+  return make_uint4(v[0] | (static_cast<uint32_t>(v[1]) << 16), v[2] | (static_cast<uint32_t>(v[3]) << 16),
+                    v[4] | (static_cast<uint32_t>(v[5]) << 16), v[6] | (static_cast<uint32_t>(v[7]) << 16));
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const T (&v)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    reinterpret_cast<uint4*>(p)[0] = make_uint4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<uint4*>(p)[1] = make_uint4(v[4], v[5], v[6], v[7]);
+  } else {
+    *reinterpret_cast<typename Pack8<T>::type*>(p) = pack8(v);
+  }
+}
+
+// Column gather with whole rows staged in LDS. Workgroup w handles rows
+// [w*rows_per_wg, ...). Phase 1 copies those rows into LDS with 16-byte
+// (8-byte for byte rows not a multiple of 16) loads; phase 2 writes 8 output
+// elements per lane and row, reading the permuted sources from LDS.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+k_gather_cols_lds(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
+                  T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
+                  const int32_t* __restrict__ cidx, int ncols, int64_t nrows, int rows_per_wg, int chunk) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  T* lds = reinterpret_cast<T*>(lds_raw);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int nr = static_cast<int>(min(static_cast<int64_t>(rows_per_wg), nrows - r0));
+  const int64_t row_bytes = static_cast<int64_t>(ncols) * sizeof(T);
+  const int cpr = static_cast<int>(row_bytes / chunk);
+  for (int c = threadIdx.x; c < nr * cpr; c += kThreads) {
+    const int rr = c / cpr, cc = c % cpr;
+    const int64_t gr = r0 + rr;
+    const int64_t src = rmap_in ? clamp_index(rmap_in[gr], nrows) : gr;
+    const char* sp = reinterpret_cast<const char*>(in + src * ld_in) + static_cast<int64_t>(cc) * chunk;
+    char* dp = lds_raw + rr * row_bytes + static_cast<int64_t>(cc) * chunk;
+    if (chunk == 16)
+      *reinterpret_cast<uint4*>(dp) = *reinterpret_cast<const uint4*>(sp);
+    else
+      *reinterpret_cast<uint2*>(dp) = *reinterpret_cast<const uint2*>(sp);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < ncols / 8; c += kThreads) {
+    const int4 i0 = reinterpret_cast<const int4*>(cidx)[2 * c];
+    const int4 i1 = reinterpret_cast<const int4*>(cidx)[2 * c + 1];
+    const int idx[8] = {clamp_index(i0.x, ncols), clamp_index(i0.y, ncols), clamp_index(i0.z, ncols),
+                        clamp_index(i0.w, ncols), clamp_index(i1.x, ncols), clamp_index(i1.y, ncols),
+                        clamp_index(i1.z, ncols), clamp_index(i1.w, ncols)};
+    for (int rr = 0; rr < nr; ++rr) {
+      T v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = lds[static_cast<int64_t>(rr) * ncols + idx[e]];
+      const int64_t gr = r0 + rr;
+      const int64_t dst = rmap_out ? clamp_index(rmap_out[gr], nrows) : gr;
+      store8(out + dst * ld_out + static_cast<int64_t>(c) * 8, v);
+    }
+  }
+}
+
+// Fallback for rows wider than LDS: the gather reads global memory directly.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+k_gather_cols_direct(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
+                     T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
+                     const int32_t* __restrict__ cidx, int64_t ncols, int64_t nrows) {
+  const int64_t r = blockIdx.y;
+  const int64_t src = rmap_in ? clamp_index(rmap_in[r], nrows) : r;
+  const int64_t dst = rmap_out ? clamp_index(rmap_out[r], nrows) : r;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < ncols;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    out[dst * ld_out + i] = in[src * ld_in + clamp_index(cidx[i], ncols)];
+}
+
+__global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __restrict__ inv, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
+}
+
+__global__ void k_gather_f32(const float* __restrict__ in, const int32_t* __restrict__ idx, float* __restrict__ out,
+                             int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) out[i] = in[clamp_index(idx[i], n)];
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) k_transpose(const T* __restrict__ in, T* __restrict__ out, int64_t rows,
+                                                       int64_t cols) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = in[r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) out[c * rows + r] = tile[tx][i];
+  }
+}
+
+__global__ void k_fill_zero(float* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// packed index of (i, l), i < l, in a block of size r
+__device__ __forceinline__ int64_t tri_index(int i, int l, int r) {
+  return static_cast<int64_t>(i) * r - static_cast<int64_t>(i) * (i + 1) / 2 + (l - i - 1);
+}
+
+__global__ void k_unpack_skew(const float* __restrict__ q, int64_t dim, int b, float* __restrict__ Qf,
+                              uint16_t* __restrict__ Qh) {
+  const int z = blockIdx.y;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= static_cast<int64_t>(b) * b) return;
+  const int i = static_cast<int>(e / b), l = static_cast<int>(e % b);
+  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(z) * b));
+  const float* qz = q + static_cast<int64_t>(z) * (static_cast<int64_t>(b) * (b - 1) / 2);
+  float v = 0.f;
+  if (i < r && l < r) {
+    if (i < l) v = qz[tri_index(i, l, r)];
+    else if (i > l) v = -qz[tri_index(l, i, r)];
+  }
+  const int64_t o = static_cast<int64_t>(z) * b * b + e;
+  Qf[o] = v;
+  if (Qh) Qh[o] = f32_to_bf16(v);
+}
+
+__global__ void k_cnp_mid(const float* __restrict__ Qf, const float* __restrict__ Q2f, uint16_t* __restrict__ Sh,
+                          float* __restrict__ Sf, int64_t n) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= n) return;
+  const float s = 2.f * Qf[e] + Q2f[e];
+  if (Sh) Sh[e] = f32_to_bf16(s);
+  if (Sf) Sf[e] = s;
+}
+
+template <typename TG>
+__global__ void __launch_bounds__(kThreads) k_cnp_finish(const float* __restrict__ Qf, const float* __restrict__ Q2f,
+                                                         const float* __restrict__ Tf, int b, int nblk,
+                                                         TG* __restrict__ gbuf) {
+  __shared__ float tile[32][33];
+  const int z = blockIdx.z;
+  const int i0 = blockIdx.y * 32, l0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 8 rows of 32
+  const int64_t bb = static_cast<int64_t>(b) * b;
+  const int64_t base = static_cast<int64_t>(z) * bb;
+  TG* plane0 = gbuf + base;
+  TG* plane1 = gbuf + static_cast<int64_t>(nblk) * bb + base;
+  for (int k = ty; k < 32; k += 8) {
+    const int i = i0 + k, l = l0 + tx;
+    if (i < b && l < b) {
+      const int64_t o = base + static_cast<int64_t>(i) * b + l;
+      const float g = 2.f * Qf[o] + 2.f * Q2f[o] + Tf[o];
+      tile[k][tx] = g;
+      store_from_f32(plane0 + static_cast<int64_t>(i) * b + l, g);
+    }
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int l = l0 + k, i = i0 + tx;  // plane1[l][i] = G[i][l]
+    if (i < b && l < b) store_from_f32(plane1 + static_cast<int64_t>(l) * b + i, tile[tx][k]);
+  }
+}
+
+__global__ void k_cnp_bwd_pack(const float* __restrict__ U, const float* __restrict__ W1,
+                               const float* __restrict__ W2, const float* __restrict__ W3, int64_t dim, int b,
+                               float* __restrict__ dq) {
+  const int z = blockIdx.y;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= static_cast<int64_t>(b) * b) return;
+  const int i = static_cast<int>(e / b), l = static_cast<int>(e % b);
+  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(z) * b));
+  if (!(i < l && l < r)) return;
+  const int64_t base = static_cast<int64_t>(z) * b * b;
+  const int64_t a = base + static_cast<int64_t>(i) * b + l, t = base + static_cast<int64_t>(l) * b + i;
+  const float dqa = 2.f * U[a] - 2.f * W1[a] + 2.f * W2[a] - W3[a];
+  const float dqt = 2.f * U[t] - 2.f * W1[t] + 2.f * W2[t] - W3[t];
+  dq[static_cast<int64_t>(z) * (static_cast<int64_t>(b) * (b - 1) / 2) + tri_index(i, l, r)] = dqa - dqt;
+}
+
+__global__ void k_reduce_splits(const float* __restrict__ part, int nsplit, int64_t n, float* __restrict__ out,
+                                uint16_t* __restrict__ out_h) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < nsplit; ++k) s += part[static_cast<int64_t>(k) * n + e];
+  out[e] = s;
+  if (out_h) out_h[e] = f32_to_bf16(s);
+}
+
+inline unsigned grid1(int64_t n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
+
+template <typename T>
+void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
+                   const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, hipStream_t s) {
+  const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
+  if (row_bytes <= kRowLdsMax) {
+    int rows = static_cast<int>(kRowLdsBudget / row_bytes);
+    rows = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
+    const int chunk = (row_bytes % 16 == 0) ? 16 : 8;
+    const unsigned nwg = static_cast<unsigned>((nrows + rows - 1) / rows);
+    hipLaunchKernelGGL(k_gather_cols_lds<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(rows * row_bytes), s,
+                       static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
+                       static_cast<int>(ncols), nrows, rows, chunk);
+  } else {
+    const unsigned gx = static_cast<unsigned>(std::min<int64_t>((ncols + kThreads - 1) / kThreads, 1024));
+    hipLaunchKernelGGL(k_gather_cols_direct<T>, dim3(gx, static_cast<unsigned>(nrows)), dim3(kThreads), 0, s,
+                       static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
+                       ncols, nrows);
+  }
+}
+
+}  // namespace
+
+bool gather_cols(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
+                 const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, int esize,
+                 hipStream_t s) {
+  if (nrows <= 0 || ncols <= 0) return true;
+  if (ncols % 8 != 0) return false;
+  switch (esize) {
+    case 1: launch_gather<uint8_t>(in, ld_in, rmap_in, out, ld_out, rmap_out, cidx, ncols, nrows, s); return true;
+    case 2: launch_gather<uint16_t>(in, ld_in, rmap_in, out, ld_out, rmap_out, cidx, ncols, nrows, s); return true;
+    case 4: launch_gather<uint32_t>(in, ld_in, rmap_in, out, ld_out, rmap_out, cidx, ncols, nrows, s); return true;
+    default: return false;
+  }
+}
+
+void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_inverse_perm, dim3(grid1(n)), dim3(kThreads), 0, s, perm, inv, n);
+}
+
+void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_gather_f32, dim3(grid1(n)), dim3(kThreads), 0, s, in, idx, out, n);
+}
+
+bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return true;
+  const dim3 g(static_cast<unsigned>((cols + 63) / 64), static_cast<unsigned>((rows + 63) / 64));
+  switch (esize) {
+    case 1: hipLaunchKernelGGL(k_transpose<uint8_t>, g, dim3(kThreads), 0, s, static_cast<const uint8_t*>(in),
+                               static_cast<uint8_t*>(out), rows, cols); return true;
+    case 2: hipLaunchKernelGGL(k_transpose<uint16_t>, g, dim3(kThreads), 0, s, static_cast<const uint16_t*>(in),
+                               static_cast<uint16_t*>(out), rows, cols); return true;
+    case 4: hipLaunchKernelGGL(k_transpose<uint32_t>, g, dim3(kThreads), 0, s, static_cast<const uint32_t*>(in),
+                               static_cast<uint32_t*>(out), rows, cols); return true;
+    default: return false;
+  }
+}
+
+void fill_zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_fill_zero, dim3(grid1(n)), dim3(kThreads), 0, s, p, n);
+}
+
+void unpack_skew(const float* q, int64_t dim, int b, int nblk, float* Qf, uint16_t* Qh, hipStream_t s) {
+  hipLaunchKernelGGL(k_unpack_skew, dim3(grid1(static_cast<int64_t>(b) * b), nblk), dim3(kThreads), 0, s, q, dim, b,
+                     Qf, Qh);
+}
+
+void cnp_mid(const float* Qf, const float* Q2f, uint16_t* Sh, float* Sf, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_cnp_mid, dim3(grid1(n)), dim3(kThreads), 0, s, Qf, Q2f, Sh, Sf, n);
+}
+
+void cnp_finish(const float* Qf, const float* Q2f, const float* Tf, int b, int nblk, void* gbuf, bool bf16,
+                hipStream_t s) {
+  const unsigned t = static_cast<unsigned>((b + 31) / 32);
+  const dim3 g(t, t, static_cast<unsigned>(nblk));
+  if (bf16)
+    hipLaunchKernelGGL(k_cnp_finish<uint16_t>, g, dim3(kThreads), 0, s, Qf, Q2f, Tf, b, nblk,
+                       static_cast<uint16_t*>(gbuf));
+  else
+    hipLaunchKernelGGL(k_cnp_finish<float>, g, dim3(kThreads), 0, s, Qf, Q2f, Tf, b, nblk,
+                       static_cast<float*>(gbuf));
+}
+
+void cnp_bwd_pack(const float* U, const float* W1, const float* W2, const float* W3, int64_t dim, int b, int nblk,
+                  float* dq, hipStream_t s) {
+  hipLaunchKernelGGL(k_cnp_bwd_pack, dim3(grid1(static_cast<int64_t>(b) * b), nblk), dim3(kThreads), 0, s, U, W1, W2,
+                     W3, dim, b, dq);
+}
+
+void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t s) {
+  hipLaunchKernelGGL(k_reduce_splits, dim3(grid1(n)), dim3(kThreads), 0, s, part, nsplit, n, out, out_h);
+}
+
+}  // namespace poetx

@@ -1,0 +1,756 @@
+// C ABI of libpoetx.so (include/poetx.h): argument validation, workspace
+// layout and the kernel sequence of each entry point.
+//
+// Data flow (row form Z = X R W0 P, R = Psi^T Diag(G) Psi, P = Phi^T Diag(H)
+// Phi; zhichai.net digest of arXiv:2603.05500, sections "1. 输入中心化架构" and
+// "2. 块随机正交变换"). Activations stay token-major; everything between the
+// boundary tensors lives in the permuted frames, where every diagonal block is
+// a contiguous run of b columns:
+//   forward   X1 = X[:, perm_r]            column gather (saved)
+//             X2 = X1 + X1 (G - I)         batched block product, MFMA
+//             Y1 = X2 Wp, Wp = Psi W0 Phi^T dense product, MFMA (saved)
+//             Y2 = Y1 + Y1 (H - I)         batched block product
+//             Z  = Y2 scattered by perm_p  column gather with perm_p^-1
+//   backward  dY2 = dZ[:, perm_p]; dY1 = dY2 H^T; dH = sum_t Y1^T dY2
+//             dX2 = dY1 Wp^T; dX1 = dX2 G^T; dG = sum_t X1^T dX2
+//             dX = dX1 scattered by perm_r; dq = skew-packed CNP adjoint of dG, dH
+// Because Wp already carries both permutations, the two dense products need
+// no gather at all.
+#include "../../include/poetx.h"
+#include "common.hpp"
+#include "gemm.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+#include <initializer_list>
+#include <mutex>
+#include <vector>
+
+using namespace poetx;
+
+namespace {
+
+struct Side {
+  int64_t dim;
+  int b;
+  int nblk;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// every pointer non-null and 16-byte aligned
+bool ptrs_ok(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return false;
+  return true;
+}
+
+bool layer_ok(const poetx_layer* L) {
+  if (!L) return false;
+  if (L->m < 8 || L->n < 8 || L->m % 8 || L->n % 8) return false;
+  if (L->m > (1 << 24) || L->n > (1 << 24)) return false;
+  for (int b : {L->b_r, L->b_p})
+    if (b < 8 || b > 1024 || b % 8) return false;
+  if (L->act_dtype == POETX_F32) return L->w_dtype == POETX_F32;
+  if (L->act_dtype == POETX_BF16) {
+    if (L->w_dtype == POETX_BF16) return true;
+    if (L->w_dtype == POETX_I8) return L->m % 16 == 0 && L->n % 16 == 0;
+  }
+  return false;
+}
+
+Side side_of(const poetx_layer* L, int side) {
+  Side s;
+  s.dim = side == POETX_SIDE_R ? L->m : L->n;
+  s.b = side == POETX_SIDE_R ? L->b_r : L->b_p;
+  s.nblk = static_cast<int>((s.dim + s.b - 1) / s.b);
+  return s;
+}
+
+bool is_bf16(const poetx_layer* L) { return L->act_dtype == POETX_BF16; }
+int act_size(const poetx_layer* L) { return is_bf16(L) ? 2 : 4; }
+int w_size(const poetx_layer* L) { return L->w_dtype == POETX_F32 ? 4 : (L->w_dtype == POETX_BF16 ? 2 : 1); }
+int64_t block_elems(const Side& s) { return static_cast<int64_t>(s.nblk) * s.b * s.b; }
+int64_t packed_len(const Side& s) {
+  const int64_t last = s.dim - static_cast<int64_t>(s.nblk - 1) * s.b;
+  return static_cast<int64_t>(s.nblk - 1) * (static_cast<int64_t>(s.b) * (s.b - 1) / 2) + last * (last - 1) / 2;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+  template <typename T>
+  T* take(int64_t count, size_t esize = sizeof(T)) {
+    const size_t o = off;
+    off = (off + static_cast<size_t>(count) * esize + 255) & ~static_cast<size_t>(255);
+    return base ? reinterpret_cast<T*>(base + o) : nullptr;
+  }
+};
+
+// Split of a token reduction over T so that about `target` workgroups run.
+struct Split {
+  int nsplit;
+  int kchunk;
+};
+
+Split token_split(const poetx_layer* L, const Side& s, int64_t T) {
+  int tiles;
+  if (is_bf16(L)) {
+    const int t = s.b >= 256 ? 256 : 128;
+    tiles = ((s.b + t - 1) / t) * ((s.b + t - 1) / t);
+  } else {
+    tiles = ((s.b + 63) / 64) * ((s.b + 63) / 64);
+  }
+  const int64_t target = 512;
+  int64_t ns = (target + static_cast<int64_t>(s.nblk) * tiles - 1) / (static_cast<int64_t>(s.nblk) * tiles);
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::max<int64_t>(1, T / 256)));
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, 65535 / s.nblk));
+  int64_t kchunk = (T + ns - 1) / ns;
+  kchunk = std::max<int64_t>(64, (kchunk + 63) / 64 * 64);
+  Split r;
+  r.kchunk = static_cast<int>(kchunk);
+  r.nsplit = static_cast<int>(std::max<int64_t>(1, (T + kchunk - 1) / kchunk));
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// workspace plans (a null base only measures)
+// ---------------------------------------------------------------------------
+
+struct CnpWs {
+  float *Qf, *Q2f, *Tf, *Sf;
+  uint16_t *Qh, *Q2h, *Sh;
+};
+
+CnpWs plan_cnp(const poetx_layer* L, const Side& s, Carve& c) {
+  const int64_t bb = block_elems(s);
+  CnpWs w{};
+  w.Qf = c.take<float>(bb);
+  w.Q2f = c.take<float>(bb);
+  w.Tf = c.take<float>(bb);
+  if (is_bf16(L)) {
+    w.Qh = c.take<uint16_t>(bb);
+    w.Q2h = c.take<uint16_t>(bb);
+    w.Sh = c.take<uint16_t>(bb);
+  } else {
+    w.Sf = c.take<float>(bb);
+  }
+  return w;
+}
+
+struct CnpBwdWs {
+  float *Qf, *Q2f, *U, *W1, *UQ2, *W2, *W3;
+  uint16_t *Qh, *Q2h, *Uh, *W1h, *UQ2h, *W2h;
+};
+
+CnpBwdWs plan_cnp_bwd(const poetx_layer* L, const Side& s, Carve& c) {
+  const int64_t bb = block_elems(s);
+  CnpBwdWs w{};
+  w.Qf = c.take<float>(bb);
+  w.Q2f = c.take<float>(bb);
+  w.U = c.take<float>(bb);
+  w.W1 = c.take<float>(bb);
+  w.UQ2 = c.take<float>(bb);
+  w.W2 = c.take<float>(bb);
+  w.W3 = c.take<float>(bb);
+  if (is_bf16(L)) {
+    w.Qh = c.take<uint16_t>(bb);
+    w.Q2h = c.take<uint16_t>(bb);
+    w.Uh = c.take<uint16_t>(bb);
+    w.W1h = c.take<uint16_t>(bb);
+    w.UQ2h = c.take<uint16_t>(bb);
+    w.W2h = c.take<uint16_t>(bb);
+  }
+  return w;
+}
+
+struct FwdWs {
+  void* buf;
+  int32_t* inv_p;
+};
+
+FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
+  FwdWs w;
+  w.buf = c.take<char>(T * std::max(L->m, L->n) * act_size(L));
+  w.inv_p = c.take<int32_t>(L->n);
+  return w;
+}
+
+struct BwdWs {
+  void *bufA, *bufB;
+  int32_t* inv_r;
+  float* part;
+  size_t cnp_off;  // the CNP adjoint scratch starts here
+};
+
+BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
+  BwdWs w;
+  const int64_t rowmax = std::max(L->m, L->n);
+  w.bufA = c.take<char>(T * rowmax * act_size(L));
+  w.bufB = c.take<char>(T * rowmax * act_size(L));
+  w.inv_r = c.take<int32_t>(L->m);
+  int64_t part = 0;
+  for (int sd : {POETX_SIDE_R, POETX_SIDE_P}) {
+    const Side s = side_of(L, sd);
+    part = std::max<int64_t>(part, static_cast<int64_t>(token_split(L, s, std::max<int64_t>(T, 1)).nsplit) *
+                                       block_elems(s));
+  }
+  w.part = c.take<float>(part);
+  w.cnp_off = c.off;
+  size_t cnp = 0;
+  for (int sd : {POETX_SIDE_R, POETX_SIDE_P}) {
+    Carve m(nullptr);
+    plan_cnp_bwd(L, side_of(L, sd), m);
+    cnp = std::max(cnp, m.off);
+  }
+  c.off += cnp;
+  return w;
+}
+
+struct MergeWs {
+  void *C1, *C2;
+  int32_t* inv_p;
+};
+
+MergeWs plan_merge(const poetx_layer* L, Carve& c) {
+  MergeWs w;
+  w.C1 = c.take<char>(L->m * L->n * w_size(L));
+  w.C2 = c.take<char>(L->m * L->n * w_size(L));
+  w.inv_p = c.take<int32_t>(L->n);
+  return w;
+}
+
+size_t cnp_build_bytes(const poetx_layer* L) {
+  size_t r = 0;
+  for (int sd : {POETX_SIDE_R, POETX_SIDE_P}) {
+    Carve m(nullptr);
+    plan_cnp(L, side_of(L, sd), m);
+    r = std::max(r, m.off);
+  }
+  return r;
+}
+
+size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
+  Carve c(nullptr);
+  switch (op) {
+    case POETX_OP_CNP_BUILD: return cnp_build_bytes(L);
+    case POETX_OP_WEIGHT_PREPARE: return 0;
+    case POETX_OP_FORWARD: plan_fwd(L, T, c); return c.off;
+    case POETX_OP_BACKWARD: plan_bwd(L, T, c); return c.off;
+    case POETX_OP_MERGE: plan_merge(L, c); return c.off;
+    default: return 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// optional kernel timing log (poetx_profile_*): HIP events around each step
+// ---------------------------------------------------------------------------
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  bool on = false;
+  hipStream_t st;
+  ProfRec rec{};
+  ProfScope(const char* name, hipStream_t s) : st(s) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!g_prof_on) return;
+    rec.name = name;
+    rec.start = prof_event();
+    rec.stop = prof_event();
+    if (!rec.start || !rec.stop) return;
+    on = hipEventRecord(rec.start, st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (hipEventRecord(rec.stop, st) == hipSuccess) g_prof.push_back(rec);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// building blocks
+// ---------------------------------------------------------------------------
+
+bool gemm(const poetx_layer* L, const GemmDesc& d, int am, int bm, int ct, hipStream_t st) {
+  if (is_bf16(L)) return gemm_bf16(d, am, bm, ct, st);
+  return gemm_f32(d, am, bm, st);
+}
+
+// Planes of a CNP block buffer: 0 = G - I row-major, 1 = (G - I)^T row-major.
+const void* plane(const poetx_layer* L, const void* g, const Side& s, int p) {
+  return static_cast<const char*>(g) + static_cast<int64_t>(p) * block_elems(s) * act_size(L);
+}
+
+// out[:, blocks] = in + in (G - I)^{T or not} for every diagonal block
+// (plane 1 gives in G, plane 0 gives in G^T), optional per-column scale.
+bool block_apply(const poetx_layer* L, const Side& s, int64_t T, const void* in, void* out, const void* gbuf,
+                 int p, const float* colscale, hipStream_t st) {
+  GemmDesc d;
+  d.A = in;
+  d.lda = s.dim;
+  d.sA = s.b;
+  d.B = plane(L, gbuf, s, p);
+  d.ldb = s.b;
+  d.sB = static_cast<int64_t>(s.b) * s.b;
+  d.R = in;
+  d.ldr = s.dim;
+  d.sR = s.b;
+  d.C = out;
+  d.ldc = s.dim;
+  d.sC = s.b;
+  d.scale = colscale;
+  d.sScale = s.b;
+  d.M = static_cast<int>(T);
+  d.N = d.K = s.b;
+  d.batch = s.nblk;
+  d.ragged_dim = static_cast<int>(s.dim);
+  d.ragged_blk = s.b;
+  d.ragged_mask = 2 | 4;
+  return gemm(L, d, A_KCONTIG, B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
+}
+
+// part[s][z] = sum over the tokens of split s of A_z^T dO_z (b x b per block)
+bool block_token_grad(const poetx_layer* L, const Side& s, int64_t T, const void* act, const void* dout,
+                      float* part, const Split& sp, hipStream_t st) {
+  GemmDesc d;
+  d.A = act;
+  d.lda = s.dim;
+  d.sA = s.b;
+  d.B = dout;
+  d.ldb = s.dim;
+  d.sB = s.b;
+  d.C = part;
+  d.ldc = s.b;
+  d.sC = static_cast<int64_t>(s.b) * s.b;
+  d.sCsplit = block_elems(s);
+  d.M = d.N = s.b;
+  d.K = static_cast<int>(T);
+  d.batch = s.nblk;
+  d.ksplit = sp.nsplit;
+  d.kchunk = sp.kchunk;
+  d.ragged_dim = static_cast<int>(s.dim);
+  d.ragged_blk = s.b;
+  d.ragged_mask = 1 | 2;
+  d.store_full = 1;
+  return gemm(L, d, A_MCONTIG, B_NCONTIG, C_F32, st);
+}
+
+// Batched b x b product C = alpha A B^T-form (see gemm.hpp) with optional
+// addend and bf16 copy, over the nblk blocks of one side.
+bool sq(const poetx_layer* L, const Side& s, const void* A, int am, const void* B, int bm, float* C, uint16_t* C2,
+        float alpha, const float* D, hipStream_t st) {
+  GemmDesc d;
+  const int64_t bb = static_cast<int64_t>(s.b) * s.b;
+  d.A = A;
+  d.lda = s.b;
+  d.sA = bb;
+  d.B = B;
+  d.ldb = s.b;
+  d.sB = bb;
+  d.C = C;
+  d.ldc = s.b;
+  d.sC = bb;
+  d.C2 = C2;
+  d.ldc2 = s.b;
+  d.sC2 = bb;
+  d.D = D;
+  d.ldd = s.b;
+  d.sD = bb;
+  d.beta = D ? 1.f : 0.f;
+  d.alpha = alpha;
+  d.M = d.N = d.K = s.b;
+  d.batch = s.nblk;
+  return gemm(L, d, am, bm, C_F32, st);
+}
+
+// G - I for every block of one side: Q2 = Q Q, S = 2Q + Q2, T = S Q2,
+// G - I = 2Q + 2Q2 + T  (= (I+Q)(I+Q+Q^2+Q^3) - I with every higher term
+// formed from Q and Q^2, section "3. Cayley-Neumann 参数化优化").
+bool cnp_side(const poetx_layer* L, const Side& s, const float* q, void* gbuf, void* ws, hipStream_t st) {
+  Carve c(ws);
+  CnpWs w = plan_cnp(L, s, c);
+  const bool bf = is_bf16(L);
+  unpack_skew(q, s.dim, s.b, s.nblk, w.Qf, bf ? w.Qh : nullptr, st);
+  const void* Qop = bf ? static_cast<const void*>(w.Qh) : w.Qf;
+  // Q Q = -Q Q^T: the NT product with B = Q and alpha = -1 (Q skew)
+  if (!sq(L, s, Qop, A_KCONTIG, Qop, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st)) return false;
+  cnp_mid(w.Qf, w.Q2f, bf ? w.Sh : nullptr, bf ? nullptr : w.Sf, block_elems(s), st);
+  // S Q2 with Q2 symmetric: B rows = Q2 rows
+  const void* Sop = bf ? static_cast<const void*>(w.Sh) : w.Sf;
+  const void* Q2op = bf ? static_cast<const void*>(w.Q2h) : w.Q2f;
+  if (!sq(L, s, Sop, A_KCONTIG, Q2op, B_KCONTIG, w.Tf, nullptr, 1.f, nullptr, st)) return false;
+  cnp_finish(w.Qf, w.Q2f, w.Tf, s.b, s.nblk, gbuf, bf, st);
+  return true;
+}
+
+// dq from dG = U for one side. With Q skew, the adjoint of
+// G = (I+Q)(I+Q+Q^2+Q^3) collapses to sums of Q^a U Q^c whose coefficient
+// depends on a + c only: dL/dQ = 2U - 2 W1 + 2 W2 - W3 with
+// W1 = QU + UQ, W2 = Q W1 + U Q^2, W3 = Q W2 + (U Q^2) Q; then
+// dq_k = dL/dQ[i][l] - dL/dQ[l][i].
+bool cnp_bwd_side(const poetx_layer* L, const Side& s, const float* q, const float* part, const Split& sp,
+                  float* dq, void* cnp_ws, hipStream_t st) {
+  Carve c(cnp_ws);
+  CnpBwdWs w = plan_cnp_bwd(L, s, c);
+  const bool bf = is_bf16(L);
+  reduce_splits(part, sp.nsplit, block_elems(s), w.U, bf ? w.Uh : nullptr, st);
+  unpack_skew(q, s.dim, s.b, s.nblk, w.Qf, bf ? w.Qh : nullptr, st);
+  const void* Q = bf ? static_cast<const void*>(w.Qh) : w.Qf;
+  const void* U = bf ? static_cast<const void*>(w.Uh) : w.U;
+  bool ok = sq(L, s, Q, A_KCONTIG, Q, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st);
+  const void* Q2 = bf ? static_cast<const void*>(w.Q2h) : w.Q2f;
+  // W1 = Q U + U Q
+  ok = ok && sq(L, s, Q, A_KCONTIG, U, B_NCONTIG, w.W1, nullptr, 1.f, nullptr, st);
+  ok = ok && sq(L, s, U, A_KCONTIG, Q, B_KCONTIG, w.W1, bf ? w.W1h : nullptr, -1.f, w.W1, st);
+  const void* W1 = bf ? static_cast<const void*>(w.W1h) : w.W1;
+  // U Q2 (Q2 symmetric)
+  ok = ok && sq(L, s, U, A_KCONTIG, Q2, B_KCONTIG, w.UQ2, bf ? w.UQ2h : nullptr, 1.f, nullptr, st);
+  const void* UQ2 = bf ? static_cast<const void*>(w.UQ2h) : w.UQ2;
+  // W2 = Q W1 + U Q2
+  ok = ok && sq(L, s, Q, A_KCONTIG, W1, B_NCONTIG, w.W2, bf ? w.W2h : nullptr, 1.f, w.UQ2, st);
+  const void* W2 = bf ? static_cast<const void*>(w.W2h) : w.W2;
+  // W3 = Q W2 + (U Q2) Q
+  ok = ok && sq(L, s, Q, A_KCONTIG, W2, B_NCONTIG, w.W3, nullptr, 1.f, nullptr, st);
+  ok = ok && sq(L, s, UQ2, A_KCONTIG, Q, B_KCONTIG, w.W3, nullptr, -1.f, w.W3, st);
+  if (!ok) return false;
+  cnp_bwd_pack(w.U, w.W1, w.W2, w.W3, s.dim, s.b, s.nblk, dq, st);
+  return true;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? POETX_OK : POETX_EHIP;
+}
+
+int check_ws(const poetx_layer* L, int64_t T, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(L, T, op);
+  if (need == 0) return POETX_OK;
+  if (ws_bytes < need) return POETX_EWORKSPACE;
+  if (!ws || !aligned16(ws)) return POETX_EINVAL;
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int poetx_abi_version(void) { return POETX_ABI_VERSION; }
+
+const char* poetx_strerror(int status) {
+  switch (status) {
+    case POETX_OK: return "ok";
+    case POETX_EINVAL: return "invalid argument (pointer, alignment, shape, dtype or size)";
+    case POETX_EUNSUPPORTED: return "valid request not supported by this build";
+    case POETX_EHIP: return "HIP kernel launch failed";
+    case POETX_EWORKSPACE: return "workspace smaller than poetx_workspace_bytes()";
+    default: return "unknown status";
+  }
+}
+
+size_t poetx_packed_len(const poetx_layer* L, int side) {
+  if (!layer_ok(L) || (side != POETX_SIDE_R && side != POETX_SIDE_P)) return 0;
+  return static_cast<size_t>(packed_len(side_of(L, side)));
+}
+
+size_t poetx_gbuf_bytes(const poetx_layer* L, int side) {
+  if (!layer_ok(L) || (side != POETX_SIDE_R && side != POETX_SIDE_P)) return 0;
+  return static_cast<size_t>(2 * block_elems(side_of(L, side)) * act_size(L));
+}
+
+size_t poetx_saved_bytes(const poetx_layer* L, int64_t T) {
+  if (!layer_ok(L) || T < 0) return 0;
+  return static_cast<size_t>(T * (L->m + L->n) * act_size(L));
+}
+
+size_t poetx_wbuf_bytes(const poetx_layer* L) {
+  if (!layer_ok(L)) return 0;
+  return static_cast<size_t>(L->m * L->n * w_size(L));
+}
+
+size_t poetx_workspace_bytes(const poetx_layer* L, int64_t T, int op) {
+  if (!layer_ok(L) || T < 0) return 0;
+  return ws_bytes_for(L, T, op);
+}
+
+int poetx_cnp_build(const poetx_layer* L, const float* q_r, const float* q_p, void* g_r, void* g_p, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (!layer_ok(L)) return POETX_EINVAL;
+  if ((q_r == nullptr) != (g_r == nullptr) || (q_p == nullptr) != (g_p == nullptr)) return POETX_EINVAL;
+  for (const void* p : {static_cast<const void*>(q_r), static_cast<const void*>(q_p), static_cast<const void*>(g_r),
+                        static_cast<const void*>(g_p)})
+    if (p && !aligned16(p)) return POETX_EINVAL;
+  if (const int e = check_ws(L, 0, POETX_OP_CNP_BUILD, ws, ws_bytes)) return e;
+  bool ok = true;
+  if (q_r) {
+    ProfScope p("cnp_build_r", stream);
+    ok = ok && cnp_side(L, side_of(L, POETX_SIDE_R), q_r, g_r, ws, stream);
+  }
+  if (q_p) {
+    ProfScope p("cnp_build_p", stream);
+    ok = ok && cnp_side(L, side_of(L, POETX_SIDE_P), q_p, g_p, ws, stream);
+  }
+  if (!ok) return POETX_EUNSUPPORTED;
+  return launch_status();
+}
+
+int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_scale, const int32_t* perm_r,
+                         const int32_t* perm_p, void* wp, void* wpt, float* wscale_p, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!layer_ok(L)) return POETX_EINVAL;
+  if (!ptrs_ok({w0, perm_r, perm_p, wp, wpt})) return POETX_EINVAL;
+  const bool i8 = L->w_dtype == POETX_I8;
+  if (i8 && (!w_scale || !wscale_p)) return POETX_EINVAL;
+  const int es = w_size(L);
+  {
+    ProfScope p("prepare_permute", stream);
+    if (!gather_cols(w0, L->n, perm_r, wp, L->n, nullptr, perm_p, L->n, L->m, es, stream))
+      return POETX_EUNSUPPORTED;
+    if (i8) gather_f32(w_scale, perm_p, wscale_p, L->n, stream);
+  }
+  {
+    ProfScope p("prepare_transpose", stream);
+    if (!transpose(wp, wpt, L->m, L->n, es, stream)) return POETX_EUNSUPPORTED;
+  }
+  return launch_status();
+}
+
+int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r, const int32_t* perm_p,
+                  const void* g_r, const void* g_p, const void* wpt, const float* wscale_p, void* z, void* saved,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (T == 0) return POETX_OK;
+  if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z, saved})) return POETX_EINVAL;
+  const bool i8 = L->w_dtype == POETX_I8;
+  if (i8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (const int e = check_ws(L, T, POETX_OP_FORWARD, ws, ws_bytes)) return e;
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  const int es = act_size(L);
+  Carve c(ws);
+  FwdWs w = plan_fwd(L, T, c);
+  void* X1 = saved;
+  void* Y1 = static_cast<char*>(saved) + T * L->m * es;
+  bool ok;
+  {
+    ProfScope p("gather_x", stream);
+    ok = gather_cols(x, L->m, nullptr, X1, L->m, nullptr, perm_r, L->m, T, es, stream);
+  }
+  {
+    ProfScope p("apply_r_fwd", stream);
+    ok = ok && block_apply(L, R, T, X1, w.buf, g_r, 1, nullptr, stream);
+  }
+  GemmDesc d;
+  d.dense = 1;
+  d.A = w.buf;
+  d.lda = L->m;
+  d.B = wpt;
+  d.ldb = L->m;
+  d.C = Y1;
+  d.ldc = L->n;
+  d.scale = i8 ? wscale_p : nullptr;
+  d.M = static_cast<int>(T);
+  d.N = static_cast<int>(L->n);
+  d.K = static_cast<int>(L->m);
+  {
+    ProfScope p("gemm_dense_fwd", stream);
+    ok = ok && gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, stream);
+  }
+  {
+    ProfScope p("apply_p_fwd", stream);
+    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream);
+  }
+  {
+    ProfScope p("scatter_z", stream);
+    inverse_perm(perm_p, w.inv_p, L->n, stream);
+    ok = ok && gather_cols(w.buf, L->n, nullptr, z, L->n, nullptr, w.inv_p, L->n, T, es, stream);
+  }
+  if (!ok) return POETX_EUNSUPPORTED;
+  return launch_status();
+}
+
+int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const void* dz, const int32_t* perm_r,
+                   const int32_t* perm_p, const float* q_r, const float* q_p, const void* g_r, const void* g_p,
+                   const void* wp, const float* wscale_p, float* dq_r, float* dq_p, void* dx, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (!ptrs_ok({dq_r, dq_p})) return POETX_EINVAL;
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  if (T == 0) {
+    fill_zero_f32(dq_r, packed_len(R), stream);
+    fill_zero_f32(dq_p, packed_len(P), stream);
+    return launch_status();
+  }
+  if (!ptrs_ok({saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, dx})) return POETX_EINVAL;
+  const bool i8 = L->w_dtype == POETX_I8;
+  if (i8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (const int e = check_ws(L, T, POETX_OP_BACKWARD, ws, ws_bytes)) return e;
+  const int es = act_size(L);
+  Carve c(ws);
+  BwdWs w = plan_bwd(L, T, c);
+  void* cnp_ws = static_cast<char*>(ws) + w.cnp_off;
+  const void* X1 = saved;
+  const void* Y1 = static_cast<const char*>(saved) + T * L->m * es;
+
+  // P side: dY2 = dZ Phi^T, dY1 = dY2 H^T (times the column scales for int8
+  // weights, which belong to Wp's columns), dH = sum_t Y1^T dY2
+  bool ok;
+  {
+    ProfScope p("gather_dz", stream);
+    ok = gather_cols(dz, L->n, nullptr, w.bufA, L->n, nullptr, perm_p, L->n, T, es, stream);
+  }
+  {
+    ProfScope p("apply_p_bwd", stream);
+    ok = ok && block_apply(L, P, T, w.bufA, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
+  }
+  const Split spP = token_split(L, P, T);
+  {
+    ProfScope p("grad_h", stream);
+    ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part, spP, stream);
+  }
+  {
+    ProfScope p("cnp_bwd_p", stream);
+    ok = ok && cnp_bwd_side(L, P, q_p, w.part, spP, dq_p, cnp_ws, stream);
+  }
+  // dX2 = dY1 Wp^T
+  GemmDesc d;
+  d.dense = 1;
+  d.A = w.bufB;
+  d.lda = L->n;
+  d.B = wp;
+  d.ldb = L->n;
+  d.C = w.bufA;
+  d.ldc = L->m;
+  d.M = static_cast<int>(T);
+  d.N = static_cast<int>(L->m);
+  d.K = static_cast<int>(L->n);
+  {
+    ProfScope p("gemm_dense_bwd", stream);
+    ok = ok && gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, stream);
+  }
+  // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
+  {
+    ProfScope p("apply_r_bwd", stream);
+    ok = ok && block_apply(L, R, T, w.bufA, w.bufB, g_r, 0, nullptr, stream);
+  }
+  const Split spR = token_split(L, R, T);
+  {
+    ProfScope p("grad_g", stream);
+    ok = ok && block_token_grad(L, R, T, X1, w.bufA, w.part, spR, stream);
+  }
+  {
+    ProfScope p("cnp_bwd_r", stream);
+    ok = ok && cnp_bwd_side(L, R, q_r, w.part, spR, dq_r, cnp_ws, stream);
+  }
+  {
+    ProfScope p("scatter_dx", stream);
+    inverse_perm(perm_r, w.inv_r, L->m, stream);
+    ok = ok && gather_cols(w.bufB, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
+  }
+  if (!ok) return POETX_EUNSUPPORTED;
+  return launch_status();
+}
+
+int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, const int32_t* perm_p, const void* g_r,
+                const void* g_p, void* w0, float* q_r, float* q_p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!layer_ok(L)) return POETX_EINVAL;
+  if (!ptrs_ok({wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p})) return POETX_EINVAL;
+  if (L->w_dtype == POETX_I8) return POETX_EUNSUPPORTED;
+  if (const int e = check_ws(L, 0, POETX_OP_MERGE, ws, ws_bytes)) return e;
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  Carve c(ws);
+  MergeWs w = plan_merge(L, c);
+  // C1 = Diag(G) Wp: row block j gets Wp_j + (G_j - I) Wp_j
+  GemmDesc d;
+  d.A = plane(L, g_r, R, 0);
+  d.lda = R.b;
+  d.sA = static_cast<int64_t>(R.b) * R.b;
+  d.B = wp;
+  d.ldb = L->n;
+  d.sB = static_cast<int64_t>(R.b) * L->n;
+  d.R = wp;
+  d.ldr = L->n;
+  d.sR = static_cast<int64_t>(R.b) * L->n;
+  d.C = w.C1;
+  d.ldc = L->n;
+  d.sC = static_cast<int64_t>(R.b) * L->n;
+  d.M = R.b;
+  d.N = static_cast<int>(L->n);
+  d.K = R.b;
+  d.batch = R.nblk;
+  d.ragged_dim = static_cast<int>(L->m);
+  d.ragged_blk = R.b;
+  d.ragged_mask = 1 | 4;
+  bool ok;
+  {
+    ProfScope p("merge_left", stream);
+    ok = gemm(L, d, A_KCONTIG, B_NCONTIG, is_bf16(L) ? C_BF16 : C_F32, stream);
+  }
+  // C2 = C1 Diag(H)
+  {
+    ProfScope p("merge_right", stream);
+    ok = ok && block_apply(L, P, L->m, w.C1, w.C2, g_p, 1, nullptr, stream);
+  }
+  // W0[perm_r[i]][perm_p[c]] = C2[i][c]
+  {
+    ProfScope p("merge_scatter", stream);
+    inverse_perm(perm_p, w.inv_p, L->n, stream);
+    ok = ok && gather_cols(w.C2, L->n, nullptr, w0, L->n, perm_r, w.inv_p, L->n, L->m, w_size(L), stream);
+    fill_zero_f32(q_r, packed_len(R), stream);
+    fill_zero_f32(q_p, packed_len(P), stream);
+  }
+  if (!ok) return POETX_EUNSUPPORTED;
+  return launch_status();
+}
+
+int poetx_profile_enable(int enable) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (const ProfRec& r : g_prof) {
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof.clear();
+  g_prof_on = enable != 0;
+  return POETX_OK;
+}
+
+int poetx_profile_count(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  return static_cast<int>(g_prof.size());
+}
+
+int poetx_profile_get(int i, const char** name, float* ms) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  if (i < 0 || i >= static_cast<int>(g_prof.size()) || !name || !ms) return POETX_EINVAL;
+  const ProfRec& r = g_prof[static_cast<size_t>(i)];
+  if (hipEventSynchronize(r.stop) != hipSuccess) return POETX_EHIP;
+  float t = 0.f;
+  if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return POETX_EHIP;
+  *name = r.name;
+  *ms = t;
+  return POETX_OK;
+}
+
+}  // extern "C"

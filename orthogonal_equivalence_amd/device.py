@@ -1,0 +1,132 @@
+"""Device-resident POET-X layer state driven through the C ABI.
+
+Holds the torch device buffers one layer needs (base weight, its permuted
+frame, packed parameters, permutations, CNP block buffers, saved activations
+and a workspace sized by poetx_workspace_bytes) and calls the ABI entry points
+in order. It allocates and marshals; all arithmetic runs in libpoetx.so.
+"""
+
+import numpy as np
+import torch
+
+from . import poetx as px
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+
+
+def to_device(arr, kind, device="cuda"):
+    """Host storage array -> device tensor. bf16 arrays are uint16 bit patterns."""
+    arr = np.ascontiguousarray(arr)
+    if kind == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    if kind == "i8":
+        return torch.from_numpy(arr.astype(np.int8)).to(device)
+    if kind == "i32":
+        return torch.from_numpy(arr.astype(np.int32)).to(device)
+    return torch.from_numpy(arr.astype(np.float32)).to(device)
+
+
+def to_host_f64(t):
+    """Device tensor (float32 / bfloat16 / int8) -> float64 numpy array."""
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+class DeviceLayer:
+    """One POET-X layer on one GPU, for up to ``T_max`` tokens per call."""
+
+    def __init__(self, m, n, b_r, b_p, act="bf16", weight="bf16", T_max=0, device="cuda"):
+        self.m, self.n, self.b_r, self.b_p = m, n, b_r, b_p
+        self.act, self.weight, self.device = act, weight, device
+        self.L = px.make_layer(m, n, b_r, b_p, act, weight)
+        if px.poetx_gbuf_bytes(self.L, px.POETX_SIDE_R) == 0:
+            raise ValueError("invalid layer shape or dtypes for libpoetx")
+        dev = device
+        u8 = torch.uint8
+        self.w0 = torch.empty((m, n), dtype=_TORCH[weight], device=dev)
+        self.wp = torch.empty((m, n), dtype=_TORCH[weight], device=dev)
+        self.wpt = torch.empty((n, m), dtype=_TORCH[weight], device=dev)
+        self.w_scale = torch.ones(n, dtype=torch.float32, device=dev) if weight == "i8" else None
+        self.wscale_p = torch.ones(n, dtype=torch.float32, device=dev) if weight == "i8" else None
+        self.perm_r = torch.arange(m, dtype=torch.int32, device=dev)
+        self.perm_p = torch.arange(n, dtype=torch.int32, device=dev)
+        self.q_r = torch.zeros(px.poetx_packed_len(self.L, px.POETX_SIDE_R), dtype=torch.float32, device=dev)
+        self.q_p = torch.zeros(px.poetx_packed_len(self.L, px.POETX_SIDE_P), dtype=torch.float32, device=dev)
+        self.g_r = torch.empty(px.poetx_gbuf_bytes(self.L, px.POETX_SIDE_R), dtype=u8, device=dev)
+        self.g_p = torch.empty(px.poetx_gbuf_bytes(self.L, px.POETX_SIDE_P), dtype=u8, device=dev)
+        self.T_max = 0
+        self.saved = None
+        self.ws = torch.empty(0, dtype=u8, device=dev)
+        self.reserve(T_max)
+
+    # -- buffers --------------------------------------------------------------
+    def reserve(self, T):
+        """Grow the saved-activation buffer and workspace for T tokens."""
+        if T <= self.T_max and self.saved is not None:
+            return
+        self.T_max = max(T, self.T_max)
+        self.saved = torch.empty(max(px.poetx_saved_bytes(self.L, self.T_max), 16), dtype=torch.uint8,
+                                 device=self.device)
+        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(5))
+        if need > self.ws.numel():
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def load(self, layer):
+        """Upload a layer dict from ``synth.make_layer``."""
+        self.w0.copy_(to_device(layer["W0_raw"], self.weight, self.device))
+        if self.weight == "i8":
+            self.w_scale.copy_(to_device(layer["w_scale"], "f32", self.device))
+        self.perm_r.copy_(to_device(layer["perm_r"], "i32", self.device))
+        self.perm_p.copy_(to_device(layer["perm_p"], "i32", self.device))
+        self.q_r.copy_(to_device(layer["q_r"], "f32", self.device))
+        self.q_p.copy_(to_device(layer["q_p"], "f32", self.device))
+
+    def act_tensor(self, rows, cols):
+        return torch.empty((rows, cols), dtype=_TORCH[self.act], device=self.device)
+
+    def saved_views(self, T):
+        es = 4 if self.act == "f32" else 2
+        x1 = self.saved[: T * self.m * es].view(_TORCH[self.act]).view(T, self.m)
+        y1 = self.saved[T * self.m * es: T * (self.m + self.n) * es].view(_TORCH[self.act]).view(T, self.n)
+        return x1, y1
+
+    def g_planes(self, side):
+        g, dim, b = (self.g_r, self.m, self.b_r) if side == px.POETX_SIDE_R else (self.g_p, self.n, self.b_p)
+        nblk = -(-dim // b)
+        return g.view(_TORCH[self.act]).view(2, nblk, b, b)
+
+    # -- hot path ---------------------------------------------------------------
+    def cnp_build(self, stream=None):
+        px.poetx_cnp_build(self.L, self.q_r, self.q_p, self.g_r, self.g_p, self.ws, None, stream)
+
+    def prepare(self, stream=None):
+        px.poetx_weight_prepare(self.L, self.w0, self.w_scale, self.perm_r, self.perm_p, self.wp, self.wpt,
+                                self.wscale_p, self.ws, None, stream)
+
+    def forward(self, x, z=None, stream=None):
+        T = x.shape[0]
+        self.reserve(T)
+        if z is None:
+            z = self.act_tensor(T, self.n)
+        px.poetx_forward(self.L, T, x, self.perm_r, self.perm_p, self.g_r, self.g_p, self.wpt, self.wscale_p,
+                         z, self.saved, self.ws, None, stream)
+        return z
+
+    def backward(self, dz, dq_r=None, dq_p=None, dx=None, stream=None):
+        T = dz.shape[0]
+        if dq_r is None:
+            dq_r = torch.empty_like(self.q_r)
+        if dq_p is None:
+            dq_p = torch.empty_like(self.q_p)
+        if dx is None:
+            dx = self.act_tensor(T, self.m)
+        px.poetx_backward(self.L, T, self.saved, dz, self.perm_r, self.perm_p, self.q_r, self.q_p, self.g_r,
+                          self.g_p, self.wp, self.wscale_p, dq_r, dq_p, dx, self.ws, None, stream)
+        return dq_r, dq_p, dx
+
+    def merge(self, stream=None):
+        px.poetx_merge(self.L, self.wp, self.perm_r, self.perm_p, self.g_r, self.g_p, self.w0, self.q_r,
+                       self.q_p, self.ws, None, stream)

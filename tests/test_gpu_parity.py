@@ -1,0 +1,323 @@
+"""Parity of the HIP path (libpoetx.so through its C ABI) with the float64
+oracle on the same seeded inputs.
+
+Bar: relative Frobenius error ||gpu - ref|| / ||ref|| per output tensor of at
+most 1e-5 for float32 layers and 2e-2 for bfloat16 layers (the tolerances the
+layer's specification states), bit-exact for pure index work (packing of the
+skew parameters, permutations). Full-size workloads are checked on sampled
+outputs: token rows of z and dx (both token-local), whole blocks of dq, and
+the whole merged weight.
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from orthogonal_equivalence_amd import synth  # noqa: E402
+from orthogonal_equivalence_amd import poetx as px  # noqa: E402
+from orthogonal_equivalence_amd.device import DeviceLayer, to_device, to_host_f64  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    torch.cuda.init()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _cfg(name, T, m, n, b_r, b_p, act, weight, cfg_id):
+    return synth.LayerConfig(name, cfg_id, T, m, n, b_r, b_p, act, weight)
+
+
+def _w0_values(cfg, L):
+    if cfg.weight == "i8":
+        return O.dequantize(L["W0_raw"], L["w_scale"])
+    return L["W0"].astype(np.float64)
+
+
+def _run(cfg, seed=0, merge=False):
+    print(f"\n[gpu] {cfg.name} T={cfg.T} m={cfg.m} n={cfg.n} b={cfg.b_r}/{cfg.b_p} "
+          f"{cfg.act}/{cfg.weight} seed={seed}", flush=True)
+    L = synth.make_layer(cfg, seed)
+    A = synth.make_activations(cfg, seed)
+    dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
+    dl.load(L)
+    dl.cnp_build()
+    dl.prepare()
+    x = to_device(A["X_raw"], cfg.act)
+    dz = to_device(A["dZ_raw"], cfg.act)
+    z = dl.forward(x)
+    dq_r, dq_p, dx = dl.backward(dz)
+    x1, y1 = dl.saved_views(cfg.T)
+    out = dict(z=to_host_f64(z), dq_r=to_host_f64(dq_r), dq_p=to_host_f64(dq_p), dx=to_host_f64(dx),
+               x1=to_host_f64(x1), y1=to_host_f64(y1),
+               g_r=to_host_f64(dl.g_planes(px.POETX_SIDE_R)), g_p=to_host_f64(dl.g_planes(px.POETX_SIDE_P)))
+    if merge:
+        dl.merge()
+        out["w0_merged"] = to_host_f64(dl.w0)
+        out["q_after"] = to_host_f64(torch.cat([dl.q_r, dl.q_p]))
+    torch.cuda.synchronize()
+    return L, A, out, dl
+
+
+def _expected_planes(q, dim, b):
+    G = O.cnp_blocks(q, dim, b)
+    nblk = len(G)
+    P = np.zeros((2, nblk, b, b))
+    for j, g in enumerate(G):
+        r = g.shape[0]
+        P[0, j, :r, :r] = g - np.eye(r)
+        P[1, j, :r, :r] = (g - np.eye(r)).T
+    return P
+
+
+# ---------------------------------------------------------------------------
+# full parity on sizes the oracle finishes in seconds
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # the float32 workload itself (256 tokens, 512 x 512, b = 64)
+    synth.CONFIGS["tiny_f32"],
+    # float32 with short last blocks on both sides and a ragged token count
+    _cfg("f32_ragged", 77, 200, 136, 64, 64, "f32", "f32", 20),
+    # bfloat16, several 256-row tiles, ragged T, b = 256
+    _cfg("bf16_multitile", 1000, 768, 1280, 256, 256, "bf16", "bf16", 21),
+    # bfloat16 with short last blocks (640 = 2*256 + 128, 1088 = 4*256 + 64)
+    _cfg("bf16_ragged_blocks", 777, 640, 1088, 256, 256, "bf16", "bf16", 22),
+    # b = 512: four output tiles per block in the token reductions
+    _cfg("bf16_b512", 300, 1024, 1536, 512, 512, "bf16", "bf16", 23),
+    # small blocks and different R / P block sizes
+    _cfg("bf16_b32_b64", 130, 256, 192, 32, 64, "bf16", "bf16", 24),
+    # int8 base weight with per-column scales
+    _cfg("xq_small", 520, 512, 768, 128, 128, "bf16", "i8", 25),
+    # a single token
+    _cfg("bf16_one_token", 1, 256, 512, 128, 128, "bf16", "bf16", 26),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_layer_parity(cfg):
+    L, A, out, _ = _run(cfg, merge=(cfg.weight != "i8"))
+    W0 = _w0_values(cfg, L)
+    args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
+    ref = O.backward(A["X"], A["dZ"], *args)
+    f = ref["fwd"]
+    tol = TOL[cfg.act]
+    errs = {
+        "cnp_r": rel(out["g_r"], _expected_planes(L["q_r"], cfg.m, cfg.b_r)),
+        "cnp_p": rel(out["g_p"], _expected_planes(L["q_p"], cfg.n, cfg.b_p)),
+        "x1": rel(out["x1"], f["X1"]),
+        "y1": rel(out["y1"], f["Y1"]),
+        "z": rel(out["z"], f["Z"]),
+        "dq_r": rel(out["dq_r"], ref["dq_r"]),
+        "dq_p": rel(out["dq_p"], ref["dq_p"]),
+        "dx": rel(out["dx"], ref["dX"]),
+    }
+    if "w0_merged" in out:
+        errs["merge"] = rel(out["w0_merged"], O.merge(*args))
+        assert np.all(out["q_after"] == 0.0)
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+    # X1 is a pure permutation of X: bit-exact
+    assert np.array_equal(out["x1"], A["X"][:, L["perm_r"]].astype(np.float64))
+
+
+def test_merge_preserves_the_layer_function():
+    cfg = _cfg("merge_invariant", 64, 256, 384, 64, 64, "f32", "f32", 27)
+    L, A, out, dl = _run(cfg, merge=True)
+    # after the merge q = 0 and the forward through the merged weight must
+    # reproduce the forward before it
+    dl.cnp_build()
+    dl.prepare()
+    z2 = to_host_f64(dl.forward(to_device(A["X_raw"], cfg.act)))
+    torch.cuda.synchronize()
+    assert rel(z2, out["z"]) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# bit-exact index work
+# ---------------------------------------------------------------------------
+
+def _round_robin(b):
+    """b-1 perfect matchings of {0..b-1} that together cover every pair once."""
+    rounds = []
+    for r in range(b - 1):
+        pairs = [(r, b - 1)]
+        for k in range(1, b // 2):
+            pairs.append(((r + k) % (b - 1), (r - k) % (b - 1)))
+        rounds.append([(min(p), max(p)) for p in pairs])
+    return rounds
+
+
+@pytest.mark.parametrize("act,s", [("f32", 2.0 ** -4), ("bf16", 0.25)])
+def test_packing_bit_exact(act, s):
+    # One perfect matching of nonzero q per block: every Q is a direct sum of
+    # 2 x 2 rotation generators, so G - I has exactly representable entries
+    # diag -2s^2 + s^4 and off-diagonal +-(2s - 2s^3) at the matched pairs.
+    b, nblk = 16, 4
+    m = n = b * nblk
+    dl = DeviceLayer(m, n, b, b, act, act, 8)
+    rounds = _round_robin(b)
+    iu = {p: k for k, p in enumerate(zip(*np.triu_indices(b, 1)))}
+    L = b * (b - 1) // 2
+    seen = set()
+    for call in range(-(-len(rounds) // nblk)):
+        q = np.zeros(nblk * L, np.float32)
+        expect = np.zeros((nblk, b, b))
+        for z in range(nblk):
+            ridx = (call * nblk + z) % len(rounds)
+            for (i, l) in rounds[ridx]:
+                q[z * L + iu[(i, l)]] = s
+                expect[z, i, i] = expect[z, l, l] = -2 * s * s + s ** 4
+                expect[z, i, l] = 2 * s - 2 * s ** 3
+                expect[z, l, i] = -(2 * s - 2 * s ** 3)
+                seen.add((i, l))
+        dl.q_r.copy_(torch.from_numpy(q))
+        dl.q_p.copy_(torch.from_numpy(q))
+        dl.cnp_build()
+        torch.cuda.synchronize()
+        for side in (px.POETX_SIDE_R, px.POETX_SIDE_P):
+            planes = to_host_f64(dl.g_planes(side))
+            assert np.array_equal(planes[0], expect), (call, side)
+            assert np.array_equal(planes[1], expect.transpose(0, 2, 1)), (call, side)
+    assert len(seen) == L
+
+
+def _shift(b, k):
+    S = np.zeros((b, b))
+    S[np.arange(b), (np.arange(b) + k) % b] = 1.0
+    return S
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_permutations_bit_exact(act):
+    # G_j, H_k cyclic shifts (0/1 matrices), W0 = I and small-integer X, dZ:
+    # every value stays a small integer, so z and dx are exact index shuffles
+    # of the inputs and any correct implementation matches bit for bit.
+    b, nblk, T = 16, 4, 40
+    m = n = b * nblk
+    rng = np.random.default_rng(5)
+    perm_r, perm_p = rng.permutation(m), rng.permutation(n)
+    X = rng.integers(-8, 9, size=(T, m)).astype(np.float32)
+    dZ = rng.integers(-8, 9, size=(T, n)).astype(np.float32)
+    Gs = [_shift(b, 1 + j % 3) for j in range(nblk)]
+    Hs = [_shift(b, 2 + k % 5) for k in range(nblk)]
+    dl = DeviceLayer(m, n, b, b, act, act, T)
+    eye = np.eye(m, dtype=np.float32)
+    dl.load(dict(W0_raw=synth.bf16_bits(eye) if act == "bf16" else eye, w_scale=None,
+                 perm_r=perm_r, perm_p=perm_p, q_r=np.zeros(dl.q_r.numel(), np.float32),
+                 q_p=np.zeros(dl.q_p.numel(), np.float32)))
+    for side, blocks in ((px.POETX_SIDE_R, Gs), (px.POETX_SIDE_P, Hs)):
+        D = np.stack([g - np.eye(b) for g in blocks])
+        host = np.stack([D, D.transpose(0, 2, 1)]).astype(np.float32)
+        dev = to_device(synth.bf16_bits(host) if act == "bf16" else host, act)
+        dl.g_planes(side).copy_(dev.view(dl.g_planes(side).shape))
+    dl.prepare()
+    raw = (lambda a: synth.bf16_bits(a)) if act == "bf16" else (lambda a: a)
+    z = to_host_f64(dl.forward(to_device(raw(X), act)))
+    _, _, dx = dl.backward(to_device(raw(dZ), act))
+    dx = to_host_f64(dx)
+    torch.cuda.synchronize()
+    R = O.dense_block_orthogonal(Gs, perm_r, b)
+    P = O.dense_block_orthogonal(Hs, perm_p, b)
+    Weff = R @ np.eye(m) @ P
+    assert np.array_equal(z, X.astype(np.float64) @ Weff)
+    assert np.array_equal(dx, dZ.astype(np.float64) @ Weff.T)
+    # the permuted-frame weight is Psi W0 Phi^T exactly
+    assert np.array_equal(to_host_f64(dl.wp), O.permuted_weight(np.eye(m), perm_r, perm_p))
+    assert np.array_equal(to_host_f64(dl.wpt), O.permuted_weight(np.eye(m), perm_r, perm_p).T)
+
+
+# ---------------------------------------------------------------------------
+# determinism, empty input, token-shard linearity
+# ---------------------------------------------------------------------------
+
+def test_backward_is_deterministic():
+    cfg = _cfg("determinism", 1024, 512, 768, 128, 128, "bf16", "bf16", 28)
+    _, A, out1, dl = _run(cfg)
+    dq_r, dq_p, dx = dl.backward(to_device(A["dZ_raw"], cfg.act))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_f64(dq_r), out1["dq_r"])
+    assert np.array_equal(to_host_f64(dq_p), out1["dq_p"])
+    assert np.array_equal(to_host_f64(dx), out1["dx"])
+
+
+def test_zero_tokens():
+    dl = DeviceLayer(64, 64, 16, 16, "bf16", "bf16", 0)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    z = dl.forward(x)
+    assert z.shape == (0, 64)
+    dq_r = torch.full_like(dl.q_r, 7.0)
+    dq_p = torch.full_like(dl.q_p, 7.0)
+    dl.backward(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), dq_r, dq_p)
+    torch.cuda.synchronize()
+    assert float(dq_r.abs().max()) == 0.0 and float(dq_p.abs().max()) == 0.0
+
+
+def test_token_shard_linearity():
+    # data parallelism exchanges only the packed gradients: the dq of a batch
+    # equals the sum of the dq of its token shards
+    cfg = _cfg("shards", 300, 256, 320, 64, 64, "f32", "f32", 29)
+    L = synth.make_layer(cfg, 0)
+    A = synth.make_activations(cfg, 0)
+    dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, "f32", "f32", cfg.T)
+    dl.load(L)
+    dl.cnp_build()
+    dl.prepare()
+    res = []
+    for sl in (slice(0, 300), slice(0, 120), slice(120, 300)):
+        dl.forward(to_device(A["X_raw"][sl], "f32"))
+        dq_r, dq_p, _ = dl.backward(to_device(A["dZ_raw"][sl], "f32"))
+        res.append((to_host_f64(dq_r), to_host_f64(dq_p)))
+    torch.cuda.synchronize()
+    assert rel(res[1][0] + res[2][0], res[0][0]) <= 1e-5
+    assert rel(res[1][1] + res[2][1], res[0][1]) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+# ---------------------------------------------------------------------------
+
+FULL = ["llama3b_proj", "llama8b_mlp_up", "llama13b_q_proj", "llama13b_down_proj", "xq_llama8b_mlp_up"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = synth.CONFIGS[name]
+    L, A, out, _ = _run(cfg, merge=cfg.merge)
+    W0 = _w0_values(cfg, L)
+    args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(cfg.T, size=16, replace=False))
+    rows[-1] = cfg.T - 1
+    sub = O.backward(A["X"][rows], A["dZ"][rows], *args)
+    nR, nP = -(-cfg.m // cfg.b_r), -(-cfg.n // cfg.b_p)
+    br, bp = [0, nR - 1], [nP // 2]
+    dqr_ref, dqp_ref = O.backward_blocks(A["X"], A["dZ"], *args, br, bp)
+    Lr, Lp = cfg.b_r * (cfg.b_r - 1) // 2, cfg.b_p * (cfg.b_p - 1) // 2
+    errs = {
+        "z_rows": rel(out["z"][rows], sub["fwd"]["Z"]),
+        "dx_rows": rel(out["dx"][rows], sub["dX"]),
+        "y1_rows": rel(out["y1"][rows], sub["fwd"]["Y1"]),
+    }
+    for j in br:
+        errs[f"dq_r[{j}]"] = rel(out["dq_r"][j * Lr:j * Lr + dqr_ref[j].size], dqr_ref[j])
+    for k in bp:
+        errs[f"dq_p[{k}]"] = rel(out["dq_p"][k * Lp:k * Lp + dqp_ref[k].size], dqp_ref[k])
+    if cfg.merge:
+        errs["merge"] = rel(out["w0_merged"], O.merge(*args))
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL[cfg.act]}
+    assert not bad, bad

@@ -322,3 +322,13 @@ def test_packed_len_matches_block_count():
     assert O.packed_len(10, 4) == 6 + 6 + 1
     assert synth.packed_count(10, 4) == O.packed_len(10, 4)
     assert synth.packed_count(14336, 256) == O.packed_len(14336, 256)
+
+
+def test_block_restricted_gradients_agree_with_full_backward():
+    _, L, A = _tiny(12, 7, 16, 24, 8, 8, sigma_q=0.1)
+    args = (L["W0"], L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], 8, 8)
+    full = O.backward(A["X"], A["dZ"], *args)
+    r, p = O.backward_blocks(A["X"], A["dZ"], *args, [0, 1], [2])
+    assert np.allclose(r[0], full["dq_r"][0:28], atol=1e-13)
+    assert np.allclose(r[1], full["dq_r"][28:56], atol=1e-13)
+    assert np.allclose(p[2], full["dq_p"][56:84], atol=1e-13)
