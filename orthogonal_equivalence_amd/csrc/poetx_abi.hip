@@ -727,11 +727,13 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
 
 int poetx_profile_enable(int enable) {
   std::lock_guard<std::mutex> g(g_prof_mu);
-  for (const ProfRec& r : g_prof) {
-    g_prof_pool.push_back(r.start);
-    g_prof_pool.push_back(r.stop);
+  if (enable) {
+    for (const ProfRec& r : g_prof) {
+      g_prof_pool.push_back(r.start);
+      g_prof_pool.push_back(r.stop);
+    }
+    g_prof.clear();
   }
-  g_prof.clear();
   g_prof_on = enable != 0;
   return POETX_OK;
 }

@@ -321,3 +321,18 @@ def test_full_size_sampled(name):
     print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL[cfg.act]}
     assert not bad, bad
+
+
+def test_profile_log_records_every_step():
+    cfg = _cfg("profile", 128, 256, 384, 64, 64, "bf16", "bf16", 30)
+    px.poetx_profile_enable(1)
+    try:
+        _run(cfg)
+    finally:
+        px.poetx_profile_enable(0)
+    names = [px.poetx_profile_get(i)[0] for i in range(px.poetx_profile_count())]
+    for want in ("cnp_build_r", "cnp_build_p", "gather_x", "apply_r_fwd", "gemm_dense_fwd", "apply_p_fwd",
+                 "scatter_z", "gather_dz", "apply_p_bwd", "grad_h", "cnp_bwd_p", "gemm_dense_bwd",
+                 "apply_r_bwd", "grad_g", "cnp_bwd_r", "scatter_dx", "prepare_permute"):
+        assert want in names, want
+    assert all(px.poetx_profile_get(i)[1] >= 0.0 for i in range(len(names)))
