@@ -49,4 +49,10 @@ struct GemmDesc {
 bool gemm_bf16(const GemmDesc& d, int a_mode, int b_mode, int c_type, hipStream_t stream);
 bool gemm_f32(const GemmDesc& d, int a_mode, int b_mode, hipStream_t stream);
 
+// Dense bfloat16 product for the W0 products (gemm_dense.hip): A [M][K] and
+// B [N][K] K-contiguous bfloat16, C bfloat16, optional per-column scale; uses
+// A, lda, B, ldb, C, ldc, scale, M, N, K only. Returns false unless
+// K % 64 == 0 and N % 8 == 0.
+bool gemm_dense_bf16(const GemmDesc& d, hipStream_t stream);
+
 }  // namespace poetx

@@ -1,0 +1,175 @@
+// Dense product C = A B^T (bfloat16 in, float32 accumulate, bfloat16 out) for
+// the layer's two W0 products: Y1 = X2 Wp (B = Wp^T rows) and dX2 = dY1 Wp^T
+// (B = Wp rows). Both operands are K-contiguous.
+//
+// gfx950 design:
+//  * 256 x 256 output tile per workgroup, K in steps of 64, 8 waves (two per
+//    SIMD, so one wave's LDS waits hide behind the other's MFMAs); each wave
+//    owns 128 x 64 outputs as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.
+//  * Operand tiles go global -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging, no LDS write instructions), double-buffered, one barrier per
+//    K step; the next tile's loads are in flight during the current MFMAs.
+//  * LDS rows are 128 bytes, unpadded; 16-byte chunk c of row r sits in slot
+//    c ^ swz(r) with swz(r) = (r & 7) ^ ((r >> 3) & 1), which keeps the
+//    fragment reads (32 rows, same chunk) free of bank conflicts whether the
+//    LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+//  * Output tiles are ordered so that each XCD works on one contiguous band
+//    of tiles (shared A/B panels stay in that XCD's L2).
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace poetx {
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int WM = 2, WN = 4;
+constexpr int NT = 64 * WM * WN;
+constexpr int WTM = BM / WM, WTN = BN / WN;  // 128 x 64 per wave
+constexpr int TM = WTM / 32, TN = WTN / 32;  // 4 x 2 MFMA tiles
+constexpr int kRowBytes = BK * 2;            // 128
+constexpr int kTileBytes = BM * kRowBytes;   // 32 KB per operand and stage
+constexpr int kStageBytes = 2 * kTileBytes;  // A + B
+constexpr int kSlabStride = WTN + 8;         // epilogue slab row, floats
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Direct-to-LDS load of one 256 x 64 bfloat16 operand tile. Wave w fills rows
+// [32w, 32w + 32) with four instructions of 8 rows (1 KB) each; lane l of an
+// instruction lands in LDS slot l % 8 of row l / 8 and fetches the chunk that
+// belongs there. Rows past `rowlim` re-read row rowlim - 1 (in bounds); their
+// products only reach outputs that are never stored.
+__device__ __forceinline__ void load_tile(const bf16_t* __restrict__ g, int64_t ld, int row0, int rowlim, int k0,
+                                          char* lds, int wave, int lane) {
+  const int sub = lane >> 3, slot = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + sub;
+    const int c = slot ^ swz(r);
+    int gr = row0 + r;
+    gr = gr < rowlim ? gr : rowlim - 1;
+    const bf16_t* src = g + static_cast<int64_t>(gr) * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                     (lds_void_t)(lds + (wave * 32 + i * 8) * kRowBytes), 16, 0, 0);
+  }
+}
+
+__global__ void __launch_bounds__(NT) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+
+  constexpr int GM = 8;
+  const int pid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int group = GM * tiles_n;
+  const int first_m = (pid / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % group) % gsz;
+  const int tn = (pid % group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const bf16_t* A = static_cast<const bf16_t*>(d.A);
+  const bf16_t* B = static_cast<const bf16_t*>(d.B);
+  const int nk = d.K / BK;
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // per-lane fragment offsets: row (lane % 32) of a 32-row tile, chunk
+  // 2*kk + lane/32, swizzled; the swizzle only depends on lane % 16
+  const int lrow = lane & 31;
+  const int sw = swz(lrow);
+  int koff[BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) koff[kk] = lrow * kRowBytes + (((2 * kk + (lane >> 5)) ^ sw) << 4);
+  const int abase = wm * WTM * kRowBytes;
+  const int bbase = kTileBytes + wn * WTN * kRowBytes;
+
+  load_tile(A, d.lda, m0, d.M, 0, smem, wave, lane);
+  load_tile(B, d.ldb, n0, d.N, 0, smem + kTileBytes, wave, lane);
+
+  for (int it = 0; it < nk; ++it) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < nk) {
+      char* nxt = smem + ((it + 1) & 1) * kStageBytes;
+      load_tile(A, d.lda, m0, d.M, (it + 1) * BK, nxt, wave, lane);
+      load_tile(B, d.ldb, n0, d.N, (it + 1) * BK, nxt + kTileBytes, wave, lane);
+    }
+    const char* st = smem + (it & 1) * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue through per-wave LDS slabs (32 rows x 64 columns), 16-byte stores
+  bf16_t* C = static_cast<bf16_t*>(d.C);
+  const float* S = d.scale;
+  float* slab = reinterpret_cast<float*>(smem) + wave * 32 * kSlabStride;
+  constexpr int kChunksPerRow = WTN / 8;
+  constexpr int kChunksPerLane = 32 * kChunksPerRow / 64;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kSlabStride + j * 32 + lrow] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kChunksPerLane; ++c) {
+      const int ch = lane + c * 64;
+      const int row = ch / kChunksPerRow, col = (ch % kChunksPerRow) * 8;
+      const int m = m0 + wm * WTM + i * 32 + row;
+      const int n = n0 + wn * WTN + col;
+      if (m < d.M && n < d.N) {
+        const float4 p0 = *reinterpret_cast<const float4*>(slab + row * kSlabStride + col);
+        const float4 p1 = *reinterpret_cast<const float4*>(slab + row * kSlabStride + col + 4);
+        float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        if (S) {
+          const float4 s0 = *reinterpret_cast<const float4*>(S + n);
+          const float4 s1 = *reinterpret_cast<const float4*>(S + n + 4);
+          v[0] *= s0.x; v[1] *= s0.y; v[2] *= s0.z; v[3] *= s0.w;
+          v[4] *= s1.x; v[5] *= s1.y; v[6] *= s1.z; v[7] *= s1.w;
+        }
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * d.ldc + n) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_dense_bf16(const GemmDesc& d, hipStream_t s) {
+  if (d.M <= 0 || d.N <= 0) return true;
+  if (d.K % BK != 0 || d.K <= 0 || d.N % 8 != 0) return false;
+  const int tm = (d.M + BM - 1) / BM, tn = (d.N + BN - 1) / BN;
+  hipLaunchKernelGGL(k_gemm_dense, dim3(tm * tn), dim3(NT), 0, s, d, tm, tn);
+  return true;
+}
+
+}  // namespace poetx

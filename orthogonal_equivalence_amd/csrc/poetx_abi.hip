@@ -298,6 +298,13 @@ bool gemm(const poetx_layer* L, const GemmDesc& d, int am, int bm, int ct, hipSt
   return gemm_f32(d, am, bm, st);
 }
 
+// The dense W0 product: the specialised kernel when its shape constraints
+// hold, else the general engine.
+bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, hipStream_t st) {
+  if (is_bf16(L) && !i8 && d.K % 64 == 0 && d.N % 8 == 0) return gemm_dense_bf16(d, st);
+  return gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
+}
+
 // Planes of a CNP block buffer: 0 = G - I row-major, 1 = (G - I)^T row-major.
 const void* plane(const poetx_layer* L, const void* g, const Side& s, int p) {
   return static_cast<const char*>(g) + static_cast<int64_t>(p) * block_elems(s) * act_size(L);
@@ -576,7 +583,7 @@ int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   d.K = static_cast<int>(L->m);
   {
     ProfScope p("gemm_dense_fwd", stream);
-    ok = ok && gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, stream);
+    ok = ok && dense_product(L, d, i8, stream);
   }
   {
     ProfScope p("apply_p_fwd", stream);
@@ -648,7 +655,7 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   d.K = static_cast<int>(L->n);
   {
     ProfScope p("gemm_dense_bwd", stream);
-    ok = ok && gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, stream);
+    ok = ok && dense_product(L, d, i8, stream);
   }
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {
