@@ -132,14 +132,38 @@ __device__ __forceinline__ int64_t tri_index(int i, int l, int r) {
   return static_cast<int64_t>(i) * r - static_cast<int64_t>(i) * (i + 1) / 2 + (l - i - 1);
 }
 
-__global__ void k_unpack_skew(const float* __restrict__ q, int64_t dim, int b, float* __restrict__ Qf,
-                              uint16_t* __restrict__ Qh) {
+// Blocks [0, seg.n0) come from side 0, the next seg.n1 from side 1 (R and P
+// share one launch when their block sizes match).
+struct Seg2 {
+  const float* q0;
+  const float* q1;
+  int64_t dim0, dim1;
+  int n0;
+};
+
+__device__ __forceinline__ void seg_pick(const Seg2& sg, int z, const float*& q, int64_t& dim, int& zl) {
+  if (z < sg.n0) {
+    q = sg.q0;
+    dim = sg.dim0;
+    zl = z;
+  } else {
+    q = sg.q1;
+    dim = sg.dim1;
+    zl = z - sg.n0;
+  }
+}
+
+__global__ void k_unpack_skew(const Seg2 sg, int b, float* __restrict__ Qf, uint16_t* __restrict__ Qh) {
   const int z = blockIdx.y;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (e >= static_cast<int64_t>(b) * b) return;
+  const float* q;
+  int64_t dim;
+  int zl;
+  seg_pick(sg, z, q, dim, zl);
   const int i = static_cast<int>(e / b), l = static_cast<int>(e % b);
-  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(z) * b));
-  const float* qz = q + static_cast<int64_t>(z) * (static_cast<int64_t>(b) * (b - 1) / 2);
+  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
+  const float* qz = q + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
   float v = 0.f;
   if (i < r && l < r) {
     if (i < l) v = qz[tri_index(i, l, r)];
@@ -161,46 +185,74 @@ __global__ void k_cnp_mid(const float* __restrict__ Qf, const float* __restrict_
 
 template <typename TG>
 __global__ void __launch_bounds__(kThreads) k_cnp_finish(const float* __restrict__ Qf, const float* __restrict__ Q2f,
-                                                         const float* __restrict__ Tf, int b, int nblk,
-                                                         TG* __restrict__ gbuf) {
+                                                         const float* __restrict__ Tf, int b, int n0, int n1,
+                                                         TG* __restrict__ g0, TG* __restrict__ g1) {
   __shared__ float tile[32][33];
   const int z = blockIdx.z;
   const int i0 = blockIdx.y * 32, l0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 8 rows of 32
   const int64_t bb = static_cast<int64_t>(b) * b;
-  const int64_t base = static_cast<int64_t>(z) * bb;
-  TG* plane0 = gbuf + base;
-  TG* plane1 = gbuf + static_cast<int64_t>(nblk) * bb + base;
+  const int64_t src = static_cast<int64_t>(z) * bb;
+  TG* g = z < n0 ? g0 : g1;
+  const int nb = z < n0 ? n0 : n1;
+  const int zl = z < n0 ? z : z - n0;
+  TG* plane0 = g + static_cast<int64_t>(zl) * bb;
+  TG* plane1 = g + static_cast<int64_t>(nb) * bb + static_cast<int64_t>(zl) * bb;
   for (int k = ty; k < 32; k += 8) {
     const int i = i0 + k, l = l0 + tx;
     if (i < b && l < b) {
-      const int64_t o = base + static_cast<int64_t>(i) * b + l;
-      const float g = 2.f * Qf[o] + 2.f * Q2f[o] + Tf[o];
-      tile[k][tx] = g;
-      store_from_f32(plane0 + static_cast<int64_t>(i) * b + l, g);
+      const int64_t o = src + static_cast<int64_t>(i) * b + l;
+      const float v = 2.f * Qf[o] + 2.f * Q2f[o] + Tf[o];
+      tile[k][tx] = v;
+      store_from_f32(plane0 + static_cast<int64_t>(i) * b + l, v);
     }
   }
   __syncthreads();
   for (int k = ty; k < 32; k += 8) {
-    const int l = l0 + k, i = i0 + tx;  // plane1[l][i] = G[i][l]
+    const int l = l0 + k, i = i0 + tx;  // plane1[l][i] = (G - I)[i][l]
     if (i < b && l < b) store_from_f32(plane1 + static_cast<int64_t>(l) * b + i, tile[tx][k]);
   }
 }
 
-__global__ void k_cnp_bwd_pack(const float* __restrict__ U, const float* __restrict__ W1,
-                               const float* __restrict__ W2, const float* __restrict__ W3, int64_t dim, int b,
-                               float* __restrict__ dq) {
-  const int z = blockIdx.y;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= static_cast<int64_t>(b) * b) return;
-  const int i = static_cast<int>(e / b), l = static_cast<int>(e % b);
-  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(z) * b));
-  if (!(i < l && l < r)) return;
+// dq for block z: dQ = 2U - 2W1 + 2W2 - W3 and dq[k(i,l)] = dQ[i][l] - dQ[l][i]
+// for i < l < r. One workgroup per 32 x 32 tile (I, L) with I <= L: the tile
+// and its mirror (L, I) are read row-wise and meet in LDS.
+__global__ void __launch_bounds__(kThreads) k_cnp_bwd_pack(const float* __restrict__ U, const float* __restrict__ W1,
+                                                          const float* __restrict__ W2, const float* __restrict__ W3,
+                                                          const Seg2 sg, float* __restrict__ dq0,
+                                                          float* __restrict__ dq1, int b) {
+  __shared__ float mir[32][33];
+  const int z = blockIdx.z;
+  const int I = blockIdx.y, Lt = blockIdx.x;
+  if (I > Lt) return;
+  const float* q;
+  int64_t dim;
+  int zl;
+  seg_pick(sg, z, q, dim, zl);
+  float* dq = z < sg.n0 ? dq0 : dq1;
+  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
   const int64_t base = static_cast<int64_t>(z) * b * b;
-  const int64_t a = base + static_cast<int64_t>(i) * b + l, t = base + static_cast<int64_t>(l) * b + i;
-  const float dqa = 2.f * U[a] - 2.f * W1[a] + 2.f * W2[a] - W3[a];
-  const float dqt = 2.f * U[t] - 2.f * W1[t] + 2.f * W2[t] - W3[t];
-  dq[static_cast<int64_t>(z) * (static_cast<int64_t>(b) * (b - 1) / 2) + tri_index(i, l, r)] = dqa - dqt;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  // mirror tile rows l in (L*32 ..), columns i in (I*32 ..)
+  for (int k = ty; k < 32; k += 8) {
+    const int l = Lt * 32 + k, i = I * 32 + tx;
+    float v = 0.f;
+    if (l < b && i < b) {
+      const int64_t o = base + static_cast<int64_t>(l) * b + i;
+      v = 2.f * U[o] - 2.f * W1[o] + 2.f * W2[o] - W3[o];
+    }
+    mir[k][tx] = v;
+  }
+  __syncthreads();
+  float* dqz = dq + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
+  for (int k = ty; k < 32; k += 8) {
+    const int i = I * 32 + k, l = Lt * 32 + tx;
+    if (i < l && l < r) {
+      const int64_t o = base + static_cast<int64_t>(i) * b + l;
+      const float a = 2.f * U[o] - 2.f * W1[o] + 2.f * W2[o] - W3[o];
+      dqz[tri_index(i, l, r)] = a - mir[tx][k];
+    }
+  }
 }
 
 __global__ void k_reduce_splits(const float* __restrict__ part, int nsplit, int64_t n, float* __restrict__ out,
@@ -276,8 +328,10 @@ void fill_zero_f32(float* p, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_fill_zero, dim3(grid1(n)), dim3(kThreads), 0, s, p, n);
 }
 
-void unpack_skew(const float* q, int64_t dim, int b, int nblk, float* Qf, uint16_t* Qh, hipStream_t s) {
-  hipLaunchKernelGGL(k_unpack_skew, dim3(grid1(static_cast<int64_t>(b) * b), nblk), dim3(kThreads), 0, s, q, dim, b,
+void unpack_skew2(const float* q0, int64_t dim0, int n0, const float* q1, int64_t dim1, int n1, int b, float* Qf,
+                  uint16_t* Qh, hipStream_t s) {
+  const Seg2 sg{q0, q1, dim0, dim1, n0};
+  hipLaunchKernelGGL(k_unpack_skew, dim3(grid1(static_cast<int64_t>(b) * b), n0 + n1), dim3(kThreads), 0, s, sg, b,
                      Qf, Qh);
 }
 
@@ -285,22 +339,24 @@ void cnp_mid(const float* Qf, const float* Q2f, uint16_t* Sh, float* Sf, int64_t
   hipLaunchKernelGGL(k_cnp_mid, dim3(grid1(n)), dim3(kThreads), 0, s, Qf, Q2f, Sh, Sf, n);
 }
 
-void cnp_finish(const float* Qf, const float* Q2f, const float* Tf, int b, int nblk, void* gbuf, bool bf16,
-                hipStream_t s) {
+void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int n0, void* g0, int n1, void* g1,
+                 bool bf16, hipStream_t s) {
   const unsigned t = static_cast<unsigned>((b + 31) / 32);
-  const dim3 g(t, t, static_cast<unsigned>(nblk));
+  const dim3 g(t, t, static_cast<unsigned>(n0 + n1));
   if (bf16)
-    hipLaunchKernelGGL(k_cnp_finish<uint16_t>, g, dim3(kThreads), 0, s, Qf, Q2f, Tf, b, nblk,
-                       static_cast<uint16_t*>(gbuf));
+    hipLaunchKernelGGL(k_cnp_finish<uint16_t>, g, dim3(kThreads), 0, s, Qf, Q2f, Tf, b, n0, n1,
+                       static_cast<uint16_t*>(g0), static_cast<uint16_t*>(g1));
   else
-    hipLaunchKernelGGL(k_cnp_finish<float>, g, dim3(kThreads), 0, s, Qf, Q2f, Tf, b, nblk,
-                       static_cast<float*>(gbuf));
+    hipLaunchKernelGGL(k_cnp_finish<float>, g, dim3(kThreads), 0, s, Qf, Q2f, Tf, b, n0, n1,
+                       static_cast<float*>(g0), static_cast<float*>(g1));
 }
 
-void cnp_bwd_pack(const float* U, const float* W1, const float* W2, const float* W3, int64_t dim, int b, int nblk,
-                  float* dq, hipStream_t s) {
-  hipLaunchKernelGGL(k_cnp_bwd_pack, dim3(grid1(static_cast<int64_t>(b) * b), nblk), dim3(kThreads), 0, s, U, W1, W2,
-                     W3, dim, b, dq);
+void cnp_bwd_pack2(const float* U, const float* W1, const float* W2, const float* W3, int b, int64_t dim0, int n0,
+                   float* dq0, int64_t dim1, int n1, float* dq1, hipStream_t s) {
+  const Seg2 sg{nullptr, nullptr, dim0, dim1, n0};
+  const unsigned t = static_cast<unsigned>((b + 31) / 32);
+  hipLaunchKernelGGL(k_cnp_bwd_pack, dim3(t, t, static_cast<unsigned>(n0 + n1)), dim3(kThreads), 0, s, U, W1, W2,
+                     W3, sg, dq0, dq1, b);
 }
 
 void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t s) {

@@ -376,9 +376,12 @@ void launch_cfg(const GemmDesc& d, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_bf16<BM, BN, BK, 2, 2, AM, BMD, CT, 0>), grid, dim3(256), 0, s, d, tm, tn);
 }
 
+// 256 x 256 tiles when they give at least two workgroups per CU (256 CUs),
+// else 128 x 128 tiles for more parallelism.
 template <int AM, int BMD, int CT>
 void launch_any(const GemmDesc& d, hipStream_t s) {
-  if (d.M >= 256 && d.N >= 256)
+  const int64_t big = static_cast<int64_t>((d.M + 255) / 256) * ((d.N + 255) / 256) * d.batch * d.ksplit;
+  if (d.M >= 256 && d.N >= 256 && big >= 512)
     launch_cfg<256, 256, AM, BMD, CT>(d, s);
   else
     launch_cfg<128, 128, AM, BMD, CT>(d, s);

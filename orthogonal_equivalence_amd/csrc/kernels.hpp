@@ -28,21 +28,26 @@ bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize,
 void fill_zero_f32(float* p, int64_t n, hipStream_t stream);
 
 // Skew blocks from packed parameters: Qf[z] (b x b, float) and, if Qh is not
-// null, a bfloat16 copy. Block z has size r = min(b, dim - z*b) and packed
-// offset z*b(b-1)/2; entries outside r x r are zero.
-void unpack_skew(const float* q, int64_t dim, int b, int nblk, float* Qf, uint16_t* Qh, hipStream_t stream);
+// null, a bfloat16 copy. Blocks [0, n0) come from (q0, dim0), blocks
+// [n0, n0 + n1) from (q1, dim1). A side's block z has size
+// r = min(b, dim - z*b) and packed offset z*b(b-1)/2; entries outside r x r
+// are zero.
+void unpack_skew2(const float* q0, int64_t dim0, int n0, const float* q1, int64_t dim1, int n1, int b, float* Qf,
+                  uint16_t* Qh, hipStream_t stream);
 
 // S = 2 Q + Q2, written as bfloat16 (Sh) or float (Sf), n elements.
 void cnp_mid(const float* Qf, const float* Q2f, uint16_t* Sh, float* Sf, int64_t n, hipStream_t stream);
 
 // G - I = 2Q + 2Q2 + T per block, written as plane 0 (row-major) and plane 1
-// (transposed) of the CNP block buffer in bfloat16 (bf16 = true) or float.
-void cnp_finish(const float* Qf, const float* Q2f, const float* Tf, int b, int nblk, void* gbuf, bool bf16,
-                hipStream_t stream);
+// (transposed) of a CNP block buffer in bfloat16 (bf16 = true) or float:
+// blocks [0, n0) into g0 (n0 blocks), the next n1 into g1.
+void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int n0, void* g0, int n1, void* g1,
+                 bool bf16, hipStream_t stream);
 
-// dQ = 2U - 2W1 + 2W2 - W3 and dq[k(i,l)] = dQ[i][l] - dQ[l][i] (i < l < r).
-void cnp_bwd_pack(const float* U, const float* W1, const float* W2, const float* W3, int64_t dim, int b,
-                  int nblk, float* dq, hipStream_t stream);
+// dQ = 2U - 2W1 + 2W2 - W3 and dq[k(i,l)] = dQ[i][l] - dQ[l][i] (i < l < r),
+// blocks [0, n0) into dq0 (side of width dim0), the next n1 into dq1.
+void cnp_bwd_pack2(const float* U, const float* W1, const float* W2, const float* W3, int b, int64_t dim0, int n0,
+                   float* dq0, int64_t dim1, int n1, float* dq1, hipStream_t stream);
 
 // out[e] = sum_{s < nsplit} part[s * n + e] (fixed order); optional bf16 copy.
 void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t stream);

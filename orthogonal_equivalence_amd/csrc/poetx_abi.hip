@@ -115,6 +115,26 @@ Split token_split(const poetx_layer* L, const Side& s, int64_t T) {
   return r;
 }
 
+// Blocks processed in one batch: side 0's n0 blocks followed by side 1's n1
+// blocks (n1 = 0 for one side alone). Both sides share a batch when their
+// block sizes match.
+struct Group {
+  int b;
+  int64_t dim0, dim1;
+  int n0, n1;
+  int64_t elems() const { return static_cast<int64_t>(n0 + n1) * b * b; }
+};
+
+Group group_of(const Side& s) { return Group{s.b, s.dim, 0, s.nblk, 0}; }
+Group group_of(const Side& s0, const Side& s1) { return Group{s0.b, s0.dim, s1.dim, s0.nblk, s1.nblk}; }
+
+// Upper bound of the block elements any CNP batch of this layer holds.
+int64_t cnp_batch_elems(const poetx_layer* L) {
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  if (R.b == P.b) return block_elems(R) + block_elems(P);
+  return std::max(block_elems(R), block_elems(P));
+}
+
 // ---------------------------------------------------------------------------
 // workspace plans (a null base only measures)
 // ---------------------------------------------------------------------------
@@ -124,8 +144,7 @@ struct CnpWs {
   uint16_t *Qh, *Q2h, *Sh;
 };
 
-CnpWs plan_cnp(const poetx_layer* L, const Side& s, Carve& c) {
-  const int64_t bb = block_elems(s);
+CnpWs plan_cnp(const poetx_layer* L, int64_t bb, Carve& c) {
   CnpWs w{};
   w.Qf = c.take<float>(bb);
   w.Q2f = c.take<float>(bb);
@@ -141,16 +160,14 @@ CnpWs plan_cnp(const poetx_layer* L, const Side& s, Carve& c) {
 }
 
 struct CnpBwdWs {
-  float *Qf, *Q2f, *U, *W1, *UQ2, *W2, *W3;
-  uint16_t *Qh, *Q2h, *Uh, *W1h, *UQ2h, *W2h;
+  float *Qf, *Q2f, *W1, *UQ2, *W2, *W3;
+  uint16_t *Qh, *Q2h, *W1h, *UQ2h, *W2h;
 };
 
-CnpBwdWs plan_cnp_bwd(const poetx_layer* L, const Side& s, Carve& c) {
-  const int64_t bb = block_elems(s);
+CnpBwdWs plan_cnp_bwd(const poetx_layer* L, int64_t bb, Carve& c) {
   CnpBwdWs w{};
   w.Qf = c.take<float>(bb);
   w.Q2f = c.take<float>(bb);
-  w.U = c.take<float>(bb);
   w.W1 = c.take<float>(bb);
   w.UQ2 = c.take<float>(bb);
   w.W2 = c.take<float>(bb);
@@ -158,7 +175,6 @@ CnpBwdWs plan_cnp_bwd(const poetx_layer* L, const Side& s, Carve& c) {
   if (is_bf16(L)) {
     w.Qh = c.take<uint16_t>(bb);
     w.Q2h = c.take<uint16_t>(bb);
-    w.Uh = c.take<uint16_t>(bb);
     w.W1h = c.take<uint16_t>(bb);
     w.UQ2h = c.take<uint16_t>(bb);
     w.W2h = c.take<uint16_t>(bb);
@@ -181,31 +197,28 @@ FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
 struct BwdWs {
   void *bufA, *bufB;
   int32_t* inv_r;
-  float* part;
-  size_t cnp_off;  // the CNP adjoint scratch starts here
+  float *part_r, *part_p;
+  float* U;           // reduced dG (side R) and dH (side P), one batch
+  uint16_t* Uh;
+  size_t cnp_off;     // the CNP adjoint scratch starts here
 };
 
 BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   BwdWs w;
   const int64_t rowmax = std::max(L->m, L->n);
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  const int64_t Tn = std::max<int64_t>(T, 1);
   w.bufA = c.take<char>(T * rowmax * act_size(L));
   w.bufB = c.take<char>(T * rowmax * act_size(L));
   w.inv_r = c.take<int32_t>(L->m);
-  int64_t part = 0;
-  for (int sd : {POETX_SIDE_R, POETX_SIDE_P}) {
-    const Side s = side_of(L, sd);
-    part = std::max<int64_t>(part, static_cast<int64_t>(token_split(L, s, std::max<int64_t>(T, 1)).nsplit) *
-                                       block_elems(s));
-  }
-  w.part = c.take<float>(part);
+  w.part_r = c.take<float>(static_cast<int64_t>(token_split(L, R, Tn).nsplit) * block_elems(R));
+  w.part_p = c.take<float>(static_cast<int64_t>(token_split(L, P, Tn).nsplit) * block_elems(P));
+  w.U = c.take<float>(block_elems(R) + block_elems(P));
+  w.Uh = c.take<uint16_t>(block_elems(R) + block_elems(P));
   w.cnp_off = c.off;
-  size_t cnp = 0;
-  for (int sd : {POETX_SIDE_R, POETX_SIDE_P}) {
-    Carve m(nullptr);
-    plan_cnp_bwd(L, side_of(L, sd), m);
-    cnp = std::max(cnp, m.off);
-  }
-  c.off += cnp;
+  Carve m(nullptr);
+  plan_cnp_bwd(L, cnp_batch_elems(L), m);
+  c.off += m.off;
   return w;
 }
 
@@ -223,13 +236,9 @@ MergeWs plan_merge(const poetx_layer* L, Carve& c) {
 }
 
 size_t cnp_build_bytes(const poetx_layer* L) {
-  size_t r = 0;
-  for (int sd : {POETX_SIDE_R, POETX_SIDE_P}) {
-    Carve m(nullptr);
-    plan_cnp(L, side_of(L, sd), m);
-    r = std::max(r, m.off);
-  }
-  return r;
+  Carve m(nullptr);
+  plan_cnp(L, cnp_batch_elems(L), m);
+  return m.off;
 }
 
 size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
@@ -366,9 +375,10 @@ bool block_token_grad(const poetx_layer* L, const Side& s, int64_t T, const void
 
 // Batched b x b product C = alpha A B^T-form (see gemm.hpp) with optional
 // addend and bf16 copy, over the nblk blocks of one side.
-bool sq(const poetx_layer* L, const Side& s, const void* A, int am, const void* B, int bm, float* C, uint16_t* C2,
+bool sq(const poetx_layer* L, const Group& g, const void* A, int am, const void* B, int bm, float* C, uint16_t* C2,
         float alpha, const float* D, hipStream_t st) {
   GemmDesc d;
+  const Side s{0, g.b, g.n0 + g.n1};
   const int64_t bb = static_cast<int64_t>(s.b) * s.b;
   d.A = A;
   d.lda = s.b;
@@ -392,57 +402,57 @@ bool sq(const poetx_layer* L, const Side& s, const void* A, int am, const void* 
   return gemm(L, d, am, bm, C_F32, st);
 }
 
-// G - I for every block of one side: Q2 = Q Q, S = 2Q + Q2, T = S Q2,
+// G - I for every block of a group: Q2 = Q Q, S = 2Q + Q2, T = S Q2,
 // G - I = 2Q + 2Q2 + T  (= (I+Q)(I+Q+Q^2+Q^3) - I with every higher term
 // formed from Q and Q^2, section "3. Cayley-Neumann 参数化优化").
-bool cnp_side(const poetx_layer* L, const Side& s, const float* q, void* gbuf, void* ws, hipStream_t st) {
+bool cnp_group(const poetx_layer* L, const Group& g, const float* q0, const float* q1, void* g0, void* g1, void* ws,
+               hipStream_t st) {
   Carve c(ws);
-  CnpWs w = plan_cnp(L, s, c);
+  CnpWs w = plan_cnp(L, g.elems(), c);
   const bool bf = is_bf16(L);
-  unpack_skew(q, s.dim, s.b, s.nblk, w.Qf, bf ? w.Qh : nullptr, st);
+  unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
   const void* Qop = bf ? static_cast<const void*>(w.Qh) : w.Qf;
   // Q Q = -Q Q^T: the NT product with B = Q and alpha = -1 (Q skew)
-  if (!sq(L, s, Qop, A_KCONTIG, Qop, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st)) return false;
-  cnp_mid(w.Qf, w.Q2f, bf ? w.Sh : nullptr, bf ? nullptr : w.Sf, block_elems(s), st);
+  if (!sq(L, g, Qop, A_KCONTIG, Qop, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st)) return false;
+  cnp_mid(w.Qf, w.Q2f, bf ? w.Sh : nullptr, bf ? nullptr : w.Sf, g.elems(), st);
   // S Q2 with Q2 symmetric: B rows = Q2 rows
   const void* Sop = bf ? static_cast<const void*>(w.Sh) : w.Sf;
   const void* Q2op = bf ? static_cast<const void*>(w.Q2h) : w.Q2f;
-  if (!sq(L, s, Sop, A_KCONTIG, Q2op, B_KCONTIG, w.Tf, nullptr, 1.f, nullptr, st)) return false;
-  cnp_finish(w.Qf, w.Q2f, w.Tf, s.b, s.nblk, gbuf, bf, st);
+  if (!sq(L, g, Sop, A_KCONTIG, Q2op, B_KCONTIG, w.Tf, nullptr, 1.f, nullptr, st)) return false;
+  cnp_finish2(w.Qf, w.Q2f, w.Tf, g.b, g.n0, g0, g.n1, g1, bf, st);
   return true;
 }
 
-// dq from dG = U for one side. With Q skew, the adjoint of
-// G = (I+Q)(I+Q+Q^2+Q^3) collapses to sums of Q^a U Q^c whose coefficient
-// depends on a + c only: dL/dQ = 2U - 2 W1 + 2 W2 - W3 with
+// dq from the reduced block gradients U (dL/dG) of a group. With Q skew,
+// the adjoint of G = (I+Q)(I+Q+Q^2+Q^3) collapses to sums of Q^a U Q^c whose
+// coefficient depends on a + c only: dL/dQ = 2U - 2 W1 + 2 W2 - W3 with
 // W1 = QU + UQ, W2 = Q W1 + U Q^2, W3 = Q W2 + (U Q^2) Q; then
 // dq_k = dL/dQ[i][l] - dL/dQ[l][i].
-bool cnp_bwd_side(const poetx_layer* L, const Side& s, const float* q, const float* part, const Split& sp,
-                  float* dq, void* cnp_ws, hipStream_t st) {
+bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const float* q1, const float* Uf,
+                   const uint16_t* Uh, float* dq0, float* dq1, void* cnp_ws, hipStream_t st) {
   Carve c(cnp_ws);
-  CnpBwdWs w = plan_cnp_bwd(L, s, c);
+  CnpBwdWs w = plan_cnp_bwd(L, g.elems(), c);
   const bool bf = is_bf16(L);
-  reduce_splits(part, sp.nsplit, block_elems(s), w.U, bf ? w.Uh : nullptr, st);
-  unpack_skew(q, s.dim, s.b, s.nblk, w.Qf, bf ? w.Qh : nullptr, st);
+  unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
   const void* Q = bf ? static_cast<const void*>(w.Qh) : w.Qf;
-  const void* U = bf ? static_cast<const void*>(w.Uh) : w.U;
-  bool ok = sq(L, s, Q, A_KCONTIG, Q, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st);
+  const void* U = bf ? static_cast<const void*>(Uh) : Uf;
+  bool ok = sq(L, g, Q, A_KCONTIG, Q, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st);
   const void* Q2 = bf ? static_cast<const void*>(w.Q2h) : w.Q2f;
   // W1 = Q U + U Q
-  ok = ok && sq(L, s, Q, A_KCONTIG, U, B_NCONTIG, w.W1, nullptr, 1.f, nullptr, st);
-  ok = ok && sq(L, s, U, A_KCONTIG, Q, B_KCONTIG, w.W1, bf ? w.W1h : nullptr, -1.f, w.W1, st);
+  ok = ok && sq(L, g, Q, A_KCONTIG, U, B_NCONTIG, w.W1, nullptr, 1.f, nullptr, st);
+  ok = ok && sq(L, g, U, A_KCONTIG, Q, B_KCONTIG, w.W1, bf ? w.W1h : nullptr, -1.f, w.W1, st);
   const void* W1 = bf ? static_cast<const void*>(w.W1h) : w.W1;
   // U Q2 (Q2 symmetric)
-  ok = ok && sq(L, s, U, A_KCONTIG, Q2, B_KCONTIG, w.UQ2, bf ? w.UQ2h : nullptr, 1.f, nullptr, st);
+  ok = ok && sq(L, g, U, A_KCONTIG, Q2, B_KCONTIG, w.UQ2, bf ? w.UQ2h : nullptr, 1.f, nullptr, st);
   const void* UQ2 = bf ? static_cast<const void*>(w.UQ2h) : w.UQ2;
   // W2 = Q W1 + U Q2
-  ok = ok && sq(L, s, Q, A_KCONTIG, W1, B_NCONTIG, w.W2, bf ? w.W2h : nullptr, 1.f, w.UQ2, st);
+  ok = ok && sq(L, g, Q, A_KCONTIG, W1, B_NCONTIG, w.W2, bf ? w.W2h : nullptr, 1.f, w.UQ2, st);
   const void* W2 = bf ? static_cast<const void*>(w.W2h) : w.W2;
   // W3 = Q W2 + (U Q2) Q
-  ok = ok && sq(L, s, Q, A_KCONTIG, W2, B_NCONTIG, w.W3, nullptr, 1.f, nullptr, st);
-  ok = ok && sq(L, s, UQ2, A_KCONTIG, Q, B_KCONTIG, w.W3, nullptr, -1.f, w.W3, st);
+  ok = ok && sq(L, g, Q, A_KCONTIG, W2, B_NCONTIG, w.W3, nullptr, 1.f, nullptr, st);
+  ok = ok && sq(L, g, UQ2, A_KCONTIG, Q, B_KCONTIG, w.W3, nullptr, -1.f, w.W3, st);
   if (!ok) return false;
-  cnp_bwd_pack(w.U, w.W1, w.W2, w.W3, s.dim, s.b, s.nblk, dq, st);
+  cnp_bwd_pack2(Uf, w.W1, w.W2, w.W3, g.b, g.dim0, g.n0, dq0, g.dim1, g.n1, dq1, st);
   return true;
 }
 
@@ -510,13 +520,19 @@ int poetx_cnp_build(const poetx_layer* L, const float* q_r, const float* q_p, vo
     if (p && !aligned16(p)) return POETX_EINVAL;
   if (const int e = check_ws(L, 0, POETX_OP_CNP_BUILD, ws, ws_bytes)) return e;
   bool ok = true;
-  if (q_r) {
-    ProfScope p("cnp_build_r", stream);
-    ok = ok && cnp_side(L, side_of(L, POETX_SIDE_R), q_r, g_r, ws, stream);
-  }
-  if (q_p) {
-    ProfScope p("cnp_build_p", stream);
-    ok = ok && cnp_side(L, side_of(L, POETX_SIDE_P), q_p, g_p, ws, stream);
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  if (q_r && q_p && R.b == P.b) {
+    ProfScope p("cnp_build", stream);
+    ok = cnp_group(L, group_of(R, P), q_r, q_p, g_r, g_p, ws, stream);
+  } else {
+    if (q_r) {
+      ProfScope p("cnp_build_r", stream);
+      ok = ok && cnp_group(L, group_of(R), q_r, nullptr, g_r, nullptr, ws, stream);
+    }
+    if (q_p) {
+      ProfScope p("cnp_build_p", stream);
+      ok = ok && cnp_group(L, group_of(P), q_p, nullptr, g_p, nullptr, ws, stream);
+    }
   }
   if (!ok) return POETX_EUNSUPPORTED;
   return launch_status();
@@ -635,11 +651,7 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   const Split spP = token_split(L, P, T);
   {
     ProfScope p("grad_h", stream);
-    ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part, spP, stream);
-  }
-  {
-    ProfScope p("cnp_bwd_p", stream);
-    ok = ok && cnp_bwd_side(L, P, q_p, w.part, spP, dq_p, cnp_ws, stream);
+    ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part_p, spP, stream);
   }
   // dX2 = dY1 Wp^T
   GemmDesc d;
@@ -665,16 +677,27 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   const Split spR = token_split(L, R, T);
   {
     ProfScope p("grad_g", stream);
-    ok = ok && block_token_grad(L, R, T, X1, w.bufA, w.part, spR, stream);
-  }
-  {
-    ProfScope p("cnp_bwd_r", stream);
-    ok = ok && cnp_bwd_side(L, R, q_r, w.part, spR, dq_r, cnp_ws, stream);
+    ok = ok && block_token_grad(L, R, T, X1, w.bufA, w.part_r, spR, stream);
   }
   {
     ProfScope p("scatter_dx", stream);
     inverse_perm(perm_r, w.inv_r, L->m, stream);
     ok = ok && gather_cols(w.bufB, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
+  }
+  // dq_r, dq_p from the token sums dG, dH
+  {
+    ProfScope p("cnp_bwd", stream);
+    const bool bf = is_bf16(L);
+    reduce_splits(w.part_r, spR.nsplit, block_elems(R), w.U, bf ? w.Uh : nullptr, stream);
+    reduce_splits(w.part_p, spP.nsplit, block_elems(P), w.U + block_elems(R), bf ? w.Uh + block_elems(R) : nullptr,
+                  stream);
+    if (R.b == P.b) {
+      ok = ok && cnp_bwd_group(L, group_of(R, P), q_r, q_p, w.U, w.Uh, dq_r, dq_p, cnp_ws, stream);
+    } else {
+      ok = ok && cnp_bwd_group(L, group_of(R), q_r, nullptr, w.U, w.Uh, dq_r, nullptr, cnp_ws, stream);
+      ok = ok && cnp_bwd_group(L, group_of(P), q_p, nullptr, w.U + block_elems(R), w.Uh + block_elems(R), dq_p,
+                               nullptr, cnp_ws, stream);
+    }
   }
   if (!ok) return POETX_EUNSUPPORTED;
   return launch_status();
