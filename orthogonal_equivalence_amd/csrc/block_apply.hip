@@ -1,0 +1,162 @@
+// Streaming block-diagonal product on token-major bfloat16 activations:
+//   out[t, J_j] = (in[t, J_j] + in[t, J_j] B_j^T) * s[J_j]     (s optional)
+// where B_j is one b x b plane of a CNP block buffer ((G-I)^T for the forward
+// apply in G, (G-I) for the backward apply in G^T). It is the layer's
+// "X1 Diag(G)" / "dY2 Diag(H)^T" step (zhichai.net digest of arXiv:2603.05500,
+// section "2. 块随机正交变换"), an HBM-bound pass (b/2 flops per byte).
+//
+// gfx950 design: one workgroup owns one block and a contiguous run of
+// tokens. Each of its b/32 waves keeps its 32 output columns of B_j resident
+// in registers as MFMA fragments for the whole run, so B_j is read once per
+// workgroup. 32-token sub-tiles stream global -> LDS with
+// global_load_lds_dwordx4 into two swizzled stages (the next sub-tile is in
+// flight while the current one is multiplied); v_mfma_f32_32x32x16_bf16 does
+// the product; a per-wave LDS slab turns the accumulator into rows, where the
+// residual (from the staged input) is added and 16-byte stores go out.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace poetx {
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+constexpr int TT = 32;  // tokens per sub-tile
+
+template <int B>
+__device__ __forceinline__ int swz_row(int r) {
+  // rows of >= 256 bytes: 16-byte slot bank group = slot % 16, spread by r;
+  // 128-byte rows: bank group = 8 * (r % 2) + slot, spread by r / 2
+  if constexpr (B >= 128) return r & 15;
+  else return (r >> 1) & 7;
+}
+
+// two workgroups per CU: 2 * (waves per SIMD of one workgroup) waves per SIMD
+template <int B>
+__global__ void __launch_bounds__(64 * (B / 32), (B >= 256 ? 4 : 2))
+k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t ld, const bf16_t* __restrict__ plane,
+              const float* __restrict__ scale, int64_t T, int64_t dim, int tokens_per_wg, int wgs_per_block) {
+  constexpr int NW = B / 32;
+  constexpr int ROWB = B * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int STAGE = TT * ROWB;
+  constexpr int KS = B / 16;
+  constexpr int SLAB = 32 * 33 * 4;  // per wave: 32 rows x 32 fp32 columns (+1 pad)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + NW * SLAB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int blk = blockIdx.x / wgs_per_block;
+  const int part = blockIdx.x % wgs_per_block;
+  const int64_t col0 = static_cast<int64_t>(blk) * B;
+  const int width = static_cast<int>(min(static_cast<int64_t>(B), dim - col0));  // short last block
+  const int cmax = width / 8 - 1;                                                  // last valid chunk
+  const int64_t t_begin = static_cast<int64_t>(part) * tokens_per_wg;
+  const int64_t t_end = min(T, t_begin + tokens_per_wg);
+  if (t_begin >= t_end) return;
+  const int nsub = static_cast<int>((t_end - t_begin + TT - 1) / TT);
+
+  // this wave's 32 columns of B_j as MFMA B-operand fragments (column n, 8 k's)
+  const int lcol = lane & 31;
+  const int ncol = wave * 32 + lcol;
+  const bf16_t* brow = plane + static_cast<int64_t>(blk) * B * B + static_cast<int64_t>(ncol) * B + (lane >> 5) * 8;
+  bf16x8_t gfrag[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) gfrag[kk] = *reinterpret_cast<const bf16x8_t*>(brow + kk * 16);
+
+  // direct loads: each wave fills 2 x 1 KB of a stage
+  auto issue = [&](int sub, int stage) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = (wave * 2 + i) * 64 + lane;
+      const int row = q / CPR, slot = q % CPR;
+      int c = slot ^ swz_row<B>(row);
+      c = c < cmax ? c : cmax;
+      int64_t t = t_begin + static_cast<int64_t>(sub) * TT + row;
+      t = t < t_end ? t : t_end - 1;
+      const bf16_t* src = in + t * ld + col0 + c * 8;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       (lds_void_t)(smem + stage * STAGE + (wave * 2 + i) * 1024), 16, 0, 0);
+    }
+  };
+
+  const int arow = lane & 31;
+  const int asw = swz_row<B>(arow);
+  float* slab = reinterpret_cast<float*>(smem + 2 * STAGE + wave * SLAB);
+  issue(0, 0);
+  for (int s = 0; s < nsub; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (s + 1 < nsub) issue(s + 1, (s + 1) & 1);
+    const char* st = smem + (s & 1) * STAGE;
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int c = 2 * kk + (lane >> 5);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + arow * ROWB + ((c ^ asw) << 4));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gfrag[kk], acc, 0, 0, 0);
+    }
+    // accumulator -> this wave's fp32 slab (32 rows x 32 columns), then per
+    // lane 8 consecutive columns of a row: + residual from the staged input,
+    // * column scale, bfloat16, one 16-byte store
+#pragma unroll
+    for (int r = 0; r < 16; ++r) slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 33 + lcol] = acc[r];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = lane + i * 64;
+      const int row = q >> 2, c4 = q & 3;
+      const int64_t t = t_begin + static_cast<int64_t>(s) * TT + row;
+      const int col = wave * 32 + c4 * 8;
+      const int chunk = col >> 3;
+      const uint4 xr = *reinterpret_cast<const uint4*>(st + row * ROWB + ((chunk ^ swz_row<B>(row)) << 4));
+      const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = slab[row * 33 + c4 * 8 + 2 * e] + __uint_as_float(xw[e] << 16);
+        v[2 * e + 1] = slab[row * 33 + c4 * 8 + 2 * e + 1] + __uint_as_float(xw[e] & 0xffff0000u);
+      }
+      if (scale) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= scale[col0 + (col < width ? col : 0) + e];
+      }
+      if (t < t_end && col < width)
+        *reinterpret_cast<uint4*>(out + t * ld + col0 + col) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+    }
+  }
+}
+
+}  // namespace
+
+bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
+                      int64_t T, int64_t dim, int b, hipStream_t s) {
+  if (T <= 0) return true;
+  if (b != 64 && b != 128 && b != 256) return false;
+  const int nblk = static_cast<int>((dim + b - 1) / b);
+  const int64_t target = 512;
+  int64_t wpb = (target + nblk - 1) / nblk;
+  int64_t tpw = (T + wpb - 1) / wpb;
+  tpw = (tpw + TT - 1) / TT * TT;
+  wpb = (T + tpw - 1) / tpw;
+  const dim3 grid(static_cast<unsigned>(nblk * wpb));
+  const int itpw = static_cast<int>(tpw), iwpb = static_cast<int>(wpb);
+  switch (b) {
+    case 64:
+      hipLaunchKernelGGL(k_block_apply<64>, grid, dim3(128), 0, s, in, out, ld, plane, scale, T, dim, itpw, iwpb);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_block_apply<128>, grid, dim3(256), 0, s, in, out, ld, plane, scale, T, dim, itpw, iwpb);
+      break;
+    default:
+      hipLaunchKernelGGL(k_block_apply<256>, grid, dim3(512), 0, s, in, out, ld, plane, scale, T, dim, itpw, iwpb);
+      break;
+  }
+  return true;
+}
+
+}  // namespace poetx

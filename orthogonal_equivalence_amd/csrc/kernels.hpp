@@ -49,6 +49,15 @@ void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int 
 void cnp_bwd_pack2(const float* U, const float* W1, const float* W2, const float* W3, int b, int64_t dim0, int n0,
                    float* dq0, int64_t dim1, int n1, float* dq1, hipStream_t stream);
 
+// Streaming block-diagonal product (block_apply.hip) on token-major bfloat16
+// rows: out[t][j*b + c] = (in[t][j*b + c] + sum_k in[t][j*b + k] *
+// plane[j][c][k]) * scale[j*b + c] (scale optional), for the ceil(dim/b)
+// blocks of a row of width dim (row stride ld). plane holds b x b bfloat16
+// blocks, zero outside a short last block. Returns false unless b is 64,
+// 128 or 256.
+bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
+                      int64_t T, int64_t dim, int b, hipStream_t stream);
+
 // out[e] = sum_{s < nsplit} part[s * n + e] (fixed order); optional bf16 copy.
 void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t stream);
 
