@@ -10,7 +10,10 @@ namespace poetx {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int64_t kRowLdsBudget = 64 * 1024;     // bytes of rows staged per workgroup
+#ifndef POETX_GATHER_LDS_KB
+#define POETX_GATHER_LDS_KB 32
+#endif
+constexpr int64_t kRowLdsBudget = POETX_GATHER_LDS_KB * 1024;  // bytes of rows staged per workgroup
 constexpr int64_t kRowLdsMax = 64 * 1024;        // wider rows use the direct kernel
 
 template <typename T> struct Pack8;
@@ -105,20 +108,48 @@ __global__ void k_gather_f32(const float* __restrict__ in, const int32_t* __rest
   if (i < n) out[i] = in[clamp_index(idx[i], n)];
 }
 
+// Transpose through a 64 x 64 LDS tile with 16-byte global accesses on both
+// sides: each lane reads 16 bytes of an input row and writes 16 bytes of an
+// output row (V = 16 / sizeof(T) elements). The LDS tile is padded by one
+// element per row so that the column reads spread over the banks.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_transpose(const T* __restrict__ in, T* __restrict__ out, int64_t rows,
                                                        int64_t cols) {
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / sizeof(T);
+  constexpr int CPR = 64 / V;  // 16-byte chunks per 64-element row
+  __shared__ T tile[64][64 + 1];
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = in[r * cols + c];
+  const bool full = (r0 + 64 <= rows) && (c0 + 64 <= cols);
+  for (int q = threadIdx.x; q < 64 * CPR; q += kThreads) {
+    const int i = q / CPR, j = (q % CPR) * V;
+    const int64_t r = r0 + i, c = c0 + j;
+    T v[V];
+    if (full) {
+      const uint4 w = *reinterpret_cast<const uint4*>(in + r * cols + c);
+      __builtin_memcpy(v, &w, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] = (r < rows && c + e < cols) ? in[r * cols + c + e] : T(0);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) tile[i][j + e] = v[e];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (r < rows && c < cols) out[c * rows + r] = tile[tx][i];
+  for (int q = threadIdx.x; q < 64 * CPR; q += kThreads) {
+    const int i = q / CPR, j = (q % CPR) * V;  // output row c0 + i, columns r0 + j ..
+    const int64_t c = c0 + i, r = r0 + j;
+    T v[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = tile[j + e][i];
+    if (full) {
+      uint4 w;
+      __builtin_memcpy(&w, v, 16);
+      *reinterpret_cast<uint4*>(out + c * rows + r) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (c < cols && r + e < rows) out[c * rows + r + e] = v[e];
+    }
   }
 }
 

@@ -23,40 +23,69 @@ namespace {
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int WM = 2, WN = 4;
+#ifndef POETX_DENSE_BK
+#define POETX_DENSE_BK 64
+#endif
+#ifndef POETX_DENSE_STAGES
+#define POETX_DENSE_STAGES 2
+#endif
+#ifndef POETX_DENSE_WN
+#define POETX_DENSE_WN 4
+#endif
+
+constexpr int BM = 256, BN = 256;
+constexpr int BK = POETX_DENSE_BK;           // K depth of one LDS stage
+constexpr int NSTAGE = POETX_DENSE_STAGES;   // LDS stages; NSTAGE - 1 in flight
+constexpr int WM = 2, WN = POETX_DENSE_WN;
 constexpr int NT = 64 * WM * WN;
 constexpr int WTM = BM / WM, WTN = BN / WN;  // 128 x 64 per wave
 constexpr int TM = WTM / 32, TN = WTN / 32;  // 4 x 2 MFMA tiles
-constexpr int kRowBytes = BK * 2;            // 128
-constexpr int kTileBytes = BM * kRowBytes;   // 32 KB per operand and stage
+constexpr int kRowBytes = BK * 2;            // 64 or 128
+constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
+constexpr int kRowsPerInst = 64 / kChunks;   // rows one 1 KB load covers
+constexpr int kTileBytes = BM * kRowBytes;   // per operand and stage
 constexpr int kStageBytes = 2 * kTileBytes;  // A + B
+constexpr int kInstPerTile = kTileBytes / 1024 / (NT / 64);  // loads per wave per operand
 constexpr int kSlabStride = WTN + 8;         // epilogue slab row, floats
+static_assert(NSTAGE * kStageBytes <= 160 * 1024, "LDS");
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Slot of 16-byte chunk c in row r: c ^ swz(r). For 128-byte rows the bank
+// group of a 16-byte read is 8 * (r % 2) + slot (16 lanes a cycle) or slot
+// (8 lanes); for 64-byte rows it is 4 * (r % 4) + slot or 4 * (r % 2) + slot.
+// Both choices below make the 32 rows of one fragment read conflict-free in
+// either model.
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (kChunks == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
 
-// Direct-to-LDS load of one 256 x 64 bfloat16 operand tile. Wave w fills rows
-// [32w, 32w + 32) with four instructions of 8 rows (1 KB) each; lane l of an
-// instruction lands in LDS slot l % 8 of row l / 8 and fetches the chunk that
-// belongs there. Rows past `rowlim` re-read row rowlim - 1 (in bounds); their
-// products only reach outputs that are never stored.
+// Direct-to-LDS load of one 256 x BK bfloat16 operand tile. Each wave issues
+// kInstPerTile instructions of 1 KB; lane l of an instruction lands in slot
+// l % kChunks of row l / kChunks and fetches the chunk that belongs there.
+// Rows past `rowlim` re-read row rowlim - 1 (in bounds); their products only
+// reach outputs that are never stored.
 __device__ __forceinline__ void load_tile(const bf16_t* __restrict__ g, int64_t ld, int row0, int rowlim, int k0,
                                           char* lds, int wave, int lane) {
-  const int sub = lane >> 3, slot = lane & 7;
+  const int sub = lane / kChunks, slot = lane % kChunks;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 32 + i * 8 + sub;
+  for (int i = 0; i < kInstPerTile; ++i) {
+    const int rbase = (wave * kInstPerTile + i) * kRowsPerInst;
+    const int r = rbase + sub;
     const int c = slot ^ swz(r);
     int gr = row0 + r;
     gr = gr < rowlim ? gr : rowlim - 1;
     const bf16_t* src = g + static_cast<int64_t>(gr) * ld + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                     (lds_void_t)(lds + (wave * 32 + i * 8) * kRowBytes), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t)(lds + rbase * kRowBytes), 16, 0, 0);
   }
 }
 
-__global__ void __launch_bounds__(NT) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,18 +123,32 @@ __global__ void __launch_bounds__(NT) k_gemm_dense(const GemmDesc d, int tiles_m
   const int abase = wm * WTM * kRowBytes;
   const int bbase = kTileBytes + wn * WTN * kRowBytes;
 
-  load_tile(A, d.lda, m0, d.M, 0, smem, wave, lane);
-  load_tile(B, d.ldb, n0, d.N, 0, smem + kTileBytes, wave, lane);
+  // prologue: stages 0 .. NSTAGE-2 in flight
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) {
+    if (p < nk) {
+      load_tile(A, d.lda, m0, d.M, p * BK, smem + p * kStageBytes, wave, lane);
+      load_tile(B, d.ldb, n0, d.N, p * BK, smem + p * kStageBytes + kTileBytes, wave, lane);
+    }
+  }
 
   for (int it = 0; it < nk; ++it) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // stage `it` is the oldest of the (up to NSTAGE - 1) stages in flight;
+    // loads complete in order, so waiting until the younger ones remain
+    // suffices. Near the end fewer younger stages exist.
+    constexpr int kPerStage = 2 * kInstPerTile;
+    const int younger = min(NSTAGE - 2, nk - 1 - it);
+    if (younger >= 2) wait_vmcnt<2 * kPerStage>();
+    else if (younger == 1) wait_vmcnt<kPerStage>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    if (it + 1 < nk) {
-      char* nxt = smem + ((it + 1) & 1) * kStageBytes;
-      load_tile(A, d.lda, m0, d.M, (it + 1) * BK, nxt, wave, lane);
-      load_tile(B, d.ldb, n0, d.N, (it + 1) * BK, nxt + kTileBytes, wave, lane);
+    const int pf = it + NSTAGE - 1;
+    if (pf < nk) {
+      char* nxt = smem + (pf % NSTAGE) * kStageBytes;
+      load_tile(A, d.lda, m0, d.M, pf * BK, nxt, wave, lane);
+      load_tile(B, d.ldb, n0, d.N, pf * BK, nxt + kTileBytes, wave, lane);
     }
-    const char* st = smem + (it & 1) * kStageBytes;
+    const char* st = smem + (it % NSTAGE) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8_t af[TM], bfr[TN];
@@ -166,7 +209,7 @@ __global__ void __launch_bounds__(NT) k_gemm_dense(const GemmDesc d, int tiles_m
 
 bool gemm_dense_bf16(const GemmDesc& d, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return true;
-  if (d.K % BK != 0 || d.K <= 0 || d.N % 8 != 0) return false;
+  if (d.K % 64 != 0 || d.K <= 0 || d.N % 8 != 0) return false;
   const int tm = (d.M + BM - 1) / BM, tn = (d.N + BN - 1) / BN;
   hipLaunchKernelGGL(k_gemm_dense, dim3(tm * tn), dim3(NT), 0, s, d, tm, tn);
   return true;
