@@ -58,6 +58,15 @@ void cnp_bwd_pack2(const float* U, const float* W1, const float* W2, const float
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
                       int64_t T, int64_t dim, int b, hipStream_t stream);
 
+// Token sums of the block gradients (block_grad.hip) for bfloat16 blocks of
+// 256 or 512: part[s][j][i][c] = sum over the tokens of split s of
+// act[t][j*b + i] * dout[t][j*b + c], written for every (i, c) < b (zeros
+// outside a short last block). block_grad_splits gives the split count the
+// kernel uses for T tokens (0 if b is not 256 or 512).
+int block_grad_splits(int64_t T, int64_t dim, int b);
+bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int64_t ld, int64_t T, int64_t dim,
+                     int b, int nsplit, hipStream_t stream);
+
 // out[e] = sum_{s < nsplit} part[s * n + e] (fixed order); optional bf16 copy.
 void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t stream);
 

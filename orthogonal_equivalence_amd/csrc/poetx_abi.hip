@@ -96,6 +96,12 @@ struct Split {
 };
 
 Split token_split(const poetx_layer* L, const Side& s, int64_t T) {
+  if (is_bf16(L) && (s.b == 256 || s.b == 512)) {
+    Split r;
+    r.nsplit = std::max(1, block_grad_splits(T, s.dim, s.b));
+    r.kchunk = 0;
+    return r;
+  }
   int tiles;
   if (is_bf16(L)) {
     const int t = s.b >= 256 ? 256 : 128;
@@ -353,6 +359,9 @@ bool block_apply(const poetx_layer* L, const Side& s, int64_t T, const void* in,
 // part[s][z] = sum over the tokens of split s of A_z^T dO_z (b x b per block)
 bool block_token_grad(const poetx_layer* L, const Side& s, int64_t T, const void* act, const void* dout,
                       float* part, const Split& sp, hipStream_t st) {
+  if (is_bf16(L) && (s.b == 256 || s.b == 512))
+    return block_grad_bf16(static_cast<const uint16_t*>(act), static_cast<const uint16_t*>(dout), part, s.dim, T,
+                           s.dim, s.b, sp.nsplit, st);
   GemmDesc d;
   d.A = act;
   d.lda = s.dim;
