@@ -184,25 +184,45 @@ __device__ __forceinline__ void seg_pick(const Seg2& sg, int z, const float*& q,
   }
 }
 
-__global__ void k_unpack_skew(const Seg2 sg, int b, float* __restrict__ Qf, uint16_t* __restrict__ Qh) {
-  const int z = blockIdx.y;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= static_cast<int64_t>(b) * b) return;
+// One workgroup per 32 x 32 tile pair (I, L), I <= L, of block z: the packed
+// entries of rows i in tile I and columns l in tile L (i < l) are contiguous
+// runs of q, read coalesced; Q[i][l] = q and Q[l][i] = -q meet in LDS.
+__global__ void __launch_bounds__(kThreads) k_unpack_skew(const Seg2 sg, int b, float* __restrict__ Qf,
+                                                         uint16_t* __restrict__ Qh) {
+  __shared__ float tile[32][33];
+  const int z = blockIdx.z, I = blockIdx.y, Lt = blockIdx.x;
+  if (I > Lt) return;
   const float* q;
   int64_t dim;
   int zl;
   seg_pick(sg, z, q, dim, zl);
-  const int i = static_cast<int>(e / b), l = static_cast<int>(e % b);
   const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
   const float* qz = q + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
-  float v = 0.f;
-  if (i < r && l < r) {
-    if (i < l) v = qz[tri_index(i, l, r)];
-    else if (i > l) v = -qz[tri_index(l, i, r)];
+  const int64_t base = static_cast<int64_t>(z) * b * b;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int k = ty; k < 32; k += 8) {
+    const int i = I * 32 + k, l = Lt * 32 + tx;
+    float v = 0.f;
+    if (i < l && l < r) v = qz[tri_index(i, l, r)];
+    tile[k][tx] = v;
+    if (i < b && l < b) {
+      const int64_t o = base + static_cast<int64_t>(i) * b + l;
+      if (I != Lt || i < l) {  // the rest of a diagonal tile is written below
+        Qf[o] = v;
+        if (Qh) Qh[o] = f32_to_bf16(v);
+      }
+    }
   }
-  const int64_t o = static_cast<int64_t>(z) * b * b + e;
-  Qf[o] = v;
-  if (Qh) Qh[o] = f32_to_bf16(v);
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int l = Lt * 32 + k, i = I * 32 + tx;  // Q[l][i] = -Q[i][l] for i < l
+    if (i < b && l < b && (I != Lt || i <= l)) {
+      const float v = (i == l) ? 0.f : -tile[tx][k];
+      const int64_t o = base + static_cast<int64_t>(l) * b + i;
+      Qf[o] = v;
+      if (Qh) Qh[o] = f32_to_bf16(v);
+    }
+  }
 }
 
 __global__ void k_cnp_mid(const float* __restrict__ Qf, const float* __restrict__ Q2f, uint16_t* __restrict__ Sh,
@@ -245,13 +265,11 @@ __global__ void __launch_bounds__(kThreads) k_cnp_finish(const float* __restrict
   }
 }
 
-// dq for block z: dQ = 2U - 2W1 + 2W2 - W3 and dq[k(i,l)] = dQ[i][l] - dQ[l][i]
-// for i < l < r. One workgroup per 32 x 32 tile (I, L) with I <= L: the tile
-// and its mirror (L, I) are read row-wise and meet in LDS.
-__global__ void __launch_bounds__(kThreads) k_cnp_bwd_pack(const float* __restrict__ U, const float* __restrict__ W1,
-                                                          const float* __restrict__ W2, const float* __restrict__ W3,
-                                                          const Seg2 sg, float* __restrict__ dq0,
-                                                          float* __restrict__ dq1, int b) {
+// dq for block z: dq[k(i,l)] = E[i][l] - E[l][i] for i < l < r. One
+// workgroup per 32 x 32 tile (I, L), I <= L: the mirror tile (L, I) is read
+// row-wise and transposed through LDS.
+__global__ void __launch_bounds__(kThreads) k_pack_asym(const float* __restrict__ E, const Seg2 sg,
+                                                       float* __restrict__ dq0, float* __restrict__ dq1, int b) {
   __shared__ float mir[32][33];
   const int z = blockIdx.z;
   const int I = blockIdx.y, Lt = blockIdx.x;
@@ -264,36 +282,112 @@ __global__ void __launch_bounds__(kThreads) k_cnp_bwd_pack(const float* __restri
   const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
   const int64_t base = static_cast<int64_t>(z) * b * b;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  // mirror tile rows l in (L*32 ..), columns i in (I*32 ..)
   for (int k = ty; k < 32; k += 8) {
     const int l = Lt * 32 + k, i = I * 32 + tx;
-    float v = 0.f;
-    if (l < b && i < b) {
-      const int64_t o = base + static_cast<int64_t>(l) * b + i;
-      v = 2.f * U[o] - 2.f * W1[o] + 2.f * W2[o] - W3[o];
-    }
-    mir[k][tx] = v;
+    mir[k][tx] = (l < b && i < b) ? E[base + static_cast<int64_t>(l) * b + i] : 0.f;
   }
   __syncthreads();
   float* dqz = dq + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
   for (int k = ty; k < 32; k += 8) {
     const int i = I * 32 + k, l = Lt * 32 + tx;
-    if (i < l && l < r) {
+    if (i < l && l < r) dqz[tri_index(i, l, r)] = E[base + static_cast<int64_t>(i) * b + l] - mir[tx][k];
+  }
+}
+
+// part[0][o] + part[1][o] + ... added in split order; four loads in flight.
+__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int nsplit, int64_t stride, int64_t o) {
+  float a = 0.f;
+  int sp = 0;
+  for (; sp + 4 <= nsplit; sp += 4) {
+    const float x0 = part[(sp + 0) * stride + o], x1 = part[(sp + 1) * stride + o];
+    const float x2 = part[(sp + 2) * stride + o], x3 = part[(sp + 3) * stride + o];
+    a += x0;
+    a += x1;
+    a += x2;
+    a += x3;
+  }
+  for (; sp < nsplit; ++sp) a += part[sp * stride + o];
+  return a;
+}
+
+// U = sum of the split partials (fixed order), written as its symmetric and
+// skew parts Us = (U + U^T) / 2, Uk = (U - U^T) / 2 (float, and bfloat16
+// copies when requested). One workgroup per tile pair (I, L), I <= L.
+__global__ void __launch_bounds__(kThreads) k_reduce_symskew(const float* __restrict__ part, int nsplit, int b,
+                                                            int64_t blocks_elems, float* __restrict__ Us,
+                                                            float* __restrict__ Uk, uint16_t* __restrict__ Ush,
+                                                            uint16_t* __restrict__ Ukh) {
+  __shared__ float ta[32][33];
+  __shared__ float tb[32][33];
+  const int z = blockIdx.z, I = blockIdx.y, Lt = blockIdx.x;
+  if (I > Lt) return;
+  const int64_t base = static_cast<int64_t>(z) * b * b;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int k = ty; k < 32; k += 8) {
+    const int i = I * 32 + k, l = Lt * 32 + tx;    // tile (I, L) row-wise
+    const int l2 = Lt * 32 + k, i2 = I * 32 + tx;  // tile (L, I) row-wise
+    float a = 0.f, m = 0.f;
+    if (i < b && l < b) a = sum_splits(part, nsplit, blocks_elems, base + static_cast<int64_t>(i) * b + l);
+    if (l2 < b && i2 < b) m = sum_splits(part, nsplit, blocks_elems, base + static_cast<int64_t>(l2) * b + i2);
+    ta[k][tx] = a;  // U[i][l]
+    tb[k][tx] = m;  // U[l2][i2]
+  }
+  __syncthreads();
+  // tile (I, L): U[i][l] and U[l][i] = tb[l - L*32][i - I*32]
+  for (int k = ty; k < 32; k += 8) {
+    const int i = I * 32 + k, l = Lt * 32 + tx;
+    if (i < b && l < b) {
+      const float u = ta[k][tx], ut = tb[tx][k];
       const int64_t o = base + static_cast<int64_t>(i) * b + l;
-      const float a = 2.f * U[o] - 2.f * W1[o] + 2.f * W2[o] - W3[o];
-      dqz[tri_index(i, l, r)] = a - mir[tx][k];
+      Us[o] = 0.5f * (u + ut);
+      Uk[o] = 0.5f * (u - ut);
+      if (Ush) Ush[o] = f32_to_bf16(0.5f * (u + ut));
+      if (Ukh) Ukh[o] = f32_to_bf16(0.5f * (u - ut));
+    }
+    const int l2 = Lt * 32 + k, i2 = I * 32 + tx;
+    if (I != Lt && l2 < b && i2 < b) {
+      const float u = tb[k][tx], ut = ta[tx][k];
+      const int64_t o = base + static_cast<int64_t>(l2) * b + i2;
+      Us[o] = 0.5f * (u + ut);
+      Uk[o] = 0.5f * (u - ut);
+      if (Ush) Ush[o] = f32_to_bf16(0.5f * (u + ut));
+      if (Ukh) Ukh[o] = f32_to_bf16(0.5f * (u - ut));
     }
   }
 }
 
-__global__ void k_reduce_splits(const float* __restrict__ part, int nsplit, int64_t n, float* __restrict__ out,
-                                uint16_t* __restrict__ out_h) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n) return;
-  float s = 0.f;
-  for (int k = 0; k < nsplit; ++k) s += part[static_cast<int64_t>(k) * n + e];
-  out[e] = s;
-  if (out_h) out_h[e] = f32_to_bf16(s);
+// H1 = 4 Uk - 2 (P1 - P1^T): tile pairs (I, L), I <= L, through LDS.
+__global__ void __launch_bounds__(kThreads) k_cnp_h1(const float* __restrict__ Uk, const float* __restrict__ P1, int b,
+                                                    float* __restrict__ Hf, uint16_t* __restrict__ Hh) {
+  __shared__ float ta[32][33];
+  __shared__ float tb[32][33];
+  const int z = blockIdx.z, I = blockIdx.y, Lt = blockIdx.x;
+  if (I > Lt) return;
+  const int64_t base = static_cast<int64_t>(z) * b * b;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int k = ty; k < 32; k += 8) {
+    const int i = I * 32 + k, l = Lt * 32 + tx;
+    const int l2 = Lt * 32 + k, i2 = I * 32 + tx;
+    ta[k][tx] = (i < b && l < b) ? P1[base + static_cast<int64_t>(i) * b + l] : 0.f;
+    tb[k][tx] = (l2 < b && i2 < b) ? P1[base + static_cast<int64_t>(l2) * b + i2] : 0.f;
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int i = I * 32 + k, l = Lt * 32 + tx;
+    if (i < b && l < b) {
+      const int64_t o = base + static_cast<int64_t>(i) * b + l;
+      const float v = 4.f * Uk[o] - 2.f * (ta[k][tx] - tb[tx][k]);
+      if (Hf) Hf[o] = v;
+      if (Hh) Hh[o] = f32_to_bf16(v);
+    }
+    const int l2 = Lt * 32 + k, i2 = I * 32 + tx;
+    if (I != Lt && l2 < b && i2 < b) {
+      const int64_t o = base + static_cast<int64_t>(l2) * b + i2;
+      const float v = 4.f * Uk[o] - 2.f * (tb[k][tx] - ta[tx][k]);
+      if (Hf) Hf[o] = v;
+      if (Hh) Hh[o] = f32_to_bf16(v);
+    }
+  }
 }
 
 inline unsigned grid1(int64_t n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
@@ -362,8 +456,8 @@ void fill_zero_f32(float* p, int64_t n, hipStream_t s) {
 void unpack_skew2(const float* q0, int64_t dim0, int n0, const float* q1, int64_t dim1, int n1, int b, float* Qf,
                   uint16_t* Qh, hipStream_t s) {
   const Seg2 sg{q0, q1, dim0, dim1, n0};
-  hipLaunchKernelGGL(k_unpack_skew, dim3(grid1(static_cast<int64_t>(b) * b), n0 + n1), dim3(kThreads), 0, s, sg, b,
-                     Qf, Qh);
+  const unsigned t = static_cast<unsigned>((b + 31) / 32);
+  hipLaunchKernelGGL(k_unpack_skew, dim3(t, t, static_cast<unsigned>(n0 + n1)), dim3(kThreads), 0, s, sg, b, Qf, Qh);
 }
 
 void cnp_mid(const float* Qf, const float* Q2f, uint16_t* Sh, float* Sf, int64_t n, hipStream_t s) {
@@ -382,16 +476,24 @@ void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int 
                        static_cast<float*>(g0), static_cast<float*>(g1));
 }
 
-void cnp_bwd_pack2(const float* U, const float* W1, const float* W2, const float* W3, int b, int64_t dim0, int n0,
-                   float* dq0, int64_t dim1, int n1, float* dq1, hipStream_t s) {
+void pack_asym2(const float* E, int b, int64_t dim0, int n0, float* dq0, int64_t dim1, int n1, float* dq1,
+                hipStream_t s) {
   const Seg2 sg{nullptr, nullptr, dim0, dim1, n0};
   const unsigned t = static_cast<unsigned>((b + 31) / 32);
-  hipLaunchKernelGGL(k_cnp_bwd_pack, dim3(t, t, static_cast<unsigned>(n0 + n1)), dim3(kThreads), 0, s, U, W1, W2,
-                     W3, sg, dq0, dq1, b);
+  hipLaunchKernelGGL(k_pack_asym, dim3(t, t, static_cast<unsigned>(n0 + n1)), dim3(kThreads), 0, s, E, sg, dq0, dq1,
+                     b);
 }
 
-void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t s) {
-  hipLaunchKernelGGL(k_reduce_splits, dim3(grid1(n)), dim3(kThreads), 0, s, part, nsplit, n, out, out_h);
+void reduce_symskew(const float* part, int nsplit, int b, int nblk, float* Us, float* Uk, uint16_t* Ush,
+                    uint16_t* Ukh, hipStream_t s) {
+  const unsigned t = static_cast<unsigned>((b + 31) / 32);
+  hipLaunchKernelGGL(k_reduce_symskew, dim3(t, t, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s, part, nsplit,
+                     b, static_cast<int64_t>(nblk) * b * b, Us, Uk, Ush, Ukh);
+}
+
+void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16_t* Hh, hipStream_t s) {
+  const unsigned t = static_cast<unsigned>((b + 31) / 32);
+  hipLaunchKernelGGL(k_cnp_h1, dim3(t, t, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s, Uk, P1, b, Hf, Hh);
 }
 
 }  // namespace poetx

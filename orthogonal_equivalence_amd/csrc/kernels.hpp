@@ -44,10 +44,19 @@ void cnp_mid(const float* Qf, const float* Q2f, uint16_t* Sh, float* Sf, int64_t
 void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int n0, void* g0, int n1, void* g1,
                  bool bf16, hipStream_t stream);
 
-// dQ = 2U - 2W1 + 2W2 - W3 and dq[k(i,l)] = dQ[i][l] - dQ[l][i] (i < l < r),
-// blocks [0, n0) into dq0 (side of width dim0), the next n1 into dq1.
-void cnp_bwd_pack2(const float* U, const float* W1, const float* W2, const float* W3, int b, int64_t dim0, int n0,
-                   float* dq0, int64_t dim1, int n1, float* dq1, hipStream_t stream);
+// dq[k(i,l)] = E[i][l] - E[l][i] (i < l < r): blocks [0, n0) into dq0 (side of
+// width dim0), the next n1 into dq1.
+void pack_asym2(const float* E, int b, int64_t dim0, int n0, float* dq0, int64_t dim1, int n1, float* dq1,
+                hipStream_t stream);
+
+// U = sum over nsplit partials part[s][z] (fixed order) for nblk b x b blocks,
+// written as Us = (U + U^T)/2 and Uk = (U - U^T)/2 (float; bfloat16 copies if
+// Ush / Ukh are not null).
+void reduce_symskew(const float* part, int nsplit, int b, int nblk, float* Us, float* Uk, uint16_t* Ush,
+                    uint16_t* Ukh, hipStream_t stream);
+
+// H1 = 4 Uk - 2 (P1 - P1^T) per block (float and/or bfloat16 outputs).
+void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16_t* Hh, hipStream_t stream);
 
 // Streaming block-diagonal product (block_apply.hip) on token-major bfloat16
 // rows: out[t][j*b + c] = (in[t][j*b + c] + sum_k in[t][j*b + k] *
@@ -66,8 +75,5 @@ bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint1
 int block_grad_splits(int64_t T, int64_t dim, int b);
 bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int64_t ld, int64_t T, int64_t dim,
                      int b, int nsplit, hipStream_t stream);
-
-// out[e] = sum_{s < nsplit} part[s * n + e] (fixed order); optional bf16 copy.
-void reduce_splits(const float* part, int nsplit, int64_t n, float* out, uint16_t* out_h, hipStream_t stream);
 
 }  // namespace poetx

@@ -166,24 +166,22 @@ CnpWs plan_cnp(const poetx_layer* L, int64_t bb, Carve& c) {
 }
 
 struct CnpBwdWs {
-  float *Qf, *Q2f, *W1, *UQ2, *W2, *W3;
-  uint16_t *Qh, *Q2h, *W1h, *UQ2h, *W2h;
+  float *Qf, *P1, *Hf, *F, *E;
+  uint16_t *Qh, *Hh, *Fh;
 };
 
 CnpBwdWs plan_cnp_bwd(const poetx_layer* L, int64_t bb, Carve& c) {
   CnpBwdWs w{};
   w.Qf = c.take<float>(bb);
-  w.Q2f = c.take<float>(bb);
-  w.W1 = c.take<float>(bb);
-  w.UQ2 = c.take<float>(bb);
-  w.W2 = c.take<float>(bb);
-  w.W3 = c.take<float>(bb);
+  w.P1 = c.take<float>(bb);
+  w.F = c.take<float>(bb);
+  w.E = c.take<float>(bb);
   if (is_bf16(L)) {
     w.Qh = c.take<uint16_t>(bb);
-    w.Q2h = c.take<uint16_t>(bb);
-    w.W1h = c.take<uint16_t>(bb);
-    w.UQ2h = c.take<uint16_t>(bb);
-    w.W2h = c.take<uint16_t>(bb);
+    w.Hh = c.take<uint16_t>(bb);
+    w.Fh = c.take<uint16_t>(bb);
+  } else {
+    w.Hf = c.take<float>(bb);
   }
   return w;
 }
@@ -204,8 +202,8 @@ struct BwdWs {
   void *bufA, *bufB;
   int32_t* inv_r;
   float *part_r, *part_p;
-  float* U;           // reduced dG (side R) and dH (side P), one batch
-  uint16_t* Uh;
+  float *Us, *Uk;     // symmetric / skew parts of dG (side R) and dH (side P)
+  uint16_t *Ush, *Ukh;
   size_t cnp_off;     // the CNP adjoint scratch starts here
 };
 
@@ -219,8 +217,11 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.inv_r = c.take<int32_t>(L->m);
   w.part_r = c.take<float>(static_cast<int64_t>(token_split(L, R, Tn).nsplit) * block_elems(R));
   w.part_p = c.take<float>(static_cast<int64_t>(token_split(L, P, Tn).nsplit) * block_elems(P));
-  w.U = c.take<float>(block_elems(R) + block_elems(P));
-  w.Uh = c.take<uint16_t>(block_elems(R) + block_elems(P));
+  const int64_t all = block_elems(R) + block_elems(P);
+  w.Us = c.take<float>(all);
+  w.Uk = c.take<float>(all);
+  w.Ush = c.take<uint16_t>(all);
+  w.Ukh = c.take<uint16_t>(all);
   w.cnp_off = c.off;
   Carve m(nullptr);
   plan_cnp_bwd(L, cnp_batch_elems(L), m);
@@ -388,7 +389,7 @@ bool block_token_grad(const poetx_layer* L, const Side& s, int64_t T, const void
 // Batched b x b product C = alpha A B^T-form (see gemm.hpp) with optional
 // addend and bf16 copy, over the nblk blocks of one side.
 bool sq(const poetx_layer* L, const Group& g, const void* A, int am, const void* B, int bm, float* C, uint16_t* C2,
-        float alpha, const float* D, hipStream_t st) {
+        float alpha, const float* D, hipStream_t st, float beta = 1.f) {
   GemmDesc d;
   const Side s{0, g.b, g.n0 + g.n1};
   const int64_t bb = static_cast<int64_t>(s.b) * s.b;
@@ -407,7 +408,7 @@ bool sq(const poetx_layer* L, const Group& g, const void* A, int am, const void*
   d.D = D;
   d.ldd = s.b;
   d.sD = bb;
-  d.beta = D ? 1.f : 0.f;
+  d.beta = D ? beta : 0.f;
   d.alpha = alpha;
   d.M = d.N = d.K = s.b;
   d.batch = s.nblk;
@@ -435,36 +436,36 @@ bool cnp_group(const poetx_layer* L, const Group& g, const float* q0, const floa
   return true;
 }
 
-// dq from the reduced block gradients U (dL/dG) of a group. With Q skew,
-// the adjoint of G = (I+Q)(I+Q+Q^2+Q^3) collapses to sums of Q^a U Q^c whose
-// coefficient depends on a + c only: dL/dQ = 2U - 2 W1 + 2 W2 - W3 with
-// W1 = QU + UQ, W2 = Q W1 + U Q^2, W3 = Q W2 + (U Q^2) Q; then
-// dq_k = dL/dQ[i][l] - dL/dQ[l][i].
-bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const float* q1, const float* Uf,
-                   const uint16_t* Uh, float* dq0, float* dq1, void* cnp_ws, hipStream_t st) {
+// dq from the block gradients U = dL/dG of a group, given as Us = (U+U^T)/2
+// and Uk = (U-U^T)/2. The packed gradient only sees the skew part of dL/dQ,
+// and with Q skew the adjoint of G = (I+Q)(I+Q+Q^2+Q^3) (a sum of
+// Q^a U Q^c with coefficients 2, -2, 2, -1 for a + c = 0..3) reduces to
+//   dq = pack(E),  E = 2 Uk + Q F,  F = -4 Us + 2 Uk Q + Q H1,
+//   H1 = 4 Uk - 2 (Q Us - (Q Us)^T),
+// four b x b products per block (pack(M)[k(i,l)] = M[i][l] - M[l][i]).
+bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const float* q1, const float* Us,
+                   const float* Uk, const uint16_t* Ush, const uint16_t* Ukh, float* dq0, float* dq1, void* cnp_ws,
+                   hipStream_t st) {
   Carve c(cnp_ws);
   CnpBwdWs w = plan_cnp_bwd(L, g.elems(), c);
   const bool bf = is_bf16(L);
+  const int nb = g.n0 + g.n1;
   unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
   const void* Q = bf ? static_cast<const void*>(w.Qh) : w.Qf;
-  const void* U = bf ? static_cast<const void*>(Uh) : Uf;
-  bool ok = sq(L, g, Q, A_KCONTIG, Q, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st);
-  const void* Q2 = bf ? static_cast<const void*>(w.Q2h) : w.Q2f;
-  // W1 = Q U + U Q
-  ok = ok && sq(L, g, Q, A_KCONTIG, U, B_NCONTIG, w.W1, nullptr, 1.f, nullptr, st);
-  ok = ok && sq(L, g, U, A_KCONTIG, Q, B_KCONTIG, w.W1, bf ? w.W1h : nullptr, -1.f, w.W1, st);
-  const void* W1 = bf ? static_cast<const void*>(w.W1h) : w.W1;
-  // U Q2 (Q2 symmetric)
-  ok = ok && sq(L, g, U, A_KCONTIG, Q2, B_KCONTIG, w.UQ2, bf ? w.UQ2h : nullptr, 1.f, nullptr, st);
-  const void* UQ2 = bf ? static_cast<const void*>(w.UQ2h) : w.UQ2;
-  // W2 = Q W1 + U Q2
-  ok = ok && sq(L, g, Q, A_KCONTIG, W1, B_NCONTIG, w.W2, bf ? w.W2h : nullptr, 1.f, w.UQ2, st);
-  const void* W2 = bf ? static_cast<const void*>(w.W2h) : w.W2;
-  // W3 = Q W2 + (U Q2) Q
-  ok = ok && sq(L, g, Q, A_KCONTIG, W2, B_NCONTIG, w.W3, nullptr, 1.f, nullptr, st);
-  ok = ok && sq(L, g, UQ2, A_KCONTIG, Q, B_KCONTIG, w.W3, nullptr, -1.f, w.W3, st);
+  const void* UsOp = bf ? static_cast<const void*>(Ush) : Us;
+  const void* UkOp = bf ? static_cast<const void*>(Ukh) : Uk;
+  // P1 = Q Us (Us symmetric: B rows = Us rows)
+  bool ok = sq(L, g, Q, A_KCONTIG, UsOp, B_KCONTIG, w.P1, nullptr, 1.f, nullptr, st);
+  cnp_h1(Uk, w.P1, g.b, nb, bf ? nullptr : w.Hf, bf ? w.Hh : nullptr, st);
+  const void* H1 = bf ? static_cast<const void*>(w.Hh) : w.Hf;
+  // F = 2 Uk Q - 4 Us  (Uk Q = -Uk Q^T: B rows = Q rows, alpha = -2), then += Q H1
+  ok = ok && sq(L, g, UkOp, A_KCONTIG, Q, B_KCONTIG, w.F, nullptr, -2.f, Us, st, -4.f);
+  ok = ok && sq(L, g, Q, A_KCONTIG, H1, B_NCONTIG, w.F, bf ? w.Fh : nullptr, 1.f, w.F, st, 1.f);
+  const void* F = bf ? static_cast<const void*>(w.Fh) : w.F;
+  // E = 2 Uk + Q F
+  ok = ok && sq(L, g, Q, A_KCONTIG, F, B_NCONTIG, w.E, nullptr, 1.f, Uk, st, 2.f);
   if (!ok) return false;
-  cnp_bwd_pack2(Uf, w.W1, w.W2, w.W3, g.b, g.dim0, g.n0, dq0, g.dim1, g.n1, dq1, st);
+  pack_asym2(w.E, g.b, g.dim0, g.n0, dq0, g.dim1, g.n1, dq1, st);
   return true;
 }
 
@@ -700,14 +701,17 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   {
     ProfScope p("cnp_bwd", stream);
     const bool bf = is_bf16(L);
-    reduce_splits(w.part_r, spR.nsplit, block_elems(R), w.U, bf ? w.Uh : nullptr, stream);
-    reduce_splits(w.part_p, spP.nsplit, block_elems(P), w.U + block_elems(R), bf ? w.Uh + block_elems(R) : nullptr,
-                  stream);
+    const int64_t eR = block_elems(R);
+    reduce_symskew(w.part_r, spR.nsplit, R.b, R.nblk, w.Us, w.Uk, bf ? w.Ush : nullptr, bf ? w.Ukh : nullptr,
+                   stream);
+    reduce_symskew(w.part_p, spP.nsplit, P.b, P.nblk, w.Us + eR, w.Uk + eR, bf ? w.Ush + eR : nullptr,
+                   bf ? w.Ukh + eR : nullptr, stream);
     if (R.b == P.b) {
-      ok = ok && cnp_bwd_group(L, group_of(R, P), q_r, q_p, w.U, w.Uh, dq_r, dq_p, cnp_ws, stream);
+      ok = ok && cnp_bwd_group(L, group_of(R, P), q_r, q_p, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, dq_p, cnp_ws, stream);
     } else {
-      ok = ok && cnp_bwd_group(L, group_of(R), q_r, nullptr, w.U, w.Uh, dq_r, nullptr, cnp_ws, stream);
-      ok = ok && cnp_bwd_group(L, group_of(P), q_p, nullptr, w.U + block_elems(R), w.Uh + block_elems(R), dq_p,
+      ok = ok && cnp_bwd_group(L, group_of(R), q_r, nullptr, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, nullptr, cnp_ws,
+                               stream);
+      ok = ok && cnp_bwd_group(L, group_of(P), q_p, nullptr, w.Us + eR, w.Uk + eR, w.Ush + eR, w.Ukh + eR, dq_p,
                                nullptr, cnp_ws, stream);
     }
   }
