@@ -90,6 +90,13 @@ POETX_API int poetx_abi_version(void);
 /* Static message for a status code; never NULL. */
 POETX_API const char* poetx_strerror(int status);
 
+/* Name and description of the HIP error behind the last POETX_EHIP returned
+ * to the calling thread ("hipSuccess: no error" if there was none); never
+ * NULL, valid until the thread's next call. The compute entry points clear
+ * HIP's per-thread last-error state before they launch, so POETX_EHIP reports
+ * errors raised by their own launches only. */
+POETX_API const char* poetx_last_hip_error(void);
+
 /* Number of packed float parameters of one side: sum over its blocks of
  * r(r-1)/2 (section "3. Cayley-Neumann 参数化优化"). 0 for an invalid layer. */
 POETX_API size_t poetx_packed_len(const poetx_layer* L, int side);

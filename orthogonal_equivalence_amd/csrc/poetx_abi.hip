@@ -24,6 +24,7 @@
 #include <algorithm>
 #include <initializer_list>
 #include <mutex>
+#include <string>
 #include <vector>
 
 using namespace poetx;
@@ -469,9 +470,18 @@ bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const 
   return true;
 }
 
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local std::string g_last_hip_msg;
+
+// Drops a HIP error left pending by earlier calls of other code on this
+// thread, so that launch_status() sees only this entry point's launches.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 int launch_status() {
   const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? POETX_OK : POETX_EHIP;
+  if (e == hipSuccess) return POETX_OK;
+  g_last_hip = e;
+  return POETX_EHIP;
 }
 
 int check_ws(const poetx_layer* L, int64_t T, int op, const void* ws, size_t ws_bytes) {
@@ -487,6 +497,11 @@ int check_ws(const poetx_layer* L, int64_t T, int op, const void* ws, size_t ws_
 extern "C" {
 
 int poetx_abi_version(void) { return POETX_ABI_VERSION; }
+
+const char* poetx_last_hip_error(void) {
+  g_last_hip_msg = std::string(hipGetErrorName(g_last_hip)) + ": " + hipGetErrorString(g_last_hip);
+  return g_last_hip_msg.c_str();
+}
 
 const char* poetx_strerror(int status) {
   switch (status) {
@@ -532,6 +547,7 @@ int poetx_cnp_build(const poetx_layer* L, const float* q_r, const float* q_p, vo
                         static_cast<const void*>(g_p)})
     if (p && !aligned16(p)) return POETX_EINVAL;
   if (const int e = check_ws(L, 0, POETX_OP_CNP_BUILD, ws, ws_bytes)) return e;
+  clear_pending_error();
   bool ok = true;
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   if (q_r && q_p && R.b == P.b) {
@@ -561,6 +577,7 @@ int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_sc
   const bool i8 = L->w_dtype == POETX_I8;
   if (i8 && (!w_scale || !wscale_p)) return POETX_EINVAL;
   const int es = w_size(L);
+  clear_pending_error();
   {
     ProfScope p("prepare_permute", stream);
     if (!gather_cols(w0, L->n, perm_r, wp, L->n, nullptr, perm_p, L->n, L->m, es, stream))
@@ -583,6 +600,7 @@ int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   const bool i8 = L->w_dtype == POETX_I8;
   if (i8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_FORWARD, ws, ws_bytes)) return e;
+  clear_pending_error();
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   const int es = act_size(L);
   Carve c(ws);
@@ -634,6 +652,7 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
   if (!ptrs_ok({dq_r, dq_p})) return POETX_EINVAL;
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  clear_pending_error();
   if (T == 0) {
     fill_zero_f32(dq_r, packed_len(R), stream);
     fill_zero_f32(dq_p, packed_len(P), stream);
@@ -726,6 +745,7 @@ int poetx_merge(const poetx_layer* L, const void* wpt, const int32_t* perm_r, co
   if (!ptrs_ok({wpt, perm_r, perm_p, g_r, g_p, w0, q_r, q_p})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8) return POETX_EUNSUPPORTED;
   if (const int e = check_ws(L, 0, POETX_OP_MERGE, ws, ws_bytes)) return e;
+  clear_pending_error();
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   Carve c(ws);
   MergeWs w = plan_merge(L, c);

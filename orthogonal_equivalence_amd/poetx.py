@@ -10,6 +10,13 @@ kernels; importing this module fails if the library is not built.
 import ctypes
 import os
 
+# torch first: its libraries load the HIP runtime it ships (soname
+# libamdhip64.so.7), which then also satisfies libpoetx.so's dependency, so the
+# process holds one HIP runtime. Loaded the other way round, libpoetx.so would
+# pull in the system runtime and torch a second one, and the two need not
+# agree on the devices.
+import torch  # noqa: F401,E402
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpoetx.so")
 if not os.path.exists(LIB_PATH):
@@ -23,7 +30,7 @@ POETX_SIDE_R, POETX_SIDE_P = 0, 1
  POETX_OP_MERGE) = 0, 1, 2, 3, 4
 
 EXPORTED = [
-    "poetx_abi_version", "poetx_strerror", "poetx_packed_len", "poetx_gbuf_bytes",
+    "poetx_abi_version", "poetx_strerror", "poetx_last_hip_error", "poetx_packed_len", "poetx_gbuf_bytes",
     "poetx_saved_bytes", "poetx_wbuf_bytes", "poetx_workspace_bytes", "poetx_cnp_build",
     "poetx_weight_prepare", "poetx_forward", "poetx_backward", "poetx_merge",
     "poetx_profile_enable", "poetx_profile_count", "poetx_profile_get",
@@ -44,7 +51,10 @@ def make_layer(m, n, b_r, b_p, act="bf16", weight="bf16"):
 
 class PoetxError(RuntimeError):
     def __init__(self, fn, status):
-        super().__init__(f"{fn}: {poetx_strerror(status)} (status {status})")
+        msg = f"{fn}: {poetx_strerror(status)} (status {status})"
+        if status == POETX_EHIP:
+            msg += f" [{poetx_last_hip_error()}]"
+        super().__init__(msg)
         self.status = status
 
 
@@ -55,6 +65,7 @@ _SZ = ctypes.c_size_t
 _sig = {
     "poetx_abi_version": (ctypes.c_int, []),
     "poetx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "poetx_last_hip_error": (ctypes.c_char_p, []),
     "poetx_packed_len": (_SZ, [_L, ctypes.c_int]),
     "poetx_gbuf_bytes": (_SZ, [_L, ctypes.c_int]),
     "poetx_saved_bytes": (_SZ, [_L, _I64]),
@@ -87,7 +98,6 @@ def _ptr(x):
 
 def _stream(s):
     if s is None:
-        import torch
         return torch.cuda.current_stream().cuda_stream
     if isinstance(s, int):
         return s
@@ -114,6 +124,10 @@ def poetx_abi_version():
 
 def poetx_strerror(status):
     return _lib.poetx_strerror(status).decode()
+
+
+def poetx_last_hip_error():
+    return _lib.poetx_last_hip_error().decode()
 
 
 def poetx_packed_len(L, side):

@@ -28,7 +28,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(px.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -131,3 +131,7 @@ def test_argument_errors_before_any_launch():
     with pytest.raises(px.PoetxError) as e:
         px.poetx_weight_prepare(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == px.POETX_EINVAL
+
+
+def test_last_hip_error_without_failure():
+    assert px.poetx_last_hip_error().startswith("hipSuccess")
