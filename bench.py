@@ -31,10 +31,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, seconds_hint=20.0):
-    """Time the float64 oracle on token samples of the workload and extrapolate
-    linearly in T (the oracle's cost is a fixed part - CNP maps, their
-    adjoints, the merge - plus a part proportional to the token count)."""
+def cpu_baseline(cfg, budget_s=30.0):
+    """Time the float64 oracle on the workload. Two token samples (256, 512)
+    give its cost as a fixed part (CNP maps, their adjoints) plus a part
+    proportional to the token count; if a whole step is predicted to fit the
+    budget it is then run on all of the workload's tokens and that time is
+    used, else the linear extrapolation is."""
     import numpy as np
     import oracle as O
     from orthogonal_equivalence_amd import synth
@@ -46,14 +48,17 @@ def cpu_baseline(cfg, seconds_hint=20.0):
     L = synth.make_layer(cfg, 0)
     W0 = O.dequantize(L["W0_raw"], L["w_scale"]) if cfg.weight == "i8" else L["W0"].astype(np.float64)
     args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
-    t_small, t_big = 256, 512
-    times = {}
-    for T in (t_small, t_big):
+
+    def fwd_bwd(T):
         A = synth.make_activations(cfg, 0, T=T)
         t0 = time.perf_counter()
         O.backward(A["X"], A["dZ"], *args)   # includes the forward
-        times[T] = time.perf_counter() - t0
-        log(f"[cpu_baseline] oracle fwd+bwd on {T} tokens: {times[T]:.2f} s")
+        dt = time.perf_counter() - t0
+        log(f"[cpu_baseline] oracle fwd+bwd on {T} tokens: {dt:.2f} s")
+        return dt
+
+    t_small, t_big = 256, 512
+    times = {T: fwd_bwd(T) for T in (t_small, t_big)}
     t_merge = 0.0
     if cfg.merge:
         t0 = time.perf_counter()
@@ -62,16 +67,126 @@ def cpu_baseline(cfg, seconds_hint=20.0):
         log(f"[cpu_baseline] oracle merge: {t_merge:.2f} s")
     per_tok = max((times[t_big] - times[t_small]) / (t_big - t_small), 0.0)
     fixed = max(times[t_small] - per_tok * t_small, 0.0)
-    step = fixed + per_tok * cfg.T + t_merge
-    return {
-        "value": cfg.T / step,
-        "unit": "tokens/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": (f"float64 oracle fwd+bwd on {t_small} and {t_big} tokens of the {cfg.name} workload"
-                   f"{' plus one full merge' if cfg.merge else ''}, extrapolated linearly in T to "
-                   f"{cfg.T} tokens ({step:.1f} s per step; {sum(times.values()) + t_merge:.1f} s measured)"),
+    predicted = fixed + per_tok * cfg.T
+    if predicted <= budget_s:
+        t_full = fwd_bwd(cfg.T)
+        step = t_full + t_merge
+        sample = (f"float64 oracle fwd+bwd on all {cfg.T} tokens of the {cfg.name} workload"
+                  f"{' plus one full merge' if cfg.merge else ''} ({step:.1f} s per step)")
+    else:
+        step = predicted + t_merge
+        sample = (f"float64 oracle fwd+bwd on {t_small} and {t_big} tokens of the {cfg.name} workload"
+                  f"{' plus one full merge' if cfg.merge else ''}, extrapolated linearly in T to "
+                  f"{cfg.T} tokens ({step:.1f} s per step; {sum(times.values()) + t_merge:.1f} s measured)")
+    return {"value": cfg.T / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "sample": sample}
+
+
+GEMM_SOURCES = ("gemm_dense.hip", "gemm.hpp", "common.hpp")
+
+
+def gemm_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "orthogonal_equivalence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per dense-product launch from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, each scaled by the same
+    counter's reading for a plain copy of known size), or None when there is
+    none for this workload or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm_dense_hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("#", " ")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != gemm_source_sha256():
+        log(f"[bench] {os.path.basename(path)} was taken on other kernel sources; traffic not reported")
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_work(cfg):
+    """(bytes, flops) each profiled step must move / compute at the layer's
+    shape: block-diagonal work only (never dense m x m or n x n rotations),
+    one pass over each operand, one G plane per CNP block."""
+    es = 4 if cfg.act == "f32" else 2
+    wes = {"f32": 4, "bf16": 2, "i8": 1}[cfg.weight]
+    T, m, n, br, bp = cfg.T, cfg.m, cfg.n, cfg.b_r, cfg.b_p
+    nr, np_ = -(-m // br), -(-n // bp)
+    pr = nr * br * (br - 1) // 2
+    pp = np_ * bp * (bp - 1) // 2
+    blk = nr * br * br + np_ * bp * bp
+    cube = nr * br ** 3 + np_ * bp ** 3
+    dense = (2.0 * T * m * n, es * T * m + wes * m * n + es * T * n)
+    w = {
+        "cnp_build": (4 * (pr + pp) + es * blk, 4.0 * cube),
+        "cnp_build_r": (4 * pr + es * nr * br * br, 4.0 * nr * br ** 3),
+        "cnp_build_p": (4 * pp + es * np_ * bp * bp, 4.0 * np_ * bp ** 3),
+        "gather_x": (2 * es * T * m, 0.0),
+        "apply_r_fwd": (2 * es * T * m, 2.0 * T * m * br),
+        "gemm_dense_fwd": (dense[1], dense[0]),
+        "apply_p_fwd": (2 * es * T * n, 2.0 * T * n * bp),
+        "scatter_z": (2 * es * T * n, 0.0),
+        "gather_dz": (2 * es * T * n, 0.0),
+        "apply_p_bwd": (2 * es * T * n, 2.0 * T * n * bp),
+        "grad_h": (2 * es * T * n + 4 * np_ * bp * bp, 2.0 * T * n * bp),
+        "gemm_dense_bwd": (dense[1], dense[0]),
+        "apply_r_bwd": (2 * es * T * m, 2.0 * T * m * br),
+        "grad_g": (2 * es * T * m + 4 * nr * br * br, 2.0 * T * m * br),
+        "scatter_dx": (2 * es * T * m, 0.0),
+        "cnp_bwd": (4 * blk + 8 * (pr + pp), 8.0 * cube),
+        "merge_left": (2 * wes * m * n, 2.0 * m * n * br),
+        "merge_transpose": (2 * wes * m * n, 0.0),
+        "merge_right": (2 * wes * m * n, 2.0 * m * n * bp),
+        "merge_scatter": (2 * wes * m * n, 0.0),
+        "prepare_permute": (2 * wes * m * n, 0.0),
+        "prepare_transpose": (2 * wes * m * n, 0.0),
     }
+    return w
+
+
+def kernel_roofline(cfg, per):
+    """Per profiled step: time, algorithmic rates and the fraction of the
+    binding roof, t_roof / t with t_roof = max(flops / MFMA peak, bytes / HBM peak)."""
+    peak_f = (PEAK_BF16_TFLOPS if cfg.act == "bf16" else PEAK_F32_TFLOPS) * 1e12
+    peak_b = PEAK_HBM_GBS * 1e9
+    work = algorithmic_work(cfg)
+    out = {}
+    for name, (tot, cnt) in sorted(per.items()):
+        if name not in work or cnt == 0:
+            continue
+        nbytes, flops = work[name]
+        t = tot / cnt * 1e-3
+        t_roof = max(flops / peak_f, nbytes / peak_b)
+        out[name] = {"ms": round(t * 1e3, 4), "bound": "mfma" if flops / peak_f > nbytes / peak_b else "hbm",
+                     "GB/s": round(nbytes / t / 1e9, 1), "TFLOP/s": round(flops / t / 1e12, 1),
+                     "frac": round(t_roof / t, 4)}
+    return out
+
+
+def copy_probe(mib):
+    """Plain device-to-device copies of a known size (the calibration for the
+    HBM byte counters: a profiler reads FETCH_SIZE / WRITE_SIZE off these)."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: 3 copies of {mib} MiB")
+    del src, dst
 
 
 def main():
@@ -82,6 +197,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run three plain copies of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -98,6 +215,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
     cfg = synth.CONFIGS[args.workload]
     log(f"[bench] workload {cfg.name}: T={cfg.T} m={cfg.m} n={cfg.n} b={cfg.b_r}/{cfg.b_p} "
         f"{cfg.act}/{cfg.weight} merge={cfg.merge}")
@@ -157,7 +276,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     achieved = flops_gemm / (g_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(cfg.name),
                 "kernel": "dense W0 product (gemm_dense_fwd and gemm_dense_bwd launches)",
                 "flops_per_launch": flops_gemm, "avg_launch_ms": round(g_ms, 4)}
 
@@ -207,6 +326,7 @@ def main():
         "merge_prepare_ms": round(ms_merge, 4),
         "tokens_per_s_merge_every_200": round(cfg.T / ((ms_fwd_bwd + ms_merge / 200) * 1e-3), 1),
         "kernels_ms": kernels,
+        "kernel_roofline": kernel_roofline(cfg, per),
         "torch_linear_fwd_bwd_ms": yard,
     }
     if not args.no_cpu_baseline:
