@@ -83,6 +83,111 @@ k_gather_cols_lds(const T* __restrict__ in, int64_t ld_in, const int32_t* __rest
   }
 }
 
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 16] (larger n waits for all)
+__device__ __forceinline__ void wait_vm16(int n) {
+  switch (n) {
+#define POETX_VM(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    POETX_VM(1) POETX_VM(2) POETX_VM(3) POETX_VM(4) POETX_VM(5) POETX_VM(6) POETX_VM(7) POETX_VM(8)
+    POETX_VM(9) POETX_VM(10) POETX_VM(11) POETX_VM(12) POETX_VM(13) POETX_VM(14) POETX_VM(15) POETX_VM(16)
+#undef POETX_VM
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Column gather, streaming version for rows of at most kPipeGroups * 8 * 256
+// elements and a multiple of 16 bytes. Each workgroup keeps its threads'
+// source indices in registers (16-bit, loaded once) and walks rows
+// blockIdx.x, blockIdx.x + gridDim.x, ...: a row is copied into one of two LDS
+// buffers with global_load_lds_dwordx4 while the previous row is gathered
+// from the other buffer and written with 16-byte stores.
+constexpr int kPipeGroups = 8;  // column groups of 8 per thread
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 2)
+k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
+                   T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
+                   const int32_t* __restrict__ cidx, int ncols, int64_t nrows) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row_bytes = ncols * static_cast<int>(sizeof(T));
+  const int nchunk = row_bytes >> 4;
+  const int ninst = (nchunk + 63) >> 6;  // 1 KB load instructions per row
+  const int ngroups = ncols >> 3;
+  uint32_t ix[kPipeGroups][4];
+#pragma unroll
+  for (int g = 0; g < kPipeGroups; ++g) {
+    const int grp = tid + g * kThreads;
+    if (grp < ngroups) {
+      const int4 i0 = reinterpret_cast<const int4*>(cidx)[2 * grp];
+      const int4 i1 = reinterpret_cast<const int4*>(cidx)[2 * grp + 1];
+      ix[g][0] = clamp_index(i0.x, ncols) | (clamp_index(i0.y, ncols) << 16);
+      ix[g][1] = clamp_index(i0.z, ncols) | (clamp_index(i0.w, ncols) << 16);
+      ix[g][2] = clamp_index(i1.x, ncols) | (clamp_index(i1.y, ncols) << 16);
+      ix[g][3] = clamp_index(i1.z, ncols) | (clamp_index(i1.w, ncols) << 16);
+    }
+  }
+  // store instructions this wave issues per row (its lane 0 has the lowest group)
+  int my_st = 0;
+#pragma unroll
+  for (int g = 0; g < kPipeGroups; ++g) my_st += (wave * 64 + g * kThreads < ngroups) ? (sizeof(T) == 4 ? 2 : 1) : 0;
+
+  auto issue = [&](int64_t r, char* buf) {
+    const int64_t src = rmap_in ? clamp_index(rmap_in[r], nrows) : r;
+    const char* sp = reinterpret_cast<const char*>(in + src * ld_in);
+    for (int i = wave; i < ninst; i += kThreads / 64) {
+      const int ch = i * 64 + lane;
+      if (ch < nchunk)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(sp + static_cast<int64_t>(ch) * 16),
+                                         (lds_void_t)(buf + i * 1024), 16, 0, 0);
+    }
+  };
+
+  int64_t r = blockIdx.x;
+  if (r >= nrows) return;
+  issue(r, lds_raw);
+  int buf = 0;
+  bool first = true;
+  for (; r < nrows; r += gridDim.x) {
+    // this row's loads are followed only by this wave's stores of the previous row
+    wait_vm16(first ? 0 : my_st);
+    first = false;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int64_t rn = r + gridDim.x;
+    if (rn < nrows) issue(rn, lds_raw + (buf ^ 1) * row_bytes);
+    const T* L = reinterpret_cast<const T*>(lds_raw + buf * row_bytes);
+    const int64_t dst = rmap_out ? clamp_index(rmap_out[r], nrows) : r;
+    T* op = out + dst * ld_out;
+    // all LDS reads of the row first (independent registers), then the stores
+    uint32_t w[kPipeGroups][8];
+#pragma unroll
+    for (int g = 0; g < kPipeGroups; ++g) {
+      if (tid + g * kThreads < ngroups) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[g][2 * e] = L[ix[g][e] & 0xffffu];
+          w[g][2 * e + 1] = L[ix[g][e] >> 16];
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kPipeGroups; ++g) {
+      const int grp = tid + g * kThreads;
+      if (grp < ngroups) {
+        T v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<T>(w[g][e]);
+        store8(op + static_cast<int64_t>(grp) * 8, v);
+      }
+    }
+    buf ^= 1;
+  }
+}
+
 // Fallback for rows wider than LDS: the gather reads global memory directly.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
@@ -396,7 +501,14 @@ template <typename T>
 void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
                    const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, hipStream_t s) {
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
-  if (row_bytes <= kRowLdsMax) {
+  if (row_bytes % 16 == 0 && ncols <= kPipeGroups * 8 * kThreads && 2 * row_bytes <= 128 * 1024) {
+    const int64_t lds = 2 * row_bytes;
+    const int per_cu = static_cast<int>(std::min<int64_t>(2, (160 * 1024) / lds));
+    const unsigned nwg = static_cast<unsigned>(std::min<int64_t>(nrows, 256 * per_cu));
+    hipLaunchKernelGGL(k_gather_rows_pipe<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(lds), s,
+                       static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
+                       static_cast<int>(ncols), nrows);
+  } else if (row_bytes <= kRowLdsMax) {
     int rows = static_cast<int>(kRowLdsBudget / row_bytes);
     rows = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
     const int chunk = (row_bytes % 16 == 0) ? 16 : 8;
