@@ -313,7 +313,7 @@ __global__ void __launch_bounds__(kThreads) k_unpack_skew(const Seg2 sg, int b, 
     if (i < b && l < b) {
       const int64_t o = base + static_cast<int64_t>(i) * b + l;
       if (I != Lt || i < l) {  // the rest of a diagonal tile is written below
-        Qf[o] = v;
+        if (Qf) Qf[o] = v;
         if (Qh) Qh[o] = f32_to_bf16(v);
       }
     }
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(kThreads) k_unpack_skew(const Seg2 sg, int b, 
     if (i < b && l < b && (I != Lt || i <= l)) {
       const float v = (i == l) ? 0.f : -tile[tx][k];
       const int64_t o = base + static_cast<int64_t>(l) * b + i;
-      Qf[o] = v;
+      if (Qf) Qf[o] = v;
       if (Qh) Qh[o] = f32_to_bf16(v);
     }
   }

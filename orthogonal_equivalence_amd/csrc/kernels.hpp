@@ -27,8 +27,8 @@ bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize,
 // Zero n floats (a fill kernel, safe inside captured graphs).
 void fill_zero_f32(float* p, int64_t n, hipStream_t stream);
 
-// Skew blocks from packed parameters: Qf[z] (b x b, float) and, if Qh is not
-// null, a bfloat16 copy. Blocks [0, n0) come from (q0, dim0), blocks
+// Skew blocks from packed parameters: Qf[z] (b x b, float) if Qf is not null
+// and a bfloat16 copy if Qh is not null. Blocks [0, n0) come from (q0, dim0), blocks
 // [n0, n0 + n1) from (q1, dim1). A side's block z has size
 // r = min(b, dim - z*b) and packed offset z*b(b-1)/2; entries outside r x r
 // are zero.
@@ -66,6 +66,37 @@ void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16
 // 128 or 256.
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
                       int64_t T, int64_t dim, int b, hipStream_t stream);
+
+// Batched b x b block products with fused epilogue (block_prod.hip), for
+// bfloat16 blocks with b a multiple of 128 (up to 1024). Per block z:
+//   acc = A1 B1^T + A2 B2^T   (A2 B2^T subtracted instead when neg2 != 0;
+//                               the second pair is optional)
+//   v1  = alpha acc + beta Ef + gamma Eh,   v2 = alpha2 acc + gamma2 Eh
+// with all matrices row-major [nblk][b][b] (Ef float, Eh and the operands
+// bfloat16, either addend optional). v1 goes to out1 (row-major) and/or
+// out1t (transposed), as float if out1_f32 else bfloat16; v2 to out2
+// (bfloat16, row-major). Outputs of blocks z >= z_split go to out1_hi /
+// out1t_hi at block z - z_split (two sides batched in one launch).
+struct BlockProdDesc {
+  const uint16_t* A1 = nullptr;
+  const uint16_t* B1 = nullptr;
+  const uint16_t* A2 = nullptr;
+  const uint16_t* B2 = nullptr;
+  int neg2 = 0;
+  int b = 0;
+  int nblk = 0;
+  float alpha = 1.f, beta = 0.f, gamma = 0.f, alpha2 = 0.f, gamma2 = 0.f;
+  const float* Ef = nullptr;
+  const uint16_t* Eh = nullptr;
+  void* out1 = nullptr;
+  void* out1t = nullptr;
+  int out1_f32 = 0;
+  void* out2 = nullptr;
+  int z_split = 1 << 30;
+  void* out1_hi = nullptr;
+  void* out1t_hi = nullptr;
+};
+bool block_prod_bf16(const BlockProdDesc& d, hipStream_t stream);
 
 // Token sums of the block gradients (block_grad.hip) for bfloat16 blocks of
 // 256 or 512: part[s][j][i][c] = sum over the tokens of split s of

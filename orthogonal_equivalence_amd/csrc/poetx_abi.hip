@@ -425,6 +425,39 @@ bool cnp_group(const poetx_layer* L, const Group& g, const float* q0, const floa
   CnpWs w = plan_cnp(L, g.elems(), c);
   const bool bf = is_bf16(L);
   unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
+  if (bf && g.b % 128 == 0) {
+    // two fused block products: Q2 = -Q Q^T with S = 2Q + Q2 in the epilogue,
+    // then G - I = S Q2 + 2Q + 2Q2 written as both planes
+    BlockProdDesc p;
+    p.A1 = w.Qh;
+    p.B1 = w.Qh;
+    p.b = g.b;
+    p.nblk = g.n0 + g.n1;
+    p.alpha = -1.f;
+    p.out1 = w.Q2h;
+    p.Eh = w.Qh;
+    p.alpha2 = -1.f;
+    p.gamma2 = 2.f;
+    p.out2 = w.Sh;
+    if (!block_prod_bf16(p, st)) return false;
+    const int64_t bb = static_cast<int64_t>(g.b) * g.b;
+    BlockProdDesc t;
+    t.A1 = w.Sh;
+    t.B1 = w.Q2h;  // Q2 symmetric: its rows are the rows of Q2^T
+    t.b = g.b;
+    t.nblk = g.n0 + g.n1;
+    t.alpha = 1.f;
+    t.beta = 2.f;
+    t.Ef = w.Qf;
+    t.gamma = 2.f;
+    t.Eh = w.Q2h;
+    t.out1 = g0;
+    t.out1t = g0 ? static_cast<uint16_t*>(g0) + g.n0 * bb : nullptr;
+    t.z_split = g.n0;
+    t.out1_hi = g1;
+    t.out1t_hi = g1 ? static_cast<uint16_t*>(g1) + g.n1 * bb : nullptr;
+    return block_prod_bf16(t, st);
+  }
   const void* Qop = bf ? static_cast<const void*>(w.Qh) : w.Qf;
   // Q Q = -Q Q^T: the NT product with B = Q and alpha = -1 (Q skew)
   if (!sq(L, g, Qop, A_KCONTIG, Qop, B_KCONTIG, w.Q2f, bf ? w.Q2h : nullptr, -1.f, nullptr, st)) return false;
@@ -451,6 +484,52 @@ bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const 
   CnpBwdWs w = plan_cnp_bwd(L, g.elems(), c);
   const bool bf = is_bf16(L);
   const int nb = g.n0 + g.n1;
+  if (bf && g.b % 128 == 0) {
+    // Same recurrence as below in three fused block products (Q skew, Us
+    // symmetric, Uk skew, so every right factor is read by rows):
+    //   H1/2 = 2 Uk - (Q Us + Us Q),          Q Us = NT(Q, Us), Us Q = -NT(Us, Q)
+    //   F    = -4 Us - 2 (NT(Uk, Q) + NT(Q, H1/2)),   written transposed
+    //   E    = 2 Uk + NT(Q, F^T)
+    unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, nullptr, w.Qh, st);
+    BlockProdDesc h;
+    h.A1 = w.Qh;
+    h.B1 = Ush;
+    h.A2 = Ush;
+    h.B2 = w.Qh;
+    h.neg2 = 1;
+    h.b = g.b;
+    h.nblk = nb;
+    h.alpha = -1.f;
+    h.beta = 2.f;
+    h.Ef = Uk;
+    h.out1 = w.Hh;
+    if (!block_prod_bf16(h, st)) return false;
+    BlockProdDesc f;
+    f.A1 = Ukh;
+    f.B1 = w.Qh;
+    f.A2 = w.Qh;
+    f.B2 = w.Hh;
+    f.b = g.b;
+    f.nblk = nb;
+    f.alpha = -2.f;
+    f.beta = -4.f;
+    f.Ef = Us;
+    f.out1t = w.Fh;
+    if (!block_prod_bf16(f, st)) return false;
+    BlockProdDesc e;
+    e.A1 = w.Qh;
+    e.B1 = w.Fh;
+    e.b = g.b;
+    e.nblk = nb;
+    e.alpha = 1.f;
+    e.beta = 2.f;
+    e.Ef = Uk;
+    e.out1 = w.E;
+    e.out1_f32 = 1;
+    if (!block_prod_bf16(e, st)) return false;
+    pack_asym2(w.E, g.b, g.dim0, g.n0, dq0, g.dim1, g.n1, dq1, st);
+    return true;
+  }
   unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
   const void* Q = bf ? static_cast<const void*>(w.Qh) : w.Qf;
   const void* UsOp = bf ? static_cast<const void*>(Ush) : Us;
