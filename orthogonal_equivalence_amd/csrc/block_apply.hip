@@ -16,6 +16,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace poetx {
 namespace {
 
@@ -138,8 +140,13 @@ bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint1
   if (T <= 0) return true;
   if (b != 64 && b != 128 && b != 256) return false;
   const int nblk = static_cast<int>((dim + b - 1) / b);
-  const int64_t target = 512;
-  int64_t wpb = (target + nblk - 1) / nblk;
+  // Workgroups resident at once on the 256 CUs: b = 256 is limited to two per
+  // CU by registers (8 waves of up to 128 VGPRs), b = 128 to four (registers
+  // and LDS), b = 64 to nine by LDS (eight used). Every workgroup streams the same number of tokens, and one
+  // more than fits would cost a whole second round: floor(resident / blocks)
+  // workgroups per block.
+  const int64_t resident = 256 * (b == 256 ? 2 : (b == 128 ? 4 : 8));
+  int64_t wpb = std::max<int64_t>(1, resident / nblk);
   int64_t tpw = (T + wpb - 1) / wpb;
   tpw = (tpw + TT - 1) / TT * TT;
   wpb = (T + tpw - 1) / tpw;
