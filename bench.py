@@ -143,6 +143,7 @@ def algorithmic_work(cfg):
         "scatter_z": (2 * es * T * n, 0.0),
         "gather_dz": (2 * es * T * n, 0.0),
         "apply_p_bwd": (2 * es * T * n, 2.0 * T * n * bp),
+        "fold_h_bwd": (2 * wes * m * n, 2.0 * m * n * bp),
         "grad_h": (2 * es * T * n + 4 * np_ * bp * bp, 2.0 * T * n * bp),
         "gemm_dense_bwd": (dense[1], dense[0]),
         "apply_r_bwd": (2 * es * T * m, 2.0 * T * m * br),

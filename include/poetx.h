@@ -161,7 +161,10 @@ POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
  *   q_r, q_p: the packed parameters the CNP buffers were built from.
  *   wp: permuted-frame weight from poetx_weight_prepare (m x n).
  * No W0 gradient exists (W0 is frozen). Outputs are overwritten, not
- * accumulated; T == 0 writes zero gradients. */
+ * accumulated; T == 0 writes zero gradients. When the weight is not int8 and
+ * m < T, the P-side product dY1 = dY2 H^T is not formed: the dense product
+ * takes dY2 and the weight Wp H (built in the workspace), which is the same
+ * dX2 = dY2 H^T Wp^T with fewer bytes moved. */
 POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const void* dz,
                    const int32_t* perm_r, const int32_t* perm_p,
                    const float* q_r, const float* q_p,

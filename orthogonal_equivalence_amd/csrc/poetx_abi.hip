@@ -201,12 +201,18 @@ FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
 
 struct BwdWs {
   void *bufA, *bufB;
+  void* wh;           // Wp H (m x n), when the backward folds H into the weight
   int32_t* inv_r;
   float *part_r, *part_p;
   float *Us, *Uk;     // symmetric / skew parts of dG (side R) and dH (side P)
   uint16_t *Ush, *Ukh;
   size_t cnp_off;     // the CNP adjoint scratch starts here
 };
+
+// dX2 = dY2 H^T Wp^T = dY2 (Wp H)^T: with a float or bf16 weight and fewer
+// weight rows than tokens it is cheaper to multiply the m x n weight by H once
+// than the T x n gradient by H^T (dH only needs dY2 and Y1, never dY1).
+bool fold_h(const poetx_layer* L, int64_t T) { return L->w_dtype != POETX_I8 && L->m < T; }
 
 BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   BwdWs w;
@@ -215,6 +221,7 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   const int64_t Tn = std::max<int64_t>(T, 1);
   w.bufA = c.take<char>(T * rowmax * act_size(L));
   w.bufB = c.take<char>(T * rowmax * act_size(L));
+  w.wh = fold_h(L, T) ? c.take<char>(L->m * L->n * w_size(L)) : nullptr;
   w.inv_r = c.take<int32_t>(L->m);
   w.part_r = c.take<float>(static_cast<int64_t>(token_split(L, R, Tn).nsplit) * block_elems(R));
   w.part_p = c.take<float>(static_cast<int64_t>(token_split(L, P, Tn).nsplit) * block_elems(P));
@@ -748,30 +755,39 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   const void* X1 = saved;
   const void* Y1 = static_cast<const char*>(saved) + T * L->m * es;
 
-  // P side: dY2 = dZ Phi^T, dY1 = dY2 H^T (times the column scales for int8
-  // weights, which belong to Wp's columns), dH = sum_t Y1^T dY2
+  // P side: dY2 = dZ Phi^T, dH = sum_t Y1^T dY2, and either dY1 = dY2 H^T
+  // (times the column scales for int8 weights, which belong to Wp's columns)
+  // for dX2 = dY1 Wp^T, or the fold dX2 = dY2 (Wp H)^T
+  const bool fold = fold_h(L, T);
   bool ok;
   {
     ProfScope p("gather_dz", stream);
     ok = gather_cols(dz, L->n, nullptr, w.bufA, L->n, nullptr, perm_p, L->n, T, es, stream);
-  }
-  {
-    ProfScope p("apply_p_bwd", stream);
-    ok = ok && block_apply(L, P, T, w.bufA, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
   }
   const Split spP = token_split(L, P, T);
   {
     ProfScope p("grad_h", stream);
     ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part_p, spP, stream);
   }
-  // dX2 = dY1 Wp^T
   GemmDesc d;
   d.dense = 1;
-  d.A = w.bufB;
+  if (fold) {
+    ProfScope p("fold_h_bwd", stream);
+    ok = ok && block_apply(L, P, L->m, wp, w.wh, g_p, 1, nullptr, stream);
+    d.A = w.bufA;
+    d.B = w.wh;
+    d.C = w.bufB;
+  } else {
+    ProfScope p("apply_p_bwd", stream);
+    ok = ok && block_apply(L, P, T, w.bufA, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
+    d.A = w.bufB;
+    d.B = wp;
+    d.C = w.bufA;
+  }
+  void* const dX2 = d.C;
+  void* const dX1 = fold ? w.bufA : w.bufB;
   d.lda = L->n;
-  d.B = wp;
   d.ldb = L->n;
-  d.C = w.bufA;
   d.ldc = L->m;
   d.M = static_cast<int>(T);
   d.N = static_cast<int>(L->m);
@@ -783,17 +799,17 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {
     ProfScope p("apply_r_bwd", stream);
-    ok = ok && block_apply(L, R, T, w.bufA, w.bufB, g_r, 0, nullptr, stream);
+    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream);
   }
   const Split spR = token_split(L, R, T);
   {
     ProfScope p("grad_g", stream);
-    ok = ok && block_token_grad(L, R, T, X1, w.bufA, w.part_r, spR, stream);
+    ok = ok && block_token_grad(L, R, T, X1, dX2, w.part_r, spR, stream);
   }
   {
     ProfScope p("scatter_dx", stream);
     inverse_perm(perm_r, w.inv_r, L->m, stream);
-    ok = ok && gather_cols(w.bufB, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
+    ok = ok && gather_cols(dX1, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
   }
   // dq_r, dq_p from the token sums dG, dH
   {

@@ -103,6 +103,8 @@ SMALL = [
     _cfg("xq_small", 520, 512, 768, 128, 128, "bf16", "i8", 25),
     # a single token
     _cfg("bf16_one_token", 1, 256, 512, 128, 128, "bf16", "bf16", 26),
+    # float32 with more tokens than weight rows: the backward folds H into the weight
+    _cfg("f32_fold", 300, 128, 192, 64, 64, "f32", "f32", 27),
 ]
 
 
@@ -336,3 +338,15 @@ def test_profile_log_records_every_step():
                  "apply_r_bwd", "grad_g", "cnp_bwd", "scatter_dx", "prepare_permute"):
         assert want in names, want
     assert all(px.poetx_profile_get(i)[1] >= 0.0 for i in range(len(names)))
+
+
+def test_profile_log_fold_path():
+    # more tokens than weight rows: the backward builds Wp H instead of dY2 H^T
+    cfg = _cfg("profile_fold", 640, 256, 384, 128, 128, "bf16", "bf16", 31)
+    px.poetx_profile_enable(1)
+    try:
+        _run(cfg)
+    finally:
+        px.poetx_profile_enable(0)
+    names = [px.poetx_profile_get(i)[0] for i in range(px.poetx_profile_count())]
+    assert "fold_h_bwd" in names and "apply_p_bwd" not in names, names
