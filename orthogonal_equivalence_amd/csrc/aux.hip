@@ -330,6 +330,88 @@ __global__ void __launch_bounds__(kThreads) k_unpack_skew(const Seg2 sg, int b, 
   }
 }
 
+// Same result for b a multiple of 64: one workgroup per 64 x 64 tile pair
+// (I, L), I <= L, with the upper tile staged in LDS and both the tile and its
+// mirror written with 16-byte stores; tile pairs with I > L are not launched.
+__global__ void __launch_bounds__(kThreads) k_unpack_skew64(const Seg2 sg, int b, int tiles, float* __restrict__ Qf,
+                                                           uint16_t* __restrict__ Qh) {
+  __shared__ float tile[64][65];
+  // blockIdx.x enumerates the pairs I <= L of one block row-major over I
+  int p = blockIdx.x, I = 0;
+  while (p >= tiles - I) {
+    p -= tiles - I;
+    ++I;
+  }
+  const int Lt = I + p;
+  const int z = blockIdx.y;
+  const float* q;
+  int64_t dim;
+  int zl;
+  seg_pick(sg, z, q, dim, zl);
+  const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
+  const float* qz = q + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
+  const int64_t base = static_cast<int64_t>(z) * b * b;
+  const int tid = threadIdx.x;
+  // U[a][c] = Q[I*64 + a][Lt*64 + c] for a row above the diagonal, else 0;
+  // all 16 loads of a thread in flight together
+  float u[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = I * 64 + (tid >> 6) + 4 * k, l = Lt * 64 + (tid & 63);
+    u[k] = (i < l && l < r) ? qz[tri_index(i, l, r)] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tile[(tid >> 6) + 4 * k][tid & 63] = u[k];
+  __syncthreads();
+  const bool diag = I == Lt;
+  if (diag) {
+    // complete the diagonal tile in LDS: lower half = -(upper half)^T
+    // (reads only touch a < c, writes only a > c)
+    float m[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int a = (tid >> 6) + 4 * k, c = tid & 63;
+      m[k] = a > c ? -tile[c][a] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int a = (tid >> 6) + 4 * k, c = tid & 63;
+      if (a > c) tile[a][c] = m[k];
+    }
+    __syncthreads();
+  }
+  // pass 0: tile (I, Lt) = LDS rows; pass 1 (off the diagonal): tile (Lt, I) = -LDS^T
+  for (int pass = 0; pass < (diag ? 1 : 2); ++pass) {
+    const int R0 = (pass == 0 ? I : Lt) * 64, C0 = (pass == 0 ? Lt : I) * 64;
+    const float sg = pass == 0 ? 1.f : -1.f;
+    if (Qh) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int ch = tid + it * kThreads;
+        const int row = ch >> 3, c8 = (ch & 7) * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = sg * (pass == 0 ? tile[row][c8 + e] : tile[c8 + e][row]);
+        *reinterpret_cast<uint4*>(Qh + base + static_cast<int64_t>(R0 + row) * b + C0 + c8) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+      }
+    }
+    if (Qf) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int ch = tid + it * kThreads;
+        const int row = ch >> 4, c4 = (ch & 15) * 4;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = sg * (pass == 0 ? tile[row][c4 + e] : tile[c4 + e][row]);
+        *reinterpret_cast<float4*>(Qf + base + static_cast<int64_t>(R0 + row) * b + C0 + c4) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
 __global__ void k_cnp_mid(const float* __restrict__ Qf, const float* __restrict__ Q2f, uint16_t* __restrict__ Sh,
                           float* __restrict__ Sf, int64_t n) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -387,32 +469,18 @@ __global__ void __launch_bounds__(kThreads) k_pack_asym(const float* __restrict_
   const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
   const int64_t base = static_cast<int64_t>(z) * b * b;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
   for (int k = ty; k < 32; k += 8) {
     const int l = Lt * 32 + k, i = I * 32 + tx;
     mir[k][tx] = (l < b && i < b) ? E[base + static_cast<int64_t>(l) * b + i] : 0.f;
   }
   __syncthreads();
   float* dqz = dq + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
+#pragma unroll
   for (int k = ty; k < 32; k += 8) {
     const int i = I * 32 + k, l = Lt * 32 + tx;
     if (i < l && l < r) dqz[tri_index(i, l, r)] = E[base + static_cast<int64_t>(i) * b + l] - mir[tx][k];
   }
-}
-
-// part[0][o] + part[1][o] + ... added in split order; four loads in flight.
-__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int nsplit, int64_t stride, int64_t o) {
-  float a = 0.f;
-  int sp = 0;
-  for (; sp + 4 <= nsplit; sp += 4) {
-    const float x0 = part[(sp + 0) * stride + o], x1 = part[(sp + 1) * stride + o];
-    const float x2 = part[(sp + 2) * stride + o], x3 = part[(sp + 3) * stride + o];
-    a += x0;
-    a += x1;
-    a += x2;
-    a += x3;
-  }
-  for (; sp < nsplit; ++sp) a += part[sp * stride + o];
-  return a;
 }
 
 // U = sum of the split partials (fixed order), written as its symmetric and
@@ -428,14 +496,49 @@ __global__ void __launch_bounds__(kThreads) k_reduce_symskew(const float* __rest
   if (I > Lt) return;
   const int64_t base = static_cast<int64_t>(z) * b * b;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int k = ty; k < 32; k += 8) {
+  // each thread sums 4 rows of tile (I, L) and 4 of tile (L, I) over the
+  // splits, in split order; a group of 4 splits puts all 32 loads in flight
+  int64_t oa[4], om[4];
+  bool va[4], vm[4];
+  float a[4], m[4];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const int k = ty + 8 * k4;
     const int i = I * 32 + k, l = Lt * 32 + tx;    // tile (I, L) row-wise
     const int l2 = Lt * 32 + k, i2 = I * 32 + tx;  // tile (L, I) row-wise
-    float a = 0.f, m = 0.f;
-    if (i < b && l < b) a = sum_splits(part, nsplit, blocks_elems, base + static_cast<int64_t>(i) * b + l);
-    if (l2 < b && i2 < b) m = sum_splits(part, nsplit, blocks_elems, base + static_cast<int64_t>(l2) * b + i2);
-    ta[k][tx] = a;  // U[i][l]
-    tb[k][tx] = m;  // U[l2][i2]
+    va[k4] = i < b && l < b;
+    vm[k4] = l2 < b && i2 < b;
+    oa[k4] = va[k4] ? base + static_cast<int64_t>(i) * b + l : base;
+    om[k4] = vm[k4] ? base + static_cast<int64_t>(l2) * b + i2 : base;
+    a[k4] = 0.f;
+    m[k4] = 0.f;
+  }
+  for (int sp = 0; sp < nsplit; sp += 4) {
+    float xa[4][4], xm[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* pp = part + static_cast<int64_t>(min(sp + u, nsplit - 1)) * blocks_elems;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        xa[u][k4] = pp[oa[k4]];
+        xm[u][k4] = pp[om[k4]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (sp + u < nsplit) {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          a[k4] += xa[u][k4];
+          m[k4] += xm[u][k4];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    ta[ty + 8 * k4][tx] = va[k4] ? a[k4] : 0.f;  // U[i][l]
+    tb[ty + 8 * k4][tx] = vm[k4] ? m[k4] : 0.f;  // U[l2][i2]
   }
   __syncthreads();
   // tile (I, L): U[i][l] and U[l][i] = tb[l - L*32][i - I*32]
@@ -568,6 +671,12 @@ void fill_zero_f32(float* p, int64_t n, hipStream_t s) {
 void unpack_skew2(const float* q0, int64_t dim0, int n0, const float* q1, int64_t dim1, int n1, int b, float* Qf,
                   uint16_t* Qh, hipStream_t s) {
   const Seg2 sg{q0, q1, dim0, dim1, n0};
+  if (b % 64 == 0) {
+    const int t = b / 64;
+    hipLaunchKernelGGL(k_unpack_skew64, dim3(static_cast<unsigned>(t * (t + 1) / 2), static_cast<unsigned>(n0 + n1)),
+                       dim3(kThreads), 0, s, sg, b, t, Qf, Qh);
+    return;
+  }
   const unsigned t = static_cast<unsigned>((b + 31) / 32);
   hipLaunchKernelGGL(k_unpack_skew, dim3(t, t, static_cast<unsigned>(n0 + n1)), dim3(kThreads), 0, s, sg, b, Qf, Qh);
 }
