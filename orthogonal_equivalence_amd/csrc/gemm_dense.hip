@@ -8,7 +8,9 @@
 //    owns 128 x 64 outputs as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.
 //  * Operand tiles go global -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging, no LDS write instructions), double-buffered, one barrier per
-//    K step; the next tile's loads are in flight during the current MFMAs.
+//    K step. The next stage's loads are spread over the current stage's four
+//    K groups (two 1 KB loads per group and wave) rather than issued in one
+//    burst, so that their LDS writes interleave with the fragment reads.
 //  * LDS rows are 128 bytes, unpadded; 16-byte chunk c of row r sits in slot
 //    c ^ swz(r) with swz(r) = (r & 7) ^ ((r >> 3) & 1), which keeps the
 //    fragment reads (32 rows, same chunk) free of bank conflicts whether the
@@ -79,6 +81,18 @@ __device__ __forceinline__ void load_tile(const bf16_t* __restrict__ g, int64_t 
   }
 }
 
+__device__ __forceinline__ void load_one(const bf16_t* __restrict__ g, int64_t ld, int row0, int rowlim, int k0,
+                                         char* lds, int wave, int lane, int i) {
+  const int sub = lane / kChunks, slot = lane % kChunks;
+  const int rbase = (wave * kInstPerTile + i) * kRowsPerInst;
+  const int r = rbase + sub;
+  const int c = slot ^ swz(r);
+  int gr = row0 + r;
+  gr = gr < rowlim ? gr : rowlim - 1;
+  const bf16_t* src = g + static_cast<int64_t>(gr) * ld + k0 + c * 8;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t)(lds + rbase * kRowBytes), 16, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -143,14 +157,20 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
     else wait_vmcnt<0>();
     __syncthreads();
     const int pf = it + NSTAGE - 1;
-    if (pf < nk) {
-      char* nxt = smem + (pf % NSTAGE) * kStageBytes;
-      load_tile(A, d.lda, m0, d.M, pf * BK, nxt, wave, lane);
-      load_tile(B, d.ldb, n0, d.N, pf * BK, nxt + kTileBytes, wave, lane);
-    }
+    char* nxt = smem + (pf % NSTAGE) * kStageBytes;
+    const int kpf = min(pf, nk - 1) * BK;
     const char* st = smem + (it % NSTAGE) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
+      // this K group's share of the next stage's loads (branch-free: the last
+      // iteration re-loads the last K slice into the idle stage)
+#pragma unroll
+      for (int u = 0; u < 2 * kInstPerTile / (BK / 16); ++u) {
+        const int i = kk * (2 * kInstPerTile / (BK / 16)) + u;
+        load_one(i < kInstPerTile ? A : B, i < kInstPerTile ? d.lda : d.ldb, i < kInstPerTile ? m0 : n0,
+                 i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
+                 i % kInstPerTile);
+      }
       bf16x8_t af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -166,6 +186,9 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
     }
   }
 
+  // the last iteration's re-load of the idle stage must land before the
+  // slabs reuse that LDS
+  wait_vmcnt<0>();
   // epilogue through per-wave LDS slabs (32 rows x 64 columns), 16-byte stores
   bf16_t* C = static_cast<bf16_t*>(d.C);
   const float* S = d.scale;
