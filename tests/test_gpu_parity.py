@@ -105,6 +105,13 @@ SMALL = [
     _cfg("bf16_one_token", 1, 256, 512, 128, 128, "bf16", "bf16", 26),
     # float32 with more tokens than weight rows: the backward folds H into the weight
     _cfg("f32_fold", 300, 128, 192, 64, 64, "f32", "f32", 27),
+    # the largest block size (general engine for the applies and token sums,
+    # 8 x 8 tiles per block in the CNP products)
+    _cfg("bf16_b1024", 200, 2048, 1024, 1024, 1024, "bf16", "bf16", 28),
+    # b = 512 with a short last block on R (1280 = 2*512 + 256)
+    _cfg("bf16_b512_ragged", 260, 1280, 1024, 512, 512, "bf16", "bf16", 29),
+    # b = 128 with short last blocks on both sides (704 = 5*128 + 64, 392 = 3*128 + 8)
+    _cfg("bf16_b128_ragged", 150, 704, 392, 128, 128, "bf16", "bf16", 32),
 ]
 
 
