@@ -170,12 +170,15 @@ def _round_robin(b):
     return rounds
 
 
-@pytest.mark.parametrize("act,s", [("f32", 2.0 ** -4), ("bf16", 0.25)])
-def test_packing_bit_exact(act, s):
+@pytest.mark.parametrize("act,s,b", [("f32", 2.0 ** -4, 16), ("bf16", 0.25, 16), ("bf16", 0.25, 128),
+                                      ("bf16", 0.25, 256)])
+def test_packing_bit_exact(act, s, b):
     # One perfect matching of nonzero q per block: every Q is a direct sum of
     # 2 x 2 rotation generators, so G - I has exactly representable entries
-    # diag -2s^2 + s^4 and off-diagonal +-(2s - 2s^3) at the matched pairs.
-    b, nblk = 16, 4
+    # diag -2s^2 + s^4 and off-diagonal +-(2s - 2s^3) at the matched pairs
+    # (as are Q^2, 2Q + Q^2 and their product on the way). b = 16 runs the
+    # general product engine, b = 128 and 256 the fused block products.
+    nblk = 4
     m = n = b * nblk
     dl = DeviceLayer(m, n, b, b, act, act, 8)
     rounds = _round_robin(b)
@@ -210,12 +213,14 @@ def _shift(b, k):
     return S
 
 
-@pytest.mark.parametrize("act", ["f32", "bf16"])
-def test_permutations_bit_exact(act):
+@pytest.mark.parametrize("act,b,T", [("f32", 16, 40), ("bf16", 16, 40), ("bf16", 256, 1100)])
+def test_permutations_bit_exact(act, b, T):
     # G_j, H_k cyclic shifts (0/1 matrices), W0 = I and small-integer X, dZ:
     # every value stays a small integer, so z and dx are exact index shuffles
     # of the inputs and any correct implementation matches bit for bit.
-    b, nblk, T = 16, 4, 40
+    # b = 256 with T > m runs the dedicated apply kernel and the backward's
+    # fold of H into the weight.
+    nblk = 4
     m = n = b * nblk
     rng = np.random.default_rng(5)
     perm_r, perm_p = rng.permutation(m), rng.permutation(n)
