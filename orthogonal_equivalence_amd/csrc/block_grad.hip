@@ -6,15 +6,18 @@
 // digest of arXiv:2603.05500, section "1. 输入中心化架构"). Blocks of 512
 // columns are four slice pairs.
 //
-// gfx950 design: the contraction runs over tokens, so both operands must be
-// token-contiguous for the MFMA fragments while the activations are stored
-// token-major. Each thread loads an 8-token x 8-feature block (eight 16-byte
-// row loads), transposes it in registers with v_perm_b32 and writes eight
-// 16-byte feature rows into a swizzled feature-major LDS stage; fragment reads
-// are then plain 16-byte LDS reads. 64-token sub-tiles, double-buffered, the
-// next sub-tile's global loads in flight during the current MFMAs. Eight waves
-// each hold a 128 x 64 region of the 256 x 256 fp32 partial in registers for
-// the whole chunk; one store of the partial at the end.
+// gfx950 design: the contraction runs over tokens while the activations are
+// stored token-major, so the MFMA fragments (8 consecutive tokens of one
+// feature per lane) are columns of the staged tiles. The tiles go global ->
+// LDS token-major with global_load_lds_dwordx4 (no register staging), and the
+// fragments are read with ds_read_b64_tr_b16: within each group of 16 lanes,
+// lane j receives element (j % 4) of the 8 bytes addressed by lane
+// 4e + j / 4, for e = 0..3. With lane i addressing token row t0 + i / 4 at
+// feature f0 + 4 (i % 4), lane j gets tokens t0 .. t0+3 of feature f0 + j;
+// two such reads make one fragment. 32-token sub-tiles in four stages (three
+// in flight ahead of the one being multiplied); eight waves each hold a
+// 128 x 64 region of the 256 x 256 fp32 partial in registers for the whole
+// chunk; one store of the partial at the end.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,39 +26,23 @@
 namespace poetx {
 namespace {
 
-constexpr int S = 256;       // slice width
-constexpr int TK = 64;       // tokens per sub-tile
-constexpr int NT = 512;      // threads
-constexpr int ROWB = TK * 2; // bytes per feature row of a stage (128)
-constexpr int TILE = S * ROWB;  // one operand stage (32 KB)
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_t;
 
-// Slot of 16-byte chunk c in feature row r (128-byte rows): c ^ swz(r).
-// Fragment reads touch 16 consecutive rows at one chunk: the bank group is
-// 8 * (r % 2) + slot, and swz takes 8 distinct values on the even and on the
-// odd rows of any aligned 16 (and on any aligned 8 rows). The transposed
-// writes of one instruction touch rows 8 * fb + e: swz = e ^ (fb & 7) spreads
-// them over all 8 slots of their parity.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 7); }
+constexpr int S = 256;              // slice width
+constexpr int TK = 32;              // tokens per sub-tile
+constexpr int NT = 512;             // threads
+constexpr int NSTAGE = 4;
+constexpr int ROWB = S * 2;         // bytes per token row of a tile (512)
+constexpr int TILE = TK * ROWB;     // one operand tile (16 KB)
+constexpr int STAGE = 2 * TILE;     // act + dout
 
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  uint32_t iw[32];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    iw[r * 4 + 0] = in[r].x;
-    iw[r * 4 + 1] = in[r].y;
-    iw[r * 4 + 2] = in[r].z;
-    iw[r * 4 + 3] = in[r].w;
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1;
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(iw[(2 * p + 1) * 4 + w], iw[(2 * p) * 4 + w], sel);
-    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
+// Slot of 16-byte chunk c (0..31) in token row r: c ^ (4 (r % 4)). A
+// transposed read touches rows t0 .. t0+3 (and t0+8 .. t0+11) at 4
+// consecutive chunks c0 .. c0+3 (c0 a multiple of 4): the XOR spreads the
+// four rows over all 16 bank groups, two cycles per read.
+__device__ __forceinline__ int slot(int r, int c) { return c ^ ((r & 3) << 2); }
 
 struct GradArgs {
   const bf16_t* act;
@@ -71,9 +58,15 @@ struct GradArgs {
   int nsplit;
 };
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroup -> (block, slice pair, split)
   const int pairs = g.slices * g.slices;
   int w = blockIdx.x;
@@ -89,42 +82,48 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
   const int64_t t_end = min(g.T, t_begin + g.tokens_per_wg);
   const int nsub = t_end > t_begin ? static_cast<int>((t_end - t_begin + TK - 1) / TK) : 0;
 
-  // staging: threads [0, 256) load act, [256, 512) load dout; each an 8x8 block
-  const int op = tid >> 8;                       // 0 act, 1 dout
-  const int q = tid & 255;
-  const int fb = q & 31, tb = q >> 5;            // feature block (8 features), token block (8 tokens)
-  const bf16_t* src = op == 0 ? g.act : g.dout;
-  const int fcol = (op == 0 ? a0 : d0) + fb * 8; // feature offset in the block
-  const bool fvalid = fcol < width;
-  uint4 reg[8];
-  auto gload = [&](int sub) {
+  // loads: a stage is 2 x 16 KB = 32 instructions of 1 KB, four per wave
+  // (two act, two dout); lane -> (row, chunk slot) of a 2-row instruction.
+  // Features past the block's width re-read its last 8 valid features (their
+  // outputs are stored as zeros), so every load stays inside the block even
+  // when a whole slice lies past a short block; tokens past the chunk re-read
+  // its last token (masked in the act fragments).
+  auto issue = [&](int sub, char* st) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t t = t_begin + static_cast<int64_t>(sub) * TK + tb * 8 + e;
-      if (fvalid && t < t_end)
-        reg[e] = *reinterpret_cast<const uint4*>(src + t * g.ld + blk0 + fcol);
-      else
-        reg[e] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint4 tr[8];
-    transpose8x8(reg, tr);
-    char* base = smem + stage * 2 * TILE + op * TILE;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = fb * 8 + e;
-      *reinterpret_cast<uint4*>(base + row * ROWB + ((tb ^ swz(row)) << 4)) = tr[e];
+    for (int u = 0; u < 4; ++u) {
+      const int op = u >> 1;                  // 0 act, 1 dout
+      const int inst = wave * 2 + (u & 1);    // 0..15 within the operand tile
+      const int row = inst * 2 + (lane >> 5);
+      const int sl = lane & 31;
+      const int c = sl ^ ((row & 3) << 2);    // the chunk that lands in slot sl
+      int f = (op ? d0 : a0) + c * 8;         // feature offset inside the block
+      f = f < width - 8 ? f : width - 8;
+      int64_t t = t_begin + static_cast<int64_t>(sub) * TK + row;
+      t = t < t_end ? t : t_end - 1;
+      const bf16_t* src = (op ? g.dout : g.act) + t * g.ld + blk0 + f;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       (lds_void_t)(st + op * TILE + inst * 1024), 16, 0, 0);
     }
   };
 
-  // wave region: rows (wave % 2) * 128 .. + 128, columns (wave / 2) * 64 .. + 64
+  // wave region: features rw0 .. rw0+127 of act, cw0 .. cw0+63 of dout
   constexpr int TMw = 4, TNw = 2;
   const int rw0 = (wave & 1) * 128, cw0 = (wave >> 1) * 64;
-  const int lrow = lane & 31;
-  // swz depends on row bits 0..5; wave regions start at multiples of 64, so a
-  // fragment row is 32 * t + lrow with t the tile index and only t's parity matters
-  const int sw0 = swz(lrow), sw1 = swz(32 + lrow);
+  // transposed-read address of this lane inside a 32-feature x 16-token
+  // fragment at (feature base fb, token base kb): group G = lane / 16 takes
+  // features fb + 16 (G % 2) .., tokens kb + 8 (G / 2) ..; lane i of the group
+  // addresses token row + i / 4, feature + 4 (i % 4)
+  const int grp = lane >> 4, li = lane & 15;
+  const int f_in = 16 * (grp & 1) + 4 * (li & 3);   // feature offset in the fragment
+  const int t_in = 8 * (grp >> 1) + (li >> 2);       // token offset in the fragment (first read)
+  auto tr_addr = [&](const char* tile, int fb, int t) {
+    const int f = fb + f_in;
+    const int c = f >> 3;
+    return reinterpret_cast<const v4i16*>(tile + t * ROWB + (slot(t, c) << 4) + (f & 7) * 2);
+  };
+  // the feature and first token this lane receives in the fragment (for masking)
+  const int tok_recv = 8 * (lane >> 5);
+
   f32x16_t acc[TMw][TNw];
 #pragma unroll
   for (int i = 0; i < TMw; ++i)
@@ -133,39 +132,104 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (nsub > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  for (int p = 0; p < NSTAGE - 1 && p < nsub; ++p) issue(p, smem + p * STAGE);
   for (int s = 0; s < nsub; ++s) {
-    if (s + 1 < nsub) gload(s + 1);
-    const char* A = smem + (s & 1) * 2 * TILE;
+    // stage s has landed once only the younger stages' loads remain
+    const int younger = min(NSTAGE - 2, nsub - 1 - s);
+    if (younger >= 2) wait_vmcnt<8>();
+    else if (younger == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    // LDS-only barrier (the loads in flight are waited for by count above)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* A = smem + (s % NSTAGE) * STAGE;
     const char* B = A + TILE;
-#pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
-      const int c = 2 * kk + (lane >> 5);
-      const int off0 = lrow * ROWB + ((c ^ sw0) << 4), off1 = lrow * ROWB + ((c ^ sw1) << 4);
-      bf16x8_t af[TMw], bfr[TNw];
+    const int valid = static_cast<int>(min(static_cast<int64_t>(TK), t_end - t_begin - static_cast<int64_t>(s) * TK));
+    // all fragments of the stage first, then the next loads, then the MFMAs.
+    // The transposed reads are issued from inline asm that waits for them
+    // itself (every output is complete when the asm statement ends): the
+    // compiler otherwise places a vmcnt(0) before each such read while direct
+    // loads are in flight, which would drain the prefetched stages. Rows +4
+    // (second half of a fragment) and +16 (second K group) keep the row
+    // swizzle, so they are immediate offsets of 2048 and 8192 bytes.
+    bf16x8_t af[TK / 16][TMw], bfr[TK / 16][TNw];
+    {
+      uint32_t ad[TMw], bd[TNw];
 #pragma unroll
       for (int i = 0; i < TMw; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(A + (rw0 + i * 32) * ROWB + ((i & 1) ? off1 : off0));
+        ad[i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tr_addr(A, rw0 + i * 32, t_in)));
 #pragma unroll
       for (int j = 0; j < TNw; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(B + (cw0 + j * 32) * ROWB + ((j & 1) ? off1 : off0));
+        bd[j] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tr_addr(B, cw0 + j * 32, t_in)));
+      typedef unsigned long long u64;
+      u64 ra[16], rb[8];
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:2048\n"
+          "ds_read_b64_tr_b16 %2, %16 offset:8192\n ds_read_b64_tr_b16 %3, %16 offset:10240\n"
+          "ds_read_b64_tr_b16 %4, %17\n ds_read_b64_tr_b16 %5, %17 offset:2048\n"
+          "ds_read_b64_tr_b16 %6, %17 offset:8192\n ds_read_b64_tr_b16 %7, %17 offset:10240\n"
+          "ds_read_b64_tr_b16 %8, %18\n ds_read_b64_tr_b16 %9, %18 offset:2048\n"
+          "ds_read_b64_tr_b16 %10, %18 offset:8192\n ds_read_b64_tr_b16 %11, %18 offset:10240\n"
+          "ds_read_b64_tr_b16 %12, %19\n ds_read_b64_tr_b16 %13, %19 offset:2048\n"
+          "ds_read_b64_tr_b16 %14, %19 offset:8192\n ds_read_b64_tr_b16 %15, %19 offset:10240\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(ra[4]), "=&v"(ra[5]), "=&v"(ra[6]),
+            "=&v"(ra[7]), "=&v"(ra[8]), "=&v"(ra[9]), "=&v"(ra[10]), "=&v"(ra[11]), "=&v"(ra[12]), "=&v"(ra[13]),
+            "=&v"(ra[14]), "=&v"(ra[15])
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+          : "memory");
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %8 offset:2048\n"
+          "ds_read_b64_tr_b16 %2, %8 offset:8192\n ds_read_b64_tr_b16 %3, %8 offset:10240\n"
+          "ds_read_b64_tr_b16 %4, %9\n ds_read_b64_tr_b16 %5, %9 offset:2048\n"
+          "ds_read_b64_tr_b16 %6, %9 offset:8192\n ds_read_b64_tr_b16 %7, %9 offset:10240\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3]), "=&v"(rb[4]), "=&v"(rb[5]), "=&v"(rb[6]),
+            "=&v"(rb[7])
+          : "v"(bd[0]), "v"(bd[1])
+          : "memory");
+      // ra[4 i + 2 kk + h]: fragment i, K group kk, half h (tokens 4h .. 4h+3),
+      // 16-bit element e of a half in bits 16 e; fragments are bit copies
+      if (valid < TK) {
+        // tokens past the chunk: zero their act values (the last sub-tile only)
+#pragma unroll
+        for (int kk = 0; kk < TK / 16; ++kk)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u64 keep = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kk * 16 + tok_recv + 4 * h + e < valid) keep |= 0xffffull << (16 * e);
+#pragma unroll
+            for (int i = 0; i < TMw; ++i) ra[4 * i + 2 * kk + h] &= keep;
+          }
+      }
+      typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int kk = 0; kk < TK / 16; ++kk) {
+#pragma unroll
+        for (int i = 0; i < TMw; ++i)
+          af[kk][i] = __builtin_bit_cast(bf16x8_t, u64x2{ra[4 * i + 2 * kk], ra[4 * i + 2 * kk + 1]});
+#pragma unroll
+        for (int j = 0; j < TNw; ++j)
+          bfr[kk][j] = __builtin_bit_cast(bf16x8_t, u64x2{rb[4 * j + 2 * kk], rb[4 * j + 2 * kk + 1]});
+      }
+    }
+    if (s + NSTAGE - 1 < nsub) issue(s + NSTAGE - 1, smem + ((s + NSTAGE - 1) % NSTAGE) * STAGE);
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; ++kk)
 #pragma unroll
       for (int i = 0; i < TMw; ++i)
 #pragma unroll
         for (int j = 0; j < TNw; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < nsub) lstore((s + 1) & 1);
-    __syncthreads();
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
   }
 
-  // partial for this split: rows a0 + i, columns d0 + c of the b x b block
-  // (entries outside a short block are exact zeros: their loads were zero)
+  // partial for this split: rows a0 + i, columns d0 + c of the b x b block;
+  // entries outside a short block are stored as zeros
   float* out = g.part + (static_cast<int64_t>(split) * g.nblk + blk) * g.b * g.b;
+  const int lrow = lane & 31;
 #pragma unroll
   for (int i = 0; i < TMw; ++i)
 #pragma unroll
@@ -174,7 +238,7 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
       for (int r = 0; r < 16; ++r) {
         const int row = a0 + rw0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int col = d0 + cw0 + j * 32 + lrow;
-        out[static_cast<int64_t>(row) * g.b + col] = acc[i][j][r];
+        out[static_cast<int64_t>(row) * g.b + col] = (row < width && col < width) ? acc[i][j][r] : 0.f;
       }
 }
 
@@ -182,14 +246,14 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
 
 // Splits of the token range: as many as fit one round of workgroups on the
 // 256 CUs (one 128 KB-LDS workgroup per CU), so that no partial second round
-// doubles the time; at least 4 sub-tiles of tokens per split.
+// doubles the time; at least 8 sub-tiles of tokens per split.
 int block_grad_splits(int64_t T, int64_t dim, int b) {
   if (b != 256 && b != 512) return 0;
   const int nblk = static_cast<int>((dim + b - 1) / b);
   const int slices = b / S;
   const int64_t units = static_cast<int64_t>(nblk) * slices * slices;
   int64_t ns = std::max<int64_t>(1, 256 / units);
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, (T + 4 * TK - 1) / (4 * TK)));
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, (T + 8 * TK - 1) / (8 * TK)));
   int64_t tpw = (T + ns - 1) / ns;
   tpw = (tpw + TK - 1) / TK * TK;
   return static_cast<int>(std::max<int64_t>(1, (T + tpw - 1) / tpw));
