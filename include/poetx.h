@@ -175,13 +175,13 @@ POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved,
 
 /* Merge (section "代码与部署", merge_if_needed): W0 <- R W0 P with the current
  * permutations and blocks, then q_r, q_p <- 0.
- *   wpt: poetx_weight_prepare's wpt (n x m) for the current W0 and
- *        permutations.
+ *   wp: poetx_weight_prepare's wp (m x n) for the current W0 and
+ *       permutations.
  *   w0 [m][n], w_dtype: overwritten with R W0 P (original frame).
  * The caller then resamples the permutations (the function no longer depends
  * on them once q = 0) and calls poetx_weight_prepare again.
  * POETX_I8 weights return POETX_EUNSUPPORTED. */
-POETX_API int poetx_merge(const poetx_layer* L, const void* wpt,
+POETX_API int poetx_merge(const poetx_layer* L, const void* wp,
                 const int32_t* perm_r, const int32_t* perm_p,
                 const void* g_r, const void* g_p,
                 void* w0, float* q_r, float* q_p,

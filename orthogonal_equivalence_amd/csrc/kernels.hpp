@@ -98,6 +98,14 @@ struct BlockProdDesc {
 };
 bool block_prod_bf16(const BlockProdDesc& d, hipStream_t stream);
 
+// Left block product (block_apply.hip) on a row-major rows x ncols bfloat16
+// matrix (row stride ld): out[j*256 + i][c] = in[j*256 + i][c] + sum_k
+// plane[j][i][k] in[j*256 + k][c] for the ceil(rows/256) row blocks; plane
+// holds 256 x 256 bfloat16 blocks, zero outside a short last block. b = 256
+// and ncols a multiple of 8 only (returns false otherwise).
+bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, int64_t rows,
+                           int64_t ncols, int b, hipStream_t stream);
+
 // Token sums of the block gradients (block_grad.hip) for bfloat16 blocks of
 // 256 or 512: part[s][j][i][c] = sum over the tokens of split s of
 // act[t][j*b + i] * dout[t][j*b + c], written for every (i, c) < b (zeros

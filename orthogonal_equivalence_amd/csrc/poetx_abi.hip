@@ -833,38 +833,56 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   return launch_status();
 }
 
-int poetx_merge(const poetx_layer* L, const void* wpt, const int32_t* perm_r, const int32_t* perm_p,
+int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, const int32_t* perm_p,
                 const void* g_r, const void* g_p, void* w0, float* q_r, float* q_p, void* ws, size_t ws_bytes,
                 hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
-  if (!ptrs_ok({wpt, perm_r, perm_p, g_r, g_p, w0, q_r, q_p})) return POETX_EINVAL;
+  if (!ptrs_ok({wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8) return POETX_EUNSUPPORTED;
   if (const int e = check_ws(L, 0, POETX_OP_MERGE, ws, ws_bytes)) return e;
   clear_pending_error();
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   Carve c(ws);
   MergeWs w = plan_merge(L, c);
-  // R W0 P = Psi^T Diag(G) Wp Diag(H) Phi with Wp = Psi W0 Phi^T.
-  // Diag(G) Wp = (Wp^T Diag(G)^T)^T: a right block product on the rows of
-  // Wp^T with the (G - I) plane, then a transpose, then Diag(H) on the right.
+  // R W0 P = Psi^T Diag(G) Wp Diag(H) Phi with Wp = Psi W0 Phi^T: the left
+  // block product on the rows of Wp, then Diag(H) on the right, then the
+  // scatter back to the original frame.
   bool ok;
-  {
-    ProfScope p("merge_left", stream);
-    ok = block_apply(L, R, L->n, wpt, w.C1, g_r, 0, nullptr, stream);
-  }
-  {
-    ProfScope p("merge_transpose", stream);
-    ok = ok && transpose(w.C1, w.C2, L->n, L->m, w_size(L), stream);
-  }
-  {
-    ProfScope p("merge_right", stream);
-    ok = ok && block_apply(L, P, L->m, w.C2, w.C1, g_p, 1, nullptr, stream);
+  void* M;  // Diag(G) Wp Diag(H), m x n
+  if (is_bf16(L) && R.b == 256) {
+    {
+      ProfScope p("merge_left", stream);
+      ok = block_apply_left_bf16(static_cast<const uint16_t*>(wp), static_cast<uint16_t*>(w.C2), L->n,
+                                 static_cast<const uint16_t*>(plane(L, g_r, R, 0)), L->m, L->n, R.b, stream);
+    }
+    {
+      ProfScope p("merge_right", stream);
+      ok = ok && block_apply(L, P, L->m, w.C2, w.C1, g_p, 1, nullptr, stream);
+    }
+    M = w.C1;
+  } else {
+    // Diag(G) Wp = (Wp^T Diag(G)^T)^T: a right block product on the rows of
+    // Wp^T with the (G - I) plane between two transposes
+    {
+      ProfScope p("merge_left", stream);
+      ok = transpose(wp, w.C1, L->m, L->n, w_size(L), stream);
+      ok = ok && block_apply(L, R, L->n, w.C1, w.C2, g_r, 0, nullptr, stream);
+    }
+    {
+      ProfScope p("merge_transpose", stream);
+      ok = ok && transpose(w.C2, w.C1, L->n, L->m, w_size(L), stream);
+    }
+    {
+      ProfScope p("merge_right", stream);
+      ok = ok && block_apply(L, P, L->m, w.C1, w.C2, g_p, 1, nullptr, stream);
+    }
+    M = w.C2;
   }
   // W0[perm_r[i]][perm_p[c]] = C[i][c]
   {
     ProfScope p("merge_scatter", stream);
     inverse_perm(perm_p, w.inv_p, L->n, stream);
-    ok = ok && gather_cols(w.C1, L->n, nullptr, w0, L->n, perm_r, w.inv_p, L->n, L->m, w_size(L), stream);
+    ok = ok && gather_cols(M, L->n, nullptr, w0, L->n, perm_r, w.inv_p, L->n, L->m, w_size(L), stream);
     fill_zero_f32(q_r, packed_len(R), stream);
     fill_zero_f32(q_p, packed_len(P), stream);
   }

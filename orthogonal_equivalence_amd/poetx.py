@@ -174,8 +174,8 @@ def poetx_backward(L, T, saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wsca
           _ptr(dx), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
-def poetx_merge(L, wpt, perm_r, perm_p, g_r, g_p, w0, q_r, q_p, ws=None, ws_bytes=None, stream=None):
-    _call("poetx_merge", ctypes.byref(L), _ptr(wpt), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
+def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p, ws=None, ws_bytes=None, stream=None):
+    _call("poetx_merge", ctypes.byref(L), _ptr(wp), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
           _ptr(w0), _ptr(q_r), _ptr(q_p), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
