@@ -112,6 +112,10 @@ SMALL = [
     _cfg("bf16_b512_ragged", 260, 1280, 1024, 512, 512, "bf16", "bf16", 29),
     # b = 128 with short last blocks on both sides (704 = 5*128 + 64, 392 = 3*128 + 8)
     _cfg("bf16_b128_ragged", 150, 704, 392, 128, 128, "bf16", "bf16", 32),
+    # shallowest dense products: K = 64 forward (one K step), K = 128 backward (two)
+    _cfg("bf16_k64", 300, 64, 128, 32, 64, "bf16", "bf16", 33),
+    # ragged token count and output width across several 256 x 256 output tiles
+    _cfg("bf16_ragged_tiles", 1100, 320, 1800, 64, 64, "bf16", "bf16", 34),
 ]
 
 
