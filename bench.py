@@ -252,13 +252,13 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def timed(steps):
+    def timed(steps, fn=step):
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(stream)
         for _ in range(steps):
-            step()
+            fn()
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
@@ -282,6 +282,24 @@ def main():
         f"({ms_logged / args.steps:.3f} ms/step with the per-kernel log)")
     kernels = {k: round(v[0] / v[1], 4) for k, v in sorted(per.items())}
     log("[bench] per-step breakdown (ms): " + json.dumps(kernels))
+
+    # pass 3: the memory variant of the same step (the forward saves nothing,
+    # the backward recomputes X1, X2 and Y1 from x), timed like pass 1
+    def step_mem():
+        dl.cnp_build()
+        dl.forward_mem(x, z)
+        dl.backward_mem(x, dz, dq_r, dq_p, dx)
+        if cfg.merge:
+            dl.merge()
+            dl.prepare()
+
+    for _ in range(2):
+        step_mem()
+    ms_mem = timed(args.steps, step_mem) / args.steps
+    log(f"[bench] memory variant: {ms_mem:.3f} ms/step")
+    variant_mem = {"ms_per_step": round(ms_mem, 4), "tokens_per_s": round(cfg.T / (ms_mem * 1e-3), 1),
+                   "activation_bytes_kept_per_layer": 0,
+                   "saving_variant_activation_bytes_per_layer": px.poetx_saved_bytes(dl.L, cfg.T)}
 
     flops_gemm = 2.0 * cfg.T * cfg.m * cfg.n
     g = [per[k] for k in ("gemm_dense_fwd", "gemm_dense_bwd") if k in per]
@@ -340,6 +358,7 @@ def main():
         "fwd_bwd_tokens_per_s": round(cfg.T / (ms_fwd_bwd * 1e-3), 1),
         "merge_prepare_ms": round(ms_merge, 4),
         "tokens_per_s_merge_every_200": round(cfg.T / ((ms_fwd_bwd + ms_merge / 200) * 1e-3), 1),
+        "variant_mem": variant_mem,
         "kernels_ms": kernels,
         "kernel_roofline": kernel_roofline(cfg, per),
         "torch_linear_fwd_bwd_ms": yard,

@@ -72,7 +72,9 @@ enum {
   POETX_OP_WEIGHT_PREPARE = 1,
   POETX_OP_FORWARD = 2,
   POETX_OP_BACKWARD = 3,
-  POETX_OP_MERGE = 4
+  POETX_OP_MERGE = 4,
+  POETX_OP_FORWARD_MEM = 5,
+  POETX_OP_BACKWARD_MEM = 6
 };
 
 typedef struct poetx_layer {
@@ -172,6 +174,33 @@ POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved,
                    const void* wp, const float* wscale_p,
                    float* dq_r, float* dq_p, void* dx,
                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Memory variant (section "三种变体，三种场景", POET-X mem; the pages give no
+ * mechanism, the reading here is recomputation): the forward saves nothing
+ * and the backward recomputes what it needs from x.
+ * poetx_forward_mem: poetx_forward without `saved` (X1 and Y1 go to the
+ *   workspace, poetx_workspace_bytes(L, T, POETX_OP_FORWARD_MEM)).
+ * poetx_backward_mem: poetx_backward with x in place of `saved`. It recomputes
+ *   X1 = X Psi^T, X2 = X1 Diag(G) and Y1 = X2 Wp (the forward's first three
+ *   steps, same kernels) into the workspace
+ *   (poetx_workspace_bytes(L, T, POETX_OP_BACKWARD_MEM)), then runs the
+ *   backward; results equal poetx_backward's for the same inputs.
+ *   x [T][m], act_dtype; wpt: the forward's weight, wp: the backward's.
+ * Costs one more dense product per step and saves poetx_saved_bytes(L, T) of
+ * activations per layer. */
+POETX_API int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x,
+                      const int32_t* perm_r, const int32_t* perm_p,
+                      const void* g_r, const void* g_p,
+                      const void* wpt, const float* wscale_p,
+                      void* z, void* ws, size_t ws_bytes, hipStream_t stream);
+
+POETX_API int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const void* dz,
+                       const int32_t* perm_r, const int32_t* perm_p,
+                       const float* q_r, const float* q_p,
+                       const void* g_r, const void* g_p,
+                       const void* wp, const void* wpt, const float* wscale_p,
+                       float* dq_r, float* dq_p, void* dx,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Merge (section "代码与部署", merge_if_needed): W0 <- R W0 P with the current
  * permutations and blocks, then q_r, q_p <- 0.

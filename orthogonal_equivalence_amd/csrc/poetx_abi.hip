@@ -256,6 +256,9 @@ size_t cnp_build_bytes(const poetx_layer* L) {
   return m.off;
 }
 
+// X1 (T x m) then Y1 (T x n), activation dtype: the forward's saved tensors
+int64_t saved_region(const poetx_layer* L, int64_t T) { return T * (L->m + L->n) * act_size(L); }
+
 size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
   Carve c(nullptr);
   switch (op) {
@@ -264,6 +267,21 @@ size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
     case POETX_OP_FORWARD: plan_fwd(L, T, c); return c.off;
     case POETX_OP_BACKWARD: plan_bwd(L, T, c); return c.off;
     case POETX_OP_MERGE: plan_merge(L, c); return c.off;
+    case POETX_OP_FORWARD_MEM: {
+      // X1 and Y1 live in the workspace
+      c.take<char>(saved_region(L, T));
+      plan_fwd(L, T, c);
+      return c.off;
+    }
+    case POETX_OP_BACKWARD_MEM: {
+      // X1 and Y1 recomputed into the workspace; the recompute's scratch and
+      // the backward's share what follows
+      c.take<char>(saved_region(L, T));
+      Carve f = c, b = c;
+      plan_fwd(L, T, f);
+      plan_bwd(L, T, b);
+      return std::max(f.off, b.off);
+    }
     default: return 0;
   }
 }
@@ -578,6 +596,139 @@ int check_ws(const poetx_layer* L, int64_t T, int op, const void* ws, size_t ws_
   return POETX_OK;
 }
 
+// Forward steps up to Y1 = X2 Wp, then (when z is given) Y2 = Y1 Diag(H) and
+// the scatter to z. X1, Y1: where the saved tensors go (the caller's buffer,
+// or the workspace in the memory variant). `recompute` only renames the
+// profiled steps: the memory variant's backward runs the first three again.
+bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r, const int32_t* perm_p,
+                  const void* g_r, const void* g_p, const void* wpt, const float* wscale_p, void* z, void* X1,
+                  void* Y1, const FwdWs& w, bool recompute, hipStream_t stream) {
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  const int es = act_size(L);
+  const bool i8 = L->w_dtype == POETX_I8;
+  bool ok;
+  {
+    ProfScope p(recompute ? "recompute_gather_x" : "gather_x", stream);
+    ok = gather_cols(x, L->m, nullptr, X1, L->m, nullptr, perm_r, L->m, T, es, stream);
+  }
+  {
+    ProfScope p(recompute ? "recompute_apply_r" : "apply_r_fwd", stream);
+    ok = ok && block_apply(L, R, T, X1, w.buf, g_r, 1, nullptr, stream);
+  }
+  GemmDesc d;
+  d.dense = 1;
+  d.A = w.buf;
+  d.lda = L->m;
+  d.B = wpt;
+  d.ldb = L->m;
+  d.C = Y1;
+  d.ldc = L->n;
+  d.scale = i8 ? wscale_p : nullptr;
+  d.M = static_cast<int>(T);
+  d.N = static_cast<int>(L->n);
+  d.K = static_cast<int>(L->m);
+  {
+    ProfScope p(recompute ? "recompute_gemm_dense" : "gemm_dense_fwd", stream);
+    ok = ok && dense_product(L, d, i8, stream);
+  }
+  if (!z) return ok;
+  {
+    ProfScope p("apply_p_fwd", stream);
+    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream);
+  }
+  {
+    ProfScope p("scatter_z", stream);
+    inverse_perm(perm_p, w.inv_p, L->n, stream);
+    ok = ok && gather_cols(w.buf, L->n, nullptr, z, L->n, nullptr, w.inv_p, L->n, T, es, stream);
+  }
+  return ok;
+}
+
+// Backward from the saved X1, Y1 to dq_r, dq_p and dx (T > 0).
+bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* Y1, const void* dz,
+                   const int32_t* perm_r, const int32_t* perm_p, const float* q_r, const float* q_p,
+                   const void* g_r, const void* g_p, const void* wp, const float* wscale_p, float* dq_r,
+                   float* dq_p, void* dx, const BwdWs& w, void* cnp_ws, hipStream_t stream) {
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  const bool i8 = L->w_dtype == POETX_I8;
+  const int es = act_size(L);
+  // P side: dY2 = dZ Phi^T, dH = sum_t Y1^T dY2, and either dY1 = dY2 H^T
+  // (times the column scales for int8 weights, which belong to Wp's columns)
+  // for dX2 = dY1 Wp^T, or the fold dX2 = dY2 (Wp H)^T
+  const bool fold = fold_h(L, T);
+  bool ok;
+  {
+    ProfScope p("gather_dz", stream);
+    ok = gather_cols(dz, L->n, nullptr, w.bufA, L->n, nullptr, perm_p, L->n, T, es, stream);
+  }
+  const Split spP = token_split(L, P, T);
+  {
+    ProfScope p("grad_h", stream);
+    ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part_p, spP, stream);
+  }
+  GemmDesc d;
+  d.dense = 1;
+  if (fold) {
+    ProfScope p("fold_h_bwd", stream);
+    ok = ok && block_apply(L, P, L->m, wp, w.wh, g_p, 1, nullptr, stream);
+    d.A = w.bufA;
+    d.B = w.wh;
+    d.C = w.bufB;
+  } else {
+    ProfScope p("apply_p_bwd", stream);
+    ok = ok && block_apply(L, P, T, w.bufA, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
+    d.A = w.bufB;
+    d.B = wp;
+    d.C = w.bufA;
+  }
+  void* const dX2 = d.C;
+  void* const dX1 = fold ? w.bufA : w.bufB;
+  d.lda = L->n;
+  d.ldb = L->n;
+  d.ldc = L->m;
+  d.M = static_cast<int>(T);
+  d.N = static_cast<int>(L->m);
+  d.K = static_cast<int>(L->n);
+  {
+    ProfScope p("gemm_dense_bwd", stream);
+    ok = ok && dense_product(L, d, i8, stream);
+  }
+  // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
+  {
+    ProfScope p("apply_r_bwd", stream);
+    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream);
+  }
+  const Split spR = token_split(L, R, T);
+  {
+    ProfScope p("grad_g", stream);
+    ok = ok && block_token_grad(L, R, T, X1, dX2, w.part_r, spR, stream);
+  }
+  {
+    ProfScope p("scatter_dx", stream);
+    inverse_perm(perm_r, w.inv_r, L->m, stream);
+    ok = ok && gather_cols(dX1, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
+  }
+  // dq_r, dq_p from the token sums dG, dH
+  {
+    ProfScope p("cnp_bwd", stream);
+    const bool bf = is_bf16(L);
+    const int64_t eR = block_elems(R);
+    reduce_symskew(w.part_r, spR.nsplit, R.b, R.nblk, w.Us, w.Uk, bf ? w.Ush : nullptr, bf ? w.Ukh : nullptr,
+                   stream);
+    reduce_symskew(w.part_p, spP.nsplit, P.b, P.nblk, w.Us + eR, w.Uk + eR, bf ? w.Ush + eR : nullptr,
+                   bf ? w.Ukh + eR : nullptr, stream);
+    if (R.b == P.b) {
+      ok = ok && cnp_bwd_group(L, group_of(R, P), q_r, q_p, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, dq_p, cnp_ws, stream);
+    } else {
+      ok = ok && cnp_bwd_group(L, group_of(R), q_r, nullptr, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, nullptr, cnp_ws,
+                               stream);
+      ok = ok && cnp_bwd_group(L, group_of(P), q_p, nullptr, w.Us + eR, w.Uk + eR, w.Ush + eR, w.Ukh + eR, dq_p,
+                               nullptr, cnp_ws, stream);
+    }
+  }
+  return ok;
+}
+
 }  // namespace
 
 extern "C" {
@@ -683,51 +834,33 @@ int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
   if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z, saved})) return POETX_EINVAL;
-  const bool i8 = L->w_dtype == POETX_I8;
-  if (i8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_FORWARD, ws, ws_bytes)) return e;
   clear_pending_error();
-  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
-  const int es = act_size(L);
   Carve c(ws);
-  FwdWs w = plan_fwd(L, T, c);
+  const FwdWs w = plan_fwd(L, T, c);
   void* X1 = saved;
-  void* Y1 = static_cast<char*>(saved) + T * L->m * es;
-  bool ok;
-  {
-    ProfScope p("gather_x", stream);
-    ok = gather_cols(x, L->m, nullptr, X1, L->m, nullptr, perm_r, L->m, T, es, stream);
-  }
-  {
-    ProfScope p("apply_r_fwd", stream);
-    ok = ok && block_apply(L, R, T, X1, w.buf, g_r, 1, nullptr, stream);
-  }
-  GemmDesc d;
-  d.dense = 1;
-  d.A = w.buf;
-  d.lda = L->m;
-  d.B = wpt;
-  d.ldb = L->m;
-  d.C = Y1;
-  d.ldc = L->n;
-  d.scale = i8 ? wscale_p : nullptr;
-  d.M = static_cast<int>(T);
-  d.N = static_cast<int>(L->n);
-  d.K = static_cast<int>(L->m);
-  {
-    ProfScope p("gemm_dense_fwd", stream);
-    ok = ok && dense_product(L, d, i8, stream);
-  }
-  {
-    ProfScope p("apply_p_fwd", stream);
-    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream);
-  }
-  {
-    ProfScope p("scatter_z", stream);
-    inverse_perm(perm_p, w.inv_p, L->n, stream);
-    ok = ok && gather_cols(w.buf, L->n, nullptr, z, L->n, nullptr, w.inv_p, L->n, T, es, stream);
-  }
-  if (!ok) return POETX_EUNSUPPORTED;
+  void* Y1 = static_cast<char*>(saved) + T * L->m * act_size(L);
+  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, X1, Y1, w, false, stream))
+    return POETX_EUNSUPPORTED;
+  return launch_status();
+}
+
+int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r,
+                      const int32_t* perm_p, const void* g_r, const void* g_p, const void* wpt,
+                      const float* wscale_p, void* z, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (T == 0) return POETX_OK;
+  if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z})) return POETX_EINVAL;
+  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (const int e = check_ws(L, T, POETX_OP_FORWARD_MEM, ws, ws_bytes)) return e;
+  clear_pending_error();
+  Carve c(ws);
+  char* X1 = c.take<char>(saved_region(L, T));
+  char* Y1 = X1 + T * L->m * act_size(L);
+  const FwdWs w = plan_fwd(L, T, c);
+  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, X1, Y1, w, false, stream))
+    return POETX_EUNSUPPORTED;
   return launch_status();
 }
 
@@ -745,91 +878,49 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
     return launch_status();
   }
   if (!ptrs_ok({saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, dx})) return POETX_EINVAL;
-  const bool i8 = L->w_dtype == POETX_I8;
-  if (i8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_BACKWARD, ws, ws_bytes)) return e;
-  const int es = act_size(L);
   Carve c(ws);
-  BwdWs w = plan_bwd(L, T, c);
+  const BwdWs w = plan_bwd(L, T, c);
   void* cnp_ws = static_cast<char*>(ws) + w.cnp_off;
   const void* X1 = saved;
-  const void* Y1 = static_cast<const char*>(saved) + T * L->m * es;
+  const void* Y1 = static_cast<const char*>(saved) + T * L->m * act_size(L);
+  if (!backward_core(L, T, X1, Y1, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wscale_p, dq_r, dq_p, dx, w,
+                     cnp_ws, stream))
+    return POETX_EUNSUPPORTED;
+  return launch_status();
+}
 
-  // P side: dY2 = dZ Phi^T, dH = sum_t Y1^T dY2, and either dY1 = dY2 H^T
-  // (times the column scales for int8 weights, which belong to Wp's columns)
-  // for dX2 = dY1 Wp^T, or the fold dX2 = dY2 (Wp H)^T
-  const bool fold = fold_h(L, T);
-  bool ok;
-  {
-    ProfScope p("gather_dz", stream);
-    ok = gather_cols(dz, L->n, nullptr, w.bufA, L->n, nullptr, perm_p, L->n, T, es, stream);
+int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const void* dz, const int32_t* perm_r,
+                       const int32_t* perm_p, const float* q_r, const float* q_p, const void* g_r,
+                       const void* g_p, const void* wp, const void* wpt, const float* wscale_p, float* dq_r,
+                       float* dq_p, void* dx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (!ptrs_ok({dq_r, dq_p})) return POETX_EINVAL;
+  const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+  clear_pending_error();
+  if (T == 0) {
+    fill_zero_f32(dq_r, packed_len(R), stream);
+    fill_zero_f32(dq_p, packed_len(P), stream);
+    return launch_status();
   }
-  const Split spP = token_split(L, P, T);
-  {
-    ProfScope p("grad_h", stream);
-    ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part_p, spP, stream);
-  }
-  GemmDesc d;
-  d.dense = 1;
-  if (fold) {
-    ProfScope p("fold_h_bwd", stream);
-    ok = ok && block_apply(L, P, L->m, wp, w.wh, g_p, 1, nullptr, stream);
-    d.A = w.bufA;
-    d.B = w.wh;
-    d.C = w.bufB;
-  } else {
-    ProfScope p("apply_p_bwd", stream);
-    ok = ok && block_apply(L, P, T, w.bufA, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
-    d.A = w.bufB;
-    d.B = wp;
-    d.C = w.bufA;
-  }
-  void* const dX2 = d.C;
-  void* const dX1 = fold ? w.bufA : w.bufB;
-  d.lda = L->n;
-  d.ldb = L->n;
-  d.ldc = L->m;
-  d.M = static_cast<int>(T);
-  d.N = static_cast<int>(L->m);
-  d.K = static_cast<int>(L->n);
-  {
-    ProfScope p("gemm_dense_bwd", stream);
-    ok = ok && dense_product(L, d, i8, stream);
-  }
-  // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
-  {
-    ProfScope p("apply_r_bwd", stream);
-    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream);
-  }
-  const Split spR = token_split(L, R, T);
-  {
-    ProfScope p("grad_g", stream);
-    ok = ok && block_token_grad(L, R, T, X1, dX2, w.part_r, spR, stream);
-  }
-  {
-    ProfScope p("scatter_dx", stream);
-    inverse_perm(perm_r, w.inv_r, L->m, stream);
-    ok = ok && gather_cols(dX1, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
-  }
-  // dq_r, dq_p from the token sums dG, dH
-  {
-    ProfScope p("cnp_bwd", stream);
-    const bool bf = is_bf16(L);
-    const int64_t eR = block_elems(R);
-    reduce_symskew(w.part_r, spR.nsplit, R.b, R.nblk, w.Us, w.Uk, bf ? w.Ush : nullptr, bf ? w.Ukh : nullptr,
-                   stream);
-    reduce_symskew(w.part_p, spP.nsplit, P.b, P.nblk, w.Us + eR, w.Uk + eR, bf ? w.Ush + eR : nullptr,
-                   bf ? w.Ukh + eR : nullptr, stream);
-    if (R.b == P.b) {
-      ok = ok && cnp_bwd_group(L, group_of(R, P), q_r, q_p, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, dq_p, cnp_ws, stream);
-    } else {
-      ok = ok && cnp_bwd_group(L, group_of(R), q_r, nullptr, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, nullptr, cnp_ws,
-                               stream);
-      ok = ok && cnp_bwd_group(L, group_of(P), q_p, nullptr, w.Us + eR, w.Uk + eR, w.Ush + eR, w.Ukh + eR, dq_p,
-                               nullptr, cnp_ws, stream);
-    }
-  }
-  if (!ok) return POETX_EUNSUPPORTED;
+  if (!ptrs_ok({x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt, dx})) return POETX_EINVAL;
+  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (const int e = check_ws(L, T, POETX_OP_BACKWARD_MEM, ws, ws_bytes)) return e;
+  Carve c(ws);
+  char* X1 = c.take<char>(saved_region(L, T));
+  char* Y1 = X1 + T * L->m * act_size(L);
+  // the recompute's scratch and the backward's start at the same offset: the
+  // recompute is done (in stream order) before the backward touches it
+  Carve f = c, b = c;
+  const FwdWs fw = plan_fwd(L, T, f);
+  const BwdWs w = plan_bwd(L, T, b);
+  void* cnp_ws = static_cast<char*>(ws) + w.cnp_off;
+  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, nullptr, X1, Y1, fw, true, stream))
+    return POETX_EUNSUPPORTED;
+  if (!backward_core(L, T, X1, Y1, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wscale_p, dq_r, dq_p, dx, w,
+                     cnp_ws, stream))
+    return POETX_EUNSUPPORTED;
   return launch_status();
 }
 

@@ -70,7 +70,7 @@ class DeviceLayer:
         self.T_max = max(T, self.T_max)
         self.saved = torch.empty(max(px.poetx_saved_bytes(self.L, self.T_max), 16), dtype=torch.uint8,
                                  device=self.device)
-        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(5))
+        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(7))
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
 
@@ -125,6 +125,30 @@ class DeviceLayer:
             dx = self.act_tensor(T, self.m)
         px.poetx_backward(self.L, T, self.saved, dz, self.perm_r, self.perm_p, self.q_r, self.q_p, self.g_r,
                           self.g_p, self.wp, self.wscale_p, dq_r, dq_p, dx, self.ws, None, stream)
+        return dq_r, dq_p, dx
+
+    def forward_mem(self, x, z=None, stream=None):
+        """Memory variant: nothing saved (X1 and Y1 only in the workspace)."""
+        T = x.shape[0]
+        self.reserve(T)
+        if z is None:
+            z = self.act_tensor(T, self.n)
+        px.poetx_forward_mem(self.L, T, x, self.perm_r, self.perm_p, self.g_r, self.g_p, self.wpt,
+                             self.wscale_p, z, self.ws, None, stream)
+        return z
+
+    def backward_mem(self, x, dz, dq_r=None, dq_p=None, dx=None, stream=None):
+        """Memory variant: recomputes X1 and Y1 from x, then the backward."""
+        T = dz.shape[0]
+        self.reserve(T)
+        if dq_r is None:
+            dq_r = torch.empty_like(self.q_r)
+        if dq_p is None:
+            dq_p = torch.empty_like(self.q_p)
+        if dx is None:
+            dx = self.act_tensor(T, self.m)
+        px.poetx_backward_mem(self.L, T, x, dz, self.perm_r, self.perm_p, self.q_r, self.q_p, self.g_r,
+                              self.g_p, self.wp, self.wpt, self.wscale_p, dq_r, dq_p, dx, self.ws, None, stream)
         return dq_r, dq_p, dx
 
     def merge(self, stream=None):

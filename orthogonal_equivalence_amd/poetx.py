@@ -27,12 +27,13 @@ POETX_OK, POETX_EINVAL, POETX_EUNSUPPORTED, POETX_EHIP, POETX_EWORKSPACE = 0, 1,
 POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
 POETX_SIDE_R, POETX_SIDE_P = 0, 1
 (POETX_OP_CNP_BUILD, POETX_OP_WEIGHT_PREPARE, POETX_OP_FORWARD, POETX_OP_BACKWARD,
- POETX_OP_MERGE) = 0, 1, 2, 3, 4
+ POETX_OP_MERGE, POETX_OP_FORWARD_MEM, POETX_OP_BACKWARD_MEM) = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTED = [
     "poetx_abi_version", "poetx_strerror", "poetx_last_hip_error", "poetx_packed_len", "poetx_gbuf_bytes",
     "poetx_saved_bytes", "poetx_wbuf_bytes", "poetx_workspace_bytes", "poetx_cnp_build",
-    "poetx_weight_prepare", "poetx_forward", "poetx_backward", "poetx_merge",
+    "poetx_weight_prepare", "poetx_forward", "poetx_backward", "poetx_forward_mem", "poetx_backward_mem",
+    "poetx_merge",
     "poetx_profile_enable", "poetx_profile_count", "poetx_profile_get",
 ]
 
@@ -76,6 +77,9 @@ _sig = {
     "poetx_forward": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_backward": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _SZ, _P]),
+    "poetx_forward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "poetx_backward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, _P, _P, _SZ, _P]),
     "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "poetx_profile_count": (ctypes.c_int, []),
@@ -172,6 +176,19 @@ def poetx_backward(L, T, saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wsca
     _call("poetx_backward", ctypes.byref(L), T, _ptr(saved), _ptr(dz), _ptr(perm_r), _ptr(perm_p),
           _ptr(q_r), _ptr(q_p), _ptr(g_r), _ptr(g_p), _ptr(wp), _ptr(wscale_p), _ptr(dq_r), _ptr(dq_p),
           _ptr(dx), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+
+
+def poetx_forward_mem(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, ws=None, ws_bytes=None,
+                      stream=None):
+    _call("poetx_forward_mem", ctypes.byref(L), T, _ptr(x), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
+          _ptr(wpt), _ptr(wscale_p), _ptr(z), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+
+
+def poetx_backward_mem(L, T, x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt, wscale_p, dq_r, dq_p, dx,
+                       ws=None, ws_bytes=None, stream=None):
+    _call("poetx_backward_mem", ctypes.byref(L), T, _ptr(x), _ptr(dz), _ptr(perm_r), _ptr(perm_p),
+          _ptr(q_r), _ptr(q_p), _ptr(g_r), _ptr(g_p), _ptr(wp), _ptr(wpt), _ptr(wscale_p), _ptr(dq_r),
+          _ptr(dq_p), _ptr(dx), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
 def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p, ws=None, ws_bytes=None, stream=None):

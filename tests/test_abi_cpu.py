@@ -28,7 +28,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 18
     lib = ctypes.CDLL(px.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -118,6 +118,22 @@ def test_argument_errors_before_any_launch():
     assert e.value.status == px.POETX_EINVAL
     # T = 0 forward is a no-op (no launch, no pointer use)
     px.poetx_forward(L, 0, *([None] * 9), None, 0, stream=0)
+    # memory variant: its own workspace sizes, the same checks
+    ws_fm = px.poetx_workspace_bytes(L, 32, px.POETX_OP_FORWARD_MEM)
+    ws_bm = px.poetx_workspace_bytes(L, 32, px.POETX_OP_BACKWARD_MEM)
+    saved = px.poetx_saved_bytes(L, 32)
+    assert ws_fm == ws_f + saved
+    assert ws_bm >= max(ws_f, ws_b) + saved
+    with pytest.raises(px.PoetxError) as e:
+        px.poetx_forward_mem(L, 32, *([FAKE] * 8), FAKE, ws_fm - 1, stream=0)
+    assert e.value.status == px.POETX_EWORKSPACE
+    with pytest.raises(px.PoetxError) as e:
+        px.poetx_backward_mem(L, 32, *([FAKE] * 14), FAKE, ws_bm - 1, stream=0)
+    assert e.value.status == px.POETX_EWORKSPACE
+    with pytest.raises(px.PoetxError) as e:
+        px.poetx_backward_mem(L, 32, None, *([FAKE] * 13), FAKE, ws_bm, stream=0)
+    assert e.value.status == px.POETX_EINVAL
+    px.poetx_forward_mem(L, 0, *([None] * 8), None, 0, stream=0)
     # cnp build: q without g
     with pytest.raises(px.PoetxError) as e:
         px.poetx_cnp_build(L, FAKE, None, None, None, FAKE, 1 << 30, stream=0)

@@ -159,6 +159,29 @@ def test_merge_preserves_the_layer_function():
     assert rel(z2, out["z"]) <= 1e-5
 
 
+@pytest.mark.parametrize("cfg", [
+    # b = 256 on the R side: left block product on the rows of Wp
+    _cfg("merge_zero_q_b256", 16, 640, 1088, 256, 256, "bf16", "bf16", 35),
+    # other block sizes: the left product between two transposes
+    _cfg("merge_zero_q_b128", 16, 384, 704, 128, 128, "bf16", "bf16", 36),
+], ids=lambda c: c.name)
+def test_merge_with_zero_q_leaves_w0_unchanged(cfg):
+    # q = 0 makes every G and H the identity, so R W0 P = W0 exactly; both
+    # roundings to bfloat16 then return the stored values bit for bit
+    print(f"\n[gpu] {cfg.name} m={cfg.m} n={cfg.n} b={cfg.b_r}/{cfg.b_p}", flush=True)
+    L = synth.make_layer(cfg, 0)
+    dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
+    dl.load(L)
+    dl.q_r.zero_()
+    dl.q_p.zero_()
+    dl.cnp_build()
+    dl.prepare()
+    before = dl.w0.clone()
+    dl.merge()
+    torch.cuda.synchronize()
+    assert torch.equal(dl.w0.view(torch.int16), before.view(torch.int16))
+
+
 # ---------------------------------------------------------------------------
 # bit-exact index work
 # ---------------------------------------------------------------------------
