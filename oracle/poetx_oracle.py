@@ -40,6 +40,7 @@ __all__ = [
     "scatter_cols", "block_diag_right", "block_diag_left", "permutation_matrix",
     "dense_block_orthogonal", "dequantize", "permuted_weight", "forward",
     "backward", "backward_blocks", "merge", "weight_centric_forward", "inner",
+    "requantize_int8_per_col", "merge_xq",
 ]
 
 
@@ -343,6 +344,30 @@ def merge(W0, q_r, q_p, perm_r, perm_p, b_r, b_p):
     out = np.empty_like(B)
     out[np.ix_(np.asarray(perm_r), np.asarray(perm_p))] = B
     return out
+
+
+def requantize_int8_per_col(W):
+    """Per-output-column int8 storage of a float weight [XQ], as this build
+    reads the page's quantized base weight: scale[c] = max_r |W[r, c]| / 127,
+    code = clip(rint(W / scale), -127, 127) with rint rounding half to even,
+    and a zero column stored with scale 1. The page fixes no precision for
+    the decision, so it is taken in float32, the kernels' precision."""
+    W32 = np.asarray(W, dtype=np.float64).astype(np.float32)
+    amax = np.abs(W32).max(axis=0)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.rint(W32 / scale[None, :]), -127, 127).astype(np.int8)
+    return codes, scale
+
+
+def merge_xq(Wq, scale, q_r, q_p, perm_r, perm_p, b_r, b_p):
+    """Merge of a quantized base weight [XQ], [MG]. The page does not say how
+    the merged weight is stored again; reading: dequantize, W0 <- R W0 P in
+    float64, then store per output column as the input was stored. Returns
+    (codes, scale, merged float64 weight before storage)."""
+    W = merge(dequantize(Wq, scale), q_r, q_p, perm_r, perm_p, b_r, b_p)
+    codes, new_scale = requantize_int8_per_col(W)
+    return codes, new_scale, W
 
 
 def weight_centric_forward(X, W0, q_r, q_p, perm_r, perm_p, b_r, b_p):

@@ -317,6 +317,53 @@ def test_dequantize_exact_and_roundtrip_bound():
     assert np.all(np.abs(Wd - W) <= 0.5 * L["w_scale"][None, :].astype(np.float64) * (1 + 1e-6))
 
 
+def test_requantize_rounds_half_to_even_and_stores_zero_columns():
+    # column 0: scale 0.25 (a power of two, exact) and codes at exact half steps;
+    # column 1 is all zero
+    s = 0.25
+    v = np.array([127, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -126.5])
+    W = np.stack([v * s, np.zeros_like(v)], axis=1)
+    codes, scale = O.requantize_int8_per_col(W)
+    assert scale.dtype == np.float32 and np.array_equal(scale, np.array([0.25, 1.0], np.float32))
+    assert np.array_equal(codes[:, 0], np.array([127, 2, 4, -2, 0, 0, 2, -126], np.int8))
+    assert np.array_equal(codes[:, 1], np.zeros(8, np.int8))
+    # sign symmetry
+    c2, s2 = O.requantize_int8_per_col(-W)
+    assert np.array_equal(c2, -codes) and np.array_equal(s2, scale)
+
+
+def test_xq_merge_with_zero_q_keeps_the_codes():
+    # merging with q = 0 is the identity on the weight; storing it again gives
+    # back every code, and the scales of that storage
+    cfg = synth.CONFIGS["xq_llama8b_mlp_up"]
+    L = synth.make_layer(cfg, 0, m=64, n=96)
+    zr = np.zeros(O.packed_len(64, 16))
+    zp = np.zeros(O.packed_len(96, 16))
+    pr, pp = np.random.default_rng(3).permutation(64), np.random.default_rng(4).permutation(96)
+    codes, scale, W = O.merge_xq(L["W0_raw"], L["w_scale"], zr, zp, pr, pp, 16, 16)
+    assert np.array_equal(W, O.dequantize(L["W0_raw"], L["w_scale"]))
+    assert np.array_equal(codes, L["W0_raw"])
+    assert np.allclose(scale, L["w_scale"], rtol=2.0 ** -22, atol=0)
+
+
+def test_xq_merge_stores_the_float_merge_within_half_a_step():
+    cfg = synth.CONFIGS["xq_llama8b_mlp_up"]
+    L = synth.make_layer(cfg, 0, m=48, n=64)
+    rng = np.random.default_rng(5)
+    qr = rng.standard_normal(O.packed_len(48, 16)) * 0.05
+    qp = rng.standard_normal(O.packed_len(64, 16)) * 0.05
+    pr, pp = rng.permutation(48), rng.permutation(64)
+    codes, scale, W = O.merge_xq(L["W0_raw"], L["w_scale"], qr, qp, pr, pp, 16, 16)
+    # the merged float weight is R W0 P of the dequantized weight
+    R = O.dense_block_orthogonal(O.cnp_blocks(qr, 48, 16), pr, 16)
+    P = O.dense_block_orthogonal(O.cnp_blocks(qp, 64, 16), pp, 16)
+    assert np.allclose(W, R @ O.dequantize(L["W0_raw"], L["w_scale"]) @ P, atol=1e-14)
+    # every column uses its full code range and stores within half a step
+    assert np.all(np.abs(codes.astype(np.int32)).max(axis=0) == 127)
+    assert np.all(np.abs(O.dequantize(codes, scale) - W) <= 0.5 * scale[None, :] * (1 + 1e-5))
+    assert not np.array_equal(codes, L["W0_raw"])
+
+
 def test_packed_len_matches_block_count():
     assert O.packed_len(4096, 256) == 16 * 256 * 255 // 2
     assert O.packed_len(10, 4) == 6 + 6 + 1
