@@ -207,13 +207,20 @@ POETX_API int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x,
  *   wp: poetx_weight_prepare's wp (m x n) for the current W0 and
  *       permutations.
  *   w0 [m][n], w_dtype: overwritten with R W0 P (original frame).
+ *   w_scale [n] float, int8 weights only (ignored otherwise, may be NULL):
+ *       in, the per-column scales W0 is stored with; out, the new scales.
+ *       The merged weight is stored again the way W0 was (section "POET-XQ：
+ *       量化训练的额外红利" stores the base weight quantized; how a merged
+ *       weight is stored again is a reading): per output column c,
+ *       scale[c] = max_r |W0'[r][c]| / 127 (1 for a zero column) and
+ *       W0[r][c] = clamp(rint(W0'[r][c] / scale[c]), -127, 127), rounding half
+ *       to even in float32. The merge itself runs in float for int8 weights.
  * The caller then resamples the permutations (the function no longer depends
- * on them once q = 0) and calls poetx_weight_prepare again.
- * POETX_I8 weights return POETX_EUNSUPPORTED. */
+ * on them once q = 0) and calls poetx_weight_prepare again. */
 POETX_API int poetx_merge(const poetx_layer* L, const void* wp,
                 const int32_t* perm_r, const int32_t* perm_p,
                 const void* g_r, const void* g_p,
-                void* w0, float* q_r, float* q_p,
+                void* w0, float* w_scale, float* q_r, float* q_p,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Kernel timing log (tracing). poetx_profile_enable(1) clears the log and

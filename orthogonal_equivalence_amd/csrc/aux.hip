@@ -263,6 +263,72 @@ __global__ void k_fill_zero(float* p, int64_t n) {
   if (i < n) p[i] = 0.f;
 }
 
+// ---- int8 base weight around a merge ----------------------------------------
+// out[r][c] = wq[r][c] * scale[cmap[c]] (cmap null: identity), 8 columns per
+// thread: 8-byte loads, 32-byte stores.
+__global__ void k_dequant_i8_cols(const int8_t* __restrict__ wq, const float* __restrict__ scale,
+                                  const int32_t* __restrict__ cmap, float* __restrict__ out, int64_t rows,
+                                  int64_t cols) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // 8-column group
+  const int64_t per_row = cols >> 3;
+  if (g >= rows * per_row) return;
+  const int64_t r = g / per_row, c0 = (g % per_row) * 8;
+  const uint2 q = *reinterpret_cast<const uint2*>(wq + r * cols + c0);
+  const uint32_t w[2] = {q.x, q.y};
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = static_cast<int>(c0) + e;
+    const float sc = scale[cmap ? clamp_index(cmap[c], cols) : c];
+    v[e] = static_cast<float>(static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xffu)) * sc;
+  }
+  float4* o = reinterpret_cast<float4*>(out + r * cols + c0);
+  o[0] = make_float4(v[0], v[1], v[2], v[3]);
+  o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__global__ void k_bf16_to_f32(const bf16_t* __restrict__ in, float* __restrict__ out, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) out[i] = bf16_to_f32(in[i]);
+}
+
+// amax[c] = max over rows of |w[r][c]|: blockIdx.y takes a band of rows, one
+// thread a column; the bands meet in an atomic max on the bit patterns (all
+// values are non-negative, so their bits order like the floats). The result
+// does not depend on the order.
+__global__ void k_col_absmax(const float* __restrict__ w, int64_t rows, int64_t cols, int64_t band,
+                             unsigned int* __restrict__ amax) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * band;
+  const int64_t r1 = r0 + band < rows ? r0 + band : rows;
+  float m = 0.f;
+  for (int64_t r = r0; r < r1; ++r) m = fmaxf(m, fabsf(w[r * cols + c]));
+  atomicMax(amax + c, __float_as_uint(m));
+}
+
+// Per-column int8 storage: scale[c] = amax[c] / 127 (1 for a zero column),
+// wq = clamp(rint(w / scale), -127, 127), rint rounding half to even; the
+// division is the correctly rounded float32 one.
+__global__ void k_quant_i8_cols(const float* __restrict__ w, const unsigned int* __restrict__ amax,
+                                int8_t* __restrict__ wq, float* __restrict__ scale, int64_t rows, int64_t cols) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // 8-column group
+  const int64_t per_row = cols >> 3;
+  if (g >= rows * per_row) return;
+  const int64_t r = g / per_row, c0 = (g % per_row) * 8;
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t c = c0 + e;
+    float sc = __uint_as_float(amax[c]) / 127.f;
+    sc = sc > 0.f ? sc : 1.f;
+    if (r == 0) scale[c] = sc;
+    const float q = fminf(fmaxf(rintf(w[r * cols + c] / sc), -127.f), 127.f);
+    out[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu) << (8 * (e & 3));
+  }
+  *reinterpret_cast<uint2*>(wq + r * cols + c0) = make_uint2(out[0], out[1]);
+}
+
 // packed index of (i, l), i < l, in a block of size r
 __device__ __forceinline__ int64_t tri_index(int i, int l, int r) {
   return static_cast<int64_t>(i) * r - static_cast<int64_t>(i) * (i + 1) / 2 + (l - i - 1);
@@ -648,6 +714,32 @@ void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s) {
 
 void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_gather_f32, dim3(grid1(n)), dim3(kThreads), 0, s, in, idx, out, n);
+}
+
+bool dequant_i8_cols(const int8_t* wq, const float* scale, const int32_t* cmap, float* out, int64_t rows,
+                     int64_t cols, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return true;
+  if (cols % 8 != 0) return false;
+  hipLaunchKernelGGL(k_dequant_i8_cols, dim3(grid1(rows * (cols / 8))), dim3(kThreads), 0, s, wq, scale, cmap, out,
+                     rows, cols);
+  return true;
+}
+
+void bf16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_bf16_to_f32, dim3(grid1(n)), dim3(kThreads), 0, s, in, out, n);
+}
+
+bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scale, int64_t rows, int64_t cols,
+                     hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return true;
+  if (cols % 8 != 0) return false;
+  fill_zero_f32(reinterpret_cast<float*>(amax), cols, s);  // bit pattern 0 = +0.0
+  const int64_t band = 64;
+  const dim3 g(static_cast<unsigned>((cols + kThreads - 1) / kThreads), static_cast<unsigned>((rows + band - 1) / band));
+  hipLaunchKernelGGL(k_col_absmax, g, dim3(kThreads), 0, s, w, rows, cols, band, amax);
+  hipLaunchKernelGGL(k_quant_i8_cols, dim3(grid1(rows * (cols / 8))), dim3(kThreads), 0, s, w, amax, wq, scale,
+                     rows, cols);
+  return true;
 }
 
 bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize, hipStream_t s) {

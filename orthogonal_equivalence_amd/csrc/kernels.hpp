@@ -27,6 +27,18 @@ bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize,
 // Zero n floats (a fill kernel, safe inside captured graphs).
 void fill_zero_f32(float* p, int64_t n, hipStream_t stream);
 
+// int8 base weight around a merge (per-output-column scales):
+// out[r][c] = wq[r][c] * scale[cmap ? cmap[c] : c] as float (cols % 8 == 0);
+bool dequant_i8_cols(const int8_t* wq, const float* scale, const int32_t* cmap, float* out, int64_t rows,
+                     int64_t cols, hipStream_t stream);
+// out[i] = in[i] widened from bfloat16;
+void bf16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t stream);
+// and the storage again: scale[c] = max_r |w[r][c]| / 127 (1 for a zero
+// column), wq = clamp(rint(w / scale), -127, 127); amax: cols words of
+// scratch (cols % 8 == 0).
+bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scale, int64_t rows, int64_t cols,
+                     hipStream_t stream);
+
 // Skew blocks from packed parameters: Qf[z] (b x b, float) if Qf is not null
 // and a bfloat16 copy if Qh is not null. Blocks [0, n0) come from (q0, dim0), blocks
 // [n0, n0 + n1) from (q1, dim1). A side's block z has size

@@ -240,13 +240,26 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
 struct MergeWs {
   void *C1, *C2;
   int32_t* inv_p;
+  // int8 weights: the merge runs in float on a float copy of both CNP buffers
+  float *gr32, *gp32;
+  unsigned int* amax;
 };
 
 MergeWs plan_merge(const poetx_layer* L, Carve& c) {
   MergeWs w;
-  w.C1 = c.take<char>(L->m * L->n * w_size(L));
-  w.C2 = c.take<char>(L->m * L->n * w_size(L));
+  const bool i8 = L->w_dtype == POETX_I8;
+  const int64_t es = i8 ? 4 : w_size(L);
+  w.C1 = c.take<char>(L->m * L->n * es);
+  w.C2 = c.take<char>(L->m * L->n * es);
   w.inv_p = c.take<int32_t>(L->n);
+  w.gr32 = w.gp32 = nullptr;
+  w.amax = nullptr;
+  if (i8) {
+    const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
+    w.gr32 = c.take<float>(2 * block_elems(R));
+    w.gp32 = c.take<float>(2 * block_elems(P));
+    w.amax = c.take<unsigned int>(L->n);
+  }
   return w;
 }
 
@@ -925,16 +938,60 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
 }
 
 int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, const int32_t* perm_p,
-                const void* g_r, const void* g_p, void* w0, float* q_r, float* q_p, void* ws, size_t ws_bytes,
-                hipStream_t stream) {
+                const void* g_r, const void* g_p, void* w0, float* w_scale, float* q_r, float* q_p, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
   if (!ptrs_ok({wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p})) return POETX_EINVAL;
-  if (L->w_dtype == POETX_I8) return POETX_EUNSUPPORTED;
+  const bool i8 = L->w_dtype == POETX_I8;
+  if (i8 && (!w_scale || !aligned16(w_scale))) return POETX_EINVAL;
   if (const int e = check_ws(L, 0, POETX_OP_MERGE, ws, ws_bytes)) return e;
   clear_pending_error();
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   Carve c(ws);
   MergeWs w = plan_merge(L, c);
+  if (i8) {
+    // Dequantize Wp (its column c carries the scale of original column
+    // perm_p[c]), merge in float with float copies of the (G - I) planes,
+    // scatter to the original frame, store per column again.
+    poetx_layer Lf = *L;
+    Lf.act_dtype = POETX_F32;
+    Lf.w_dtype = POETX_F32;
+    bool ok;
+    {
+      ProfScope p("merge_dequant", stream);
+      ok = dequant_i8_cols(static_cast<const int8_t*>(wp), w_scale, perm_p, static_cast<float*>(w.C1), L->m, L->n,
+                           stream);
+      bf16_to_f32(static_cast<const uint16_t*>(g_r), w.gr32, 2 * block_elems(R), stream);
+      bf16_to_f32(static_cast<const uint16_t*>(g_p), w.gp32, 2 * block_elems(P), stream);
+    }
+    {
+      ProfScope p("merge_left", stream);
+      ok = ok && transpose(w.C1, w.C2, L->m, L->n, 4, stream);
+      ok = ok && block_apply(&Lf, R, L->n, w.C2, w.C1, w.gr32, 0, nullptr, stream);
+    }
+    {
+      ProfScope p("merge_transpose", stream);
+      ok = ok && transpose(w.C1, w.C2, L->n, L->m, 4, stream);
+    }
+    {
+      ProfScope p("merge_right", stream);
+      ok = ok && block_apply(&Lf, P, L->m, w.C2, w.C1, w.gp32, 1, nullptr, stream);
+    }
+    {
+      ProfScope p("merge_scatter", stream);
+      inverse_perm(perm_p, w.inv_p, L->n, stream);
+      ok = ok && gather_cols(w.C1, L->n, nullptr, w.C2, L->n, perm_r, w.inv_p, L->n, L->m, 4, stream);
+    }
+    {
+      ProfScope p("merge_requant", stream);
+      ok = ok && requant_i8_cols(static_cast<const float*>(w.C2), w.amax, static_cast<int8_t*>(w0), w_scale, L->m,
+                                 L->n, stream);
+      fill_zero_f32(q_r, packed_len(R), stream);
+      fill_zero_f32(q_p, packed_len(P), stream);
+    }
+    if (!ok) return POETX_EUNSUPPORTED;
+    return launch_status();
+  }
   // R W0 P = Psi^T Diag(G) Wp Diag(H) Phi with Wp = Psi W0 Phi^T: the left
   // block product on the rows of Wp, then Diag(H) on the right, then the
   // scatter back to the original frame.

@@ -152,5 +152,5 @@ class DeviceLayer:
         return dq_r, dq_p, dx
 
     def merge(self, stream=None):
-        px.poetx_merge(self.L, self.wp, self.perm_r, self.perm_p, self.g_r, self.g_p, self.w0, self.q_r,
-                       self.q_p, self.ws, None, stream)
+        px.poetx_merge(self.L, self.wp, self.perm_r, self.perm_p, self.g_r, self.g_p, self.w0,
+                       self.w_scale if self.weight == "i8" else None, self.q_r, self.q_p, self.ws, None, stream)

@@ -80,7 +80,7 @@ _sig = {
     "poetx_forward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_backward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, _SZ, _P]),
-    "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "poetx_profile_count": (ctypes.c_int, []),
     "poetx_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -191,9 +191,9 @@ def poetx_backward_mem(L, T, x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt,
           _ptr(dq_p), _ptr(dx), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
-def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p, ws=None, ws_bytes=None, stream=None):
+def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, w_scale, q_r, q_p, ws=None, ws_bytes=None, stream=None):
     _call("poetx_merge", ctypes.byref(L), _ptr(wp), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
-          _ptr(w0), _ptr(q_r), _ptr(q_p), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+          _ptr(w0), _ptr(w_scale), _ptr(q_r), _ptr(q_p), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
 def poetx_profile_enable(enable):

@@ -138,11 +138,13 @@ def test_argument_errors_before_any_launch():
     with pytest.raises(px.PoetxError) as e:
         px.poetx_cnp_build(L, FAKE, None, None, None, FAKE, 1 << 30, stream=0)
     assert e.value.status == px.POETX_EINVAL
-    # merge of an int8 weight is not implemented
+    # merge of an int8 weight needs its scales (in and out)
     Lq = px.make_layer(64, 64, 16, 16, "bf16", "i8")
+    ws_m = px.poetx_workspace_bytes(Lq, 0, px.POETX_OP_MERGE)
+    assert ws_m >= 2 * 64 * 64 * 4
     with pytest.raises(px.PoetxError) as e:
-        px.poetx_merge(Lq, *([FAKE] * 8), FAKE, 1 << 30, stream=0)
-    assert e.value.status == px.POETX_EUNSUPPORTED
+        px.poetx_merge(Lq, *([FAKE] * 6), None, FAKE, FAKE, FAKE, ws_m, stream=0)
+    assert e.value.status == px.POETX_EINVAL
     # int8 weights need their scales
     with pytest.raises(px.PoetxError) as e:
         px.poetx_weight_prepare(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
