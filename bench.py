@@ -15,6 +15,7 @@ a token sample when the whole would take too long).
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -65,7 +66,10 @@ def cpu_baseline(cfg, budget_s=30.0):
     t_merge = 0.0
     if cfg.merge:
         t0 = time.perf_counter()
-        O.merge(*args)
+        if cfg.weight == "i8":
+            O.merge_xq(L["W0_raw"], L["w_scale"], *args[1:])
+        else:
+            O.merge(*args)
         t_merge = time.perf_counter() - t0
         log(f"[cpu_baseline] oracle merge: {t_merge:.2f} s")
     per_tok = max((times[t_big] - times[t_small]) / (t_big - t_small), 0.0)
@@ -201,6 +205,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
+    ap.add_argument("--merge", action="store_true",
+                    help="include one merge and the weight rebuild in every step (the 8B MLP-up workload always does)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run three plain copies of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -222,6 +228,8 @@ def main():
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
     cfg = synth.CONFIGS[args.workload]
+    if args.merge and not cfg.merge:
+        cfg = dataclasses.replace(cfg, merge=True)
     log(f"[bench] workload {cfg.name}: T={cfg.T} m={cfg.m} n={cfg.n} b={cfg.b_r}/{cfg.b_p} "
         f"{cfg.act}/{cfg.weight} merge={cfg.merge}")
     L = synth.make_layer(cfg, 0)

@@ -275,13 +275,20 @@ __global__ void k_dequant_i8_cols(const int8_t* __restrict__ wq, const float* __
   const int64_t r = g / per_row, c0 = (g % per_row) * 8;
   const uint2 q = *reinterpret_cast<const uint2*>(wq + r * cols + c0);
   const uint32_t w[2] = {q.x, q.y};
+  float sc[8];
+  if (cmap) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = scale[clamp_index(cmap[c0 + e], cols)];
+  } else {
+    const float4 s0 = *reinterpret_cast<const float4*>(scale + c0);
+    const float4 s1 = *reinterpret_cast<const float4*>(scale + c0 + 4);
+    sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+    sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+  }
   float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = static_cast<int>(c0) + e;
-    const float sc = scale[cmap ? clamp_index(cmap[c], cols) : c];
-    v[e] = static_cast<float>(static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xffu)) * sc;
-  }
+  for (int e = 0; e < 8; ++e)
+    v[e] = static_cast<float>(static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xffu)) * sc[e];
   float4* o = reinterpret_cast<float4*>(out + r * cols + c0);
   o[0] = make_float4(v[0], v[1], v[2], v[3]);
   o[1] = make_float4(v[4], v[5], v[6], v[7]);

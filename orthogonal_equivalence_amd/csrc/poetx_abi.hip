@@ -243,6 +243,7 @@ struct MergeWs {
   // int8 weights: the merge runs in float on a float copy of both CNP buffers
   float *gr32, *gp32;
   unsigned int* amax;
+  float* scale_p;  // scale of Wp's columns: w_scale[perm_p[c]]
 };
 
 MergeWs plan_merge(const poetx_layer* L, Carve& c) {
@@ -254,11 +255,13 @@ MergeWs plan_merge(const poetx_layer* L, Carve& c) {
   w.inv_p = c.take<int32_t>(L->n);
   w.gr32 = w.gp32 = nullptr;
   w.amax = nullptr;
+  w.scale_p = nullptr;
   if (i8) {
     const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
     w.gr32 = c.take<float>(2 * block_elems(R));
     w.gp32 = c.take<float>(2 * block_elems(P));
     w.amax = c.take<unsigned int>(L->n);
+    w.scale_p = c.take<float>(L->n);
   }
   return w;
 }
@@ -959,8 +962,9 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
     bool ok;
     {
       ProfScope p("merge_dequant", stream);
-      ok = dequant_i8_cols(static_cast<const int8_t*>(wp), w_scale, perm_p, static_cast<float*>(w.C1), L->m, L->n,
-                           stream);
+      gather_f32(w_scale, perm_p, w.scale_p, L->n, stream);
+      ok = dequant_i8_cols(static_cast<const int8_t*>(wp), w.scale_p, nullptr, static_cast<float*>(w.C1), L->m,
+                           L->n, stream);
       bf16_to_f32(static_cast<const uint16_t*>(g_r), w.gr32, 2 * block_elems(R), stream);
       bf16_to_f32(static_cast<const uint16_t*>(g_p), w.gp32, 2 * block_elems(P), stream);
     }
