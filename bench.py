@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
+    ap.add_argument("--no-mem-variant", action="store_true",
+                    help="skip the memory variant's timed pass (profiling runs)")
     ap.add_argument("--merge", action="store_true",
                     help="include one merge and the weight rebuild in every step (the 8B MLP-up workload always does)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -301,13 +303,15 @@ def main():
             dl.merge()
             dl.prepare()
 
-    for _ in range(2):
-        step_mem()
-    ms_mem = timed(args.steps, step_mem) / args.steps
-    log(f"[bench] memory variant: {ms_mem:.3f} ms/step")
-    variant_mem = {"ms_per_step": round(ms_mem, 4), "tokens_per_s": round(cfg.T / (ms_mem * 1e-3), 1),
-                   "activation_bytes_kept_per_layer": 0,
-                   "saving_variant_activation_bytes_per_layer": px.poetx_saved_bytes(dl.L, cfg.T)}
+    variant_mem = None
+    if not args.no_mem_variant:
+        for _ in range(2):
+            step_mem()
+        ms_mem = timed(args.steps, step_mem) / args.steps
+        log(f"[bench] memory variant: {ms_mem:.3f} ms/step")
+        variant_mem = {"ms_per_step": round(ms_mem, 4), "tokens_per_s": round(cfg.T / (ms_mem * 1e-3), 1),
+                       "activation_bytes_kept_per_layer": 0,
+                       "saving_variant_activation_bytes_per_layer": px.poetx_saved_bytes(dl.L, cfg.T)}
 
     flops_gemm = 2.0 * cfg.T * cfg.m * cfg.n
     g = [per[k] for k in ("gemm_dense_fwd", "gemm_dense_bwd") if k in per]
