@@ -160,6 +160,27 @@ def test_merge_preserves_the_layer_function():
 
 
 @pytest.mark.parametrize("cfg", [
+    _cfg("merge_resample_f32", 96, 256, 384, 64, 64, "f32", "f32", 37),
+    _cfg("merge_resample_bf16", 300, 512, 768, 256, 256, "bf16", "bf16", 38),
+], ids=lambda c: c.name)
+def test_merge_then_new_permutations_keep_the_function(cfg):
+    # after a merge q = 0, so the layer no longer depends on its permutations:
+    # fresh ones (as the caller draws at a merge) and a rebuilt weight must
+    # give the forward from before the merge
+    L, A, out, dl = _run(cfg, merge=True)
+    rng = np.random.default_rng(11)
+    dl.perm_r.copy_(to_device(rng.permutation(cfg.m).astype(np.int32), "i32"))
+    dl.perm_p.copy_(to_device(rng.permutation(cfg.n).astype(np.int32), "i32"))
+    dl.cnp_build()
+    dl.prepare()
+    z2 = to_host_f64(dl.forward(to_device(A["X_raw"], cfg.act)))
+    torch.cuda.synchronize()
+    err = rel(z2, out["z"])
+    print(f"rel {err:.2e}", flush=True)
+    assert err <= TOL[cfg.act]
+
+
+@pytest.mark.parametrize("cfg", [
     # b = 256 on the R side: left block product on the rows of Wp
     _cfg("merge_zero_q_b256", 16, 640, 1088, 256, 256, "bf16", "bf16", 35),
     # other block sizes: the left product between two transposes
