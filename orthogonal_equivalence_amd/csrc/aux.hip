@@ -528,12 +528,26 @@ __global__ void __launch_bounds__(kThreads) k_cnp_finish(const float* __restrict
 // dq for block z: dq[k(i,l)] = E[i][l] - E[l][i] for i < l < r. One
 // workgroup per 32 x 32 tile (I, L), I <= L: the mirror tile (L, I) is read
 // row-wise and transposed through LDS.
+// Tile pair p of a t x t grid with I <= L, row-major over the upper triangle.
+__device__ __forceinline__ void tile_pair(int p, int t, int& I, int& L) {
+  int i = 0;
+  while (p >= t - i) {
+    p -= t - i;
+    ++i;
+  }
+  I = i;
+  L = i + p;
+}
+
+// dq[k(i, l)] = E[i][l] - E[l][i] for the i < l of a 64 x 64 tile pair (I, L):
+// both tiles are read row-wise (256-byte rows), the mirror tile through LDS.
 __global__ void __launch_bounds__(kThreads) k_pack_asym(const float* __restrict__ E, const Seg2 sg,
-                                                       float* __restrict__ dq0, float* __restrict__ dq1, int b) {
-  __shared__ float mir[32][33];
-  const int z = blockIdx.z;
-  const int I = blockIdx.y, Lt = blockIdx.x;
-  if (I > Lt) return;
+                                                       float* __restrict__ dq0, float* __restrict__ dq1, int b,
+                                                       int t) {
+  __shared__ float mir[64][65];
+  const int z = blockIdx.y;
+  int I, Lt;
+  tile_pair(static_cast<int>(blockIdx.x), t, I, Lt);
   const float* q;
   int64_t dim;
   int zl;
@@ -541,17 +555,18 @@ __global__ void __launch_bounds__(kThreads) k_pack_asym(const float* __restrict_
   float* dq = z < sg.n0 ? dq0 : dq1;
   const int r = static_cast<int>(min(static_cast<int64_t>(b), dim - static_cast<int64_t>(zl) * b));
   const int64_t base = static_cast<int64_t>(z) * b * b;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // mirror tile (L, I): mir[l - 64 L][i - 64 I] = E[l][i]
 #pragma unroll
-  for (int k = ty; k < 32; k += 8) {
-    const int l = Lt * 32 + k, i = I * 32 + tx;
+  for (int k = ty; k < 64; k += 4) {
+    const int l = Lt * 64 + k, i = I * 64 + tx;
     mir[k][tx] = (l < b && i < b) ? E[base + static_cast<int64_t>(l) * b + i] : 0.f;
   }
   __syncthreads();
   float* dqz = dq + static_cast<int64_t>(zl) * (static_cast<int64_t>(b) * (b - 1) / 2);
 #pragma unroll
-  for (int k = ty; k < 32; k += 8) {
-    const int i = I * 32 + k, l = Lt * 32 + tx;
+  for (int k = ty; k < 64; k += 4) {
+    const int i = I * 64 + k, l = Lt * 64 + tx;
     if (i < l && l < r) dqz[tri_index(i, l, r)] = E[base + static_cast<int64_t>(i) * b + l] - mir[tx][k];
   }
 }
@@ -565,8 +580,9 @@ __global__ void __launch_bounds__(kThreads) k_reduce_symskew(const float* __rest
                                                             uint16_t* __restrict__ Ukh) {
   __shared__ float ta[32][33];
   __shared__ float tb[32][33];
-  const int z = blockIdx.z, I = blockIdx.y, Lt = blockIdx.x;
-  if (I > Lt) return;
+  const int z = blockIdx.y;
+  int I, Lt;
+  tile_pair(static_cast<int>(blockIdx.x), (b + 31) / 32, I, Lt);
   const int64_t base = static_cast<int64_t>(z) * b * b;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   // each thread sums 4 rows of tile (I, L) and 4 of tile (L, I) over the
@@ -642,8 +658,9 @@ __global__ void __launch_bounds__(kThreads) k_cnp_h1(const float* __restrict__ U
                                                     float* __restrict__ Hf, uint16_t* __restrict__ Hh) {
   __shared__ float ta[32][33];
   __shared__ float tb[32][33];
-  const int z = blockIdx.z, I = blockIdx.y, Lt = blockIdx.x;
-  if (I > Lt) return;
+  const int z = blockIdx.y;
+  int I, Lt;
+  tile_pair(static_cast<int>(blockIdx.x), (b + 31) / 32, I, Lt);
   const int64_t base = static_cast<int64_t>(z) * b * b;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int k = ty; k < 32; k += 8) {
@@ -799,21 +816,22 @@ void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int 
 void pack_asym2(const float* E, int b, int64_t dim0, int n0, float* dq0, int64_t dim1, int n1, float* dq1,
                 hipStream_t s) {
   const Seg2 sg{nullptr, nullptr, dim0, dim1, n0};
-  const unsigned t = static_cast<unsigned>((b + 31) / 32);
-  hipLaunchKernelGGL(k_pack_asym, dim3(t, t, static_cast<unsigned>(n0 + n1)), dim3(kThreads), 0, s, E, sg, dq0, dq1,
-                     b);
+  const int t = (b + 63) / 64;
+  hipLaunchKernelGGL(k_pack_asym, dim3(static_cast<unsigned>(t * (t + 1) / 2), static_cast<unsigned>(n0 + n1)),
+                     dim3(kThreads), 0, s, E, sg, dq0, dq1, b, t);
 }
 
 void reduce_symskew(const float* part, int nsplit, int b, int nblk, float* Us, float* Uk, uint16_t* Ush,
                     uint16_t* Ukh, hipStream_t s) {
   const unsigned t = static_cast<unsigned>((b + 31) / 32);
-  hipLaunchKernelGGL(k_reduce_symskew, dim3(t, t, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s, part, nsplit,
-                     b, static_cast<int64_t>(nblk) * b * b, Us, Uk, Ush, Ukh);
+  hipLaunchKernelGGL(k_reduce_symskew, dim3(t * (t + 1) / 2, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s,
+                     part, nsplit, b, static_cast<int64_t>(nblk) * b * b, Us, Uk, Ush, Ukh);
 }
 
 void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16_t* Hh, hipStream_t s) {
   const unsigned t = static_cast<unsigned>((b + 31) / 32);
-  hipLaunchKernelGGL(k_cnp_h1, dim3(t, t, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s, Uk, P1, b, Hf, Hh);
+  hipLaunchKernelGGL(k_cnp_h1, dim3(t * (t + 1) / 2, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s, Uk, P1, b,
+                     Hf, Hh);
 }
 
 }  // namespace poetx
