@@ -40,7 +40,8 @@ __all__ = [
     "scatter_cols", "block_diag_right", "block_diag_left", "permutation_matrix",
     "dense_block_orthogonal", "dequantize", "permuted_weight", "forward",
     "backward", "backward_blocks", "merge", "weight_centric_forward", "inner",
-    "requantize_int8_per_col", "merge_xq",
+    "requantize_int8_per_col", "merge_xq", "philox4x64_10", "perm_keys",
+    "sample_perm", "merge_due",
 ]
 
 
@@ -368,6 +369,83 @@ def merge_xq(Wq, scale, q_r, q_p, perm_r, perm_p, b_r, b_p):
     W = merge(dequantize(Wq, scale), q_r, q_p, perm_r, perm_p, b_r, b_p)
     codes, new_scale = requantize_int8_per_col(W)
     return codes, new_scale, W
+
+
+# ----------------------------------------------------------------------------
+# permutation draws and the merge schedule  ([BS], [MG])
+# ----------------------------------------------------------------------------
+#
+# [BS] makes Psi and Phi random permutations and [MG] restarts the rotations
+# at every merge, but the pages say neither how a permutation is drawn nor
+# when a new one is. Reading: after every merge both permutations are drawn
+# again, uniformly, from a counter-based generator, so that any device can
+# reproduce a draw from (seed, tag, draw number) alone. The generator is
+# Philox4x64 with 10 rounds, as defined by Salmon, Moraes, Dror and Shaw,
+# "Parallel random numbers: as easy as 1, 2, 3" (SC 2011).
+
+_PHILOX_MUL = (0xD2E7470EE14C6C93, 0xCA5A826395121157)  # round multipliers
+_PHILOX_WEYL = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)  # key increments
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def _mulhilo64(a, b):
+    """Full 128-bit product of uint64 arrays, as (high, low) words, from
+    32-bit limbs (NumPy has no 128-bit integers)."""
+    s32 = np.uint64(32)
+    al, ah = a & _U32, a >> s32
+    bl, bh = b & _U32, b >> s32
+    ll, lh, hl, hh = al * bl, al * bh, ah * bl, ah * bh
+    mid = (ll >> s32) + (lh & _U32) + (hl & _U32)
+    lo = (ll & _U32) | ((mid & _U32) << s32)
+    hi = hh + (lh >> s32) + (hl >> s32) + (mid >> s32)
+    return hi, lo
+
+
+def philox4x64_10(ctr, key):
+    """Philox4x64-10 of counters ctr (N x 4 uint64) under key (2 uint64).
+
+    Each round multiplies counter words 0 and 2 by the two round multipliers
+    and forms the new counter (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the
+    key gains the two Weyl increments before every round after the first.
+    Returns N x 4 uint64 output words."""
+    c = np.array(ctr, dtype=np.uint64).reshape(-1, 4).copy()
+    k0, k1 = (np.uint64(int(v)) for v in key)
+    m0, m1 = (np.uint64(v) for v in _PHILOX_MUL)
+    with np.errstate(over="ignore"):
+        for r in range(10):
+            if r:
+                k0 = k0 + np.uint64(_PHILOX_WEYL[0])
+                k1 = k1 + np.uint64(_PHILOX_WEYL[1])
+            hi0, lo0 = _mulhilo64(np.full(len(c), m0), c[:, 0])
+            hi1, lo1 = _mulhilo64(np.full(len(c), m1), c[:, 2])
+            c = np.stack([hi1 ^ c[:, 1] ^ k0, lo1, hi0 ^ c[:, 3] ^ k1, lo0], axis=1)
+    return c
+
+
+def perm_keys(dim, seed, tag, draw):
+    """Random 64-bit key of every index i < dim: word i mod 4 of the Philox
+    block at counter (i div 4, draw, 0, 0) under key (seed, tag). `tag` keeps
+    the draws of different layers and sides apart; `draw` numbers the draws
+    of one permutation."""
+    nb = (dim + 3) // 4
+    ctr = np.zeros((nb, 4), dtype=np.uint64)
+    ctr[:, 0] = np.arange(nb, dtype=np.uint64)
+    ctr[:, 1] = np.uint64(draw)
+    return philox4x64_10(ctr, (seed, tag)).reshape(-1)[:dim]
+
+
+def sample_perm(dim, seed, tag, draw):
+    """A uniformly random permutation of range(dim) [BS]: the indices in
+    ascending order of their keys, equal keys in ascending index order."""
+    return np.argsort(perm_keys(dim, seed, tag, draw), kind="stable").astype(np.int64)
+
+
+def merge_due(step, interval):
+    """[MG]: the training loop asks after optimizer step `step` (counted from
+    0) whether to merge. Reading: a merge follows every `interval`-th update,
+    so after steps interval-1, 2*interval-1, ...; the k-th merge is followed by
+    draw k of both permutations (draw 0 being the initial one)."""
+    return (step + 1) % interval == 0
 
 
 def weight_centric_forward(X, W0, q_r, q_p, perm_r, perm_p, b_r, b_p):

@@ -379,3 +379,67 @@ def test_block_restricted_gradients_agree_with_full_backward():
     assert np.allclose(r[0], full["dq_r"][0:28], atol=1e-13)
     assert np.allclose(r[1], full["dq_r"][28:56], atol=1e-13)
     assert np.allclose(p[2], full["dq_p"][56:84], atol=1e-13)
+
+
+# --- permutation draws and the merge schedule -------------------------------
+# NumPy's Philox bit generator implements the same published Philox4x64-10;
+# it increments its 256-bit counter (word 0 lowest) before each block.
+
+_U64 = (1 << 64) - 1
+
+
+def _numpy_philox_words(key, start_ctr, count):
+    g = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(start_ctr, dtype=np.uint64))
+    return g.random_raw(count).astype(np.uint64)
+
+
+@pytest.mark.parametrize("key,ctr", [((0, 0), (0, 0, 0, 0)), ((123, 456), (5, 9, 0, 0)),
+                                     ((_U64, 7), (_U64 - 1, 3, 1, 2)), ((2**63 + 11, 1), (40, 0, 0, 2**62))])
+def test_philox_is_numpy_philox(key, ctr):
+    ref = _numpy_philox_words(key, ctr, 12).reshape(3, 4)
+    c = np.array(ctr, dtype=object)
+    mine = []
+    for _ in range(3):
+        # the next counter, carried through the four words as NumPy does
+        v = int(c[0]) + int(c[1]) * 2**64 + int(c[2]) * 2**128 + int(c[3]) * 2**192 + 1
+        c = np.array([(v >> (64 * w)) & _U64 for w in range(4)], dtype=object)
+        mine.append(O.philox4x64_10(np.array(c, dtype=np.uint64)[None, :], key)[0])
+    assert np.array_equal(np.array(mine, dtype=np.uint64), ref)
+
+
+@pytest.mark.parametrize("dim,draw", [(1, 0), (13, 0), (64, 3), (1031, 2**40)])
+def test_perm_keys_are_the_philox_stream_from_counter_zero(dim, draw):
+    seed, tag = 987654321, 5
+    # a start one block before (0, draw, 0, 0): NumPy increments before drawing
+    start = (_U64, _U64, _U64, _U64) if draw == 0 else (_U64, draw - 1, 0, 0)
+    ref = _numpy_philox_words((seed, tag), start, dim)
+    assert np.array_equal(O.perm_keys(dim, seed, tag, draw), ref)
+
+
+def test_sample_perm_sorts_by_key_then_index():
+    for dim in (1, 2, 37, 300):
+        keys = O.perm_keys(dim, 11, 3, 1)
+        p = O.sample_perm(dim, 11, 3, 1)
+        assert sorted(p.tolist()) == list(range(dim))
+        brute = sorted(range(dim), key=lambda i: (int(keys[i]), i))
+        assert p.tolist() == brute
+    # different tags and draws give different permutations
+    assert not np.array_equal(O.sample_perm(300, 11, 3, 1), O.sample_perm(300, 11, 4, 1))
+    assert not np.array_equal(O.sample_perm(300, 11, 3, 1), O.sample_perm(300, 11, 3, 2))
+
+
+def test_sample_perm_is_uniform_on_four_elements():
+    # 2400 draws of a 4-element permutation: each of the 24 appears about 100
+    # times (binomial standard deviation 9.8)
+    counts = {}
+    for d in range(2400):
+        k = tuple(O.sample_perm(4, 2024, 9, d).tolist())
+        counts[k] = counts.get(k, 0) + 1
+    assert len(counts) == 24
+    assert min(counts.values()) >= 60 and max(counts.values()) <= 140
+
+
+def test_merge_schedule_merges_after_every_interval_updates():
+    due = [s for s in range(1000) if O.merge_due(s, 200)]
+    assert due == [199, 399, 599, 799, 999]
+    assert all(O.merge_due(s, 1) for s in range(10))
