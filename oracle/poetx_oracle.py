@@ -40,8 +40,8 @@ __all__ = [
     "scatter_cols", "block_diag_right", "block_diag_left", "permutation_matrix",
     "dense_block_orthogonal", "dequantize", "permuted_weight", "forward",
     "backward", "backward_blocks", "merge", "weight_centric_forward", "inner",
-    "requantize_int8_per_col", "merge_xq", "philox4x64_10", "perm_keys",
-    "sample_perm", "merge_due",
+    "requantize_int8_per_col", "merge_xq", "philox4x64_10", "perm_words",
+    "perm_keys", "sample_perm", "merge_due", "PERM_KEY_BITS",
 ]
 
 
@@ -422,8 +422,8 @@ def philox4x64_10(ctr, key):
     return c
 
 
-def perm_keys(dim, seed, tag, draw):
-    """Random 64-bit key of every index i < dim: word i mod 4 of the Philox
+def perm_words(dim, seed, tag, draw):
+    """Random 64-bit word of every index i < dim: word i mod 4 of the Philox
     block at counter (i div 4, draw, 0, 0) under key (seed, tag). `tag` keeps
     the draws of different layers and sides apart; `draw` numbers the draws
     of one permutation."""
@@ -434,9 +434,20 @@ def perm_keys(dim, seed, tag, draw):
     return philox4x64_10(ctr, (seed, tag)).reshape(-1)[:dim]
 
 
+PERM_KEY_BITS = 44  # random bits of a sort key; dim <= 2**20 keeps the index in the rest
+
+
+def perm_keys(dim, seed, tag, draw):
+    """Sort key of every index: the top 44 bits of its random word."""
+    return perm_words(dim, seed, tag, draw) >> np.uint64(64 - PERM_KEY_BITS)
+
+
 def sample_perm(dim, seed, tag, draw):
     """A uniformly random permutation of range(dim) [BS]: the indices in
-    ascending order of their keys, equal keys in ascending index order."""
+    ascending order of their keys, equal keys in ascending index order. (With
+    dim <= 2**20 two keys of 44 random bits are equal with probability below
+    dim**2 / 2**45, so the index order decides almost never.)"""
+    assert 1 <= dim <= 1 << 20
     return np.argsort(perm_keys(dim, seed, tag, draw), kind="stable").astype(np.int64)
 
 

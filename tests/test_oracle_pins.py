@@ -408,20 +408,22 @@ def test_philox_is_numpy_philox(key, ctr):
 
 
 @pytest.mark.parametrize("dim,draw", [(1, 0), (13, 0), (64, 3), (1031, 2**40)])
-def test_perm_keys_are_the_philox_stream_from_counter_zero(dim, draw):
+def test_perm_words_are_the_philox_stream_from_counter_zero(dim, draw):
     seed, tag = 987654321, 5
     # a start one block before (0, draw, 0, 0): NumPy increments before drawing
     start = (_U64, _U64, _U64, _U64) if draw == 0 else (_U64, draw - 1, 0, 0)
     ref = _numpy_philox_words((seed, tag), start, dim)
-    assert np.array_equal(O.perm_keys(dim, seed, tag, draw), ref)
+    assert np.array_equal(O.perm_words(dim, seed, tag, draw), ref)
+    # the sort keys are the words' top 44 bits
+    assert np.array_equal(O.perm_keys(dim, seed, tag, draw), np.array([int(v) >> 20 for v in ref], dtype=np.uint64))
 
 
 def test_sample_perm_sorts_by_key_then_index():
     for dim in (1, 2, 37, 300):
-        keys = O.perm_keys(dim, 11, 3, 1)
+        words = O.perm_words(dim, 11, 3, 1)
         p = O.sample_perm(dim, 11, 3, 1)
         assert sorted(p.tolist()) == list(range(dim))
-        brute = sorted(range(dim), key=lambda i: (int(keys[i]), i))
+        brute = sorted(range(dim), key=lambda i: (int(words[i]) >> 20, i))
         assert p.tolist() == brute
     # different tags and draws give different permutations
     assert not np.array_equal(O.sample_perm(300, 11, 3, 1), O.sample_perm(300, 11, 4, 1))
