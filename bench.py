@@ -2,9 +2,9 @@
 """Throughput of the POET-X layer hot path on one GPU.
 
 One step = CNP build of R and P, forward, backward to dq_R / dq_P / dx, and
-(for the Llama-8B MLP up-projection workload) one merge W0 <- R W0 P followed
-by the permuted-frame weight rebuild, all on synthetic seeded inputs already
-resident in HBM. Prints one JSON line on stdout; progress goes to stderr.
+(for the Llama-8B MLP up-projection workload) one merge cycle: W0 <- R W0 P,
+new draws of both permutations and the permuted-frame weight rebuild, all on
+synthetic seeded inputs already resident in HBM. Prints one JSON line on stdout; progress goes to stderr.
 
 The step time comes from a timed pass of K steps with nothing else on the
 stream. A second timed pass of K steps runs with the library's HIP-event log
@@ -16,6 +16,7 @@ a token sample when the whole would take too long).
 
 import argparse
 import dataclasses
+import itertools
 import json
 import os
 import sys
@@ -29,6 +30,7 @@ METRIC = "POET-X layer fwd+bwd tokens/s at Llama-8B shapes; % of MFMA/HBM peak o
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+MERGE_SEED = 2026  # seed of the permutation draws that follow each merge
 
 
 def log(*a):
@@ -246,14 +248,21 @@ def main():
     dq_r = torch.empty_like(dl.q_r)
     dq_p = torch.empty_like(dl.q_p)
     dl.prepare()
+    draws = itertools.count(1)
+
+    def merge_cycle():
+        # what a training loop runs at a merge: W0 <- R W0 P with q <- 0, a
+        # new draw of both permutations, the permuted-frame weight rebuilt
+        dl.merge()
+        dl.resample(MERGE_SEED, 0, next(draws))
+        dl.prepare()
 
     def step():
         dl.cnp_build()
         dl.forward(x, z)
         dl.backward(dz, dq_r, dq_p, dx)
         if cfg.merge:
-            dl.merge()
-            dl.prepare()
+            merge_cycle()
 
     for _ in range(args.warmup):
         step()
@@ -300,8 +309,7 @@ def main():
         dl.forward_mem(x, z)
         dl.backward_mem(x, dz, dq_r, dq_p, dx)
         if cfg.merge:
-            dl.merge()
-            dl.prepare()
+            merge_cycle()
 
     variant_mem = None
     if not args.no_mem_variant:
@@ -327,7 +335,7 @@ def main():
     fwd_bwd_names = [k for k in per if k.startswith(("cnp_build", "gather", "apply", "gemm", "scatter",
                                                      "grad", "cnp_bwd"))]
     ms_fwd_bwd = sum(per[k][0] for k in fwd_bwd_names) / args.steps
-    ms_merge = sum(per[k][0] for k in per if k.startswith(("merge", "prepare"))) / args.steps
+    ms_merge = sum(per[k][0] for k in per if k.startswith(("merge", "sample_perm", "prepare"))) / args.steps
 
     yard = None
     if not args.no_yardstick and bf16:
@@ -362,13 +370,13 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weight, N(0,1e-3^2) packed skew params)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "m": cfg.m, "n": cfg.n, "b_r": cfg.b_r,
                    "b_p": cfg.b_p, "weight": cfg.weight,
-                   "step": "cnp_build+forward+backward" + ("+merge+weight_prepare" if cfg.merge else "")},
+                   "step": "cnp_build+forward+backward" + ("+merge+perm_draw+weight_prepare" if cfg.merge else "")},
         "roofline": roofline,
         "cpu_baseline": None,
         "ms_per_step_with_kernel_log": round(ms_logged / args.steps, 4),
         "fwd_bwd_ms": round(ms_fwd_bwd, 4),
         "fwd_bwd_tokens_per_s": round(cfg.T / (ms_fwd_bwd * 1e-3), 1),
-        "merge_prepare_ms": round(ms_merge, 4),
+        "merge_cycle_ms": round(ms_merge, 4),
         "tokens_per_s_merge_every_200": round(cfg.T / ((ms_fwd_bwd + ms_merge / 200) * 1e-3), 1),
         "variant_mem": variant_mem,
         "kernels_ms": kernels,

@@ -74,7 +74,8 @@ enum {
   POETX_OP_BACKWARD = 3,
   POETX_OP_MERGE = 4,
   POETX_OP_FORWARD_MEM = 5,
-  POETX_OP_BACKWARD_MEM = 6
+  POETX_OP_BACKWARD_MEM = 6,
+  POETX_OP_SAMPLE_PERM = 7
 };
 
 typedef struct poetx_layer {
@@ -119,7 +120,7 @@ POETX_API size_t poetx_saved_bytes(const poetx_layer* L, int64_t T);
 POETX_API size_t poetx_wbuf_bytes(const poetx_layer* L);
 
 /* Workspace bytes an operation needs for T tokens (T ignored by CNP build,
- * weight preparation and merge). 0 means none. */
+ * weight preparation, merge and permutation draws). 0 means none. */
 POETX_API size_t poetx_workspace_bytes(const poetx_layer* L, int64_t T, int op);
 
 /* CNP build (section "3. Cayley-Neumann 参数化优化": G = (I+Q)(I+Q+Q^2+Q^3),
@@ -222,6 +223,25 @@ POETX_API int poetx_merge(const poetx_layer* L, const void* wp,
                 const void* g_r, const void* g_p,
                 void* w0, float* w_scale, float* q_r, float* q_p,
                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Draw of a uniformly random permutation of [0, dim) for Psi or Phi. The
+ * permutations are random (section "2. 块随机正交变换"); a merge restarts
+ * the rotations every merge_interval steps (section "代码与部署"), and a
+ * training loop then draws both permutations again. Index i's key is the top
+ * 44 bits of word (i mod 4) of Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter
+ * (i div 4, draw, 0, 0) under key (seed, tag); perm lists the indices in
+ * ascending order of (key, index). The same (dim, seed, tag, draw) gives the
+ * same permutation on every device and in every process.
+ *   seed: run seed; tag: separates layers and the two sides; draw: number of
+ *       the draw (0 = initial, k = after the k-th merge).
+ *   perm [dim] int32, overwritten.
+ *   ws: at least 8 * dim bytes of scratch (poetx_workspace_bytes(L, 0,
+ *       POETX_OP_SAMPLE_PERM) covers both sides of a layer L).
+ * 1 <= dim <= 2^20 (POETX_EUNSUPPORTED above). Each index is ranked by
+ * counting smaller keys, so the work grows as dim^2. */
+POETX_API int poetx_sample_perm(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw,
+                      int32_t* perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Kernel timing log (tracing). poetx_profile_enable(1) clears the log and
  * starts recording: from then on every step of every entry point (e.g.

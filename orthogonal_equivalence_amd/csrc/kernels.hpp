@@ -127,4 +127,13 @@ int block_grad_splits(int64_t T, int64_t dim, int b);
 bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int64_t ld, int64_t T, int64_t dim,
                      int b, int nsplit, hipStream_t stream);
 
+// Seeded uniformly random permutation of [0, n) (perm.hip): index i's key is
+// the top 44 bits of word i mod 4 of Philox4x64-10 at counter
+// (i div 4, draw, 0, 0) under key (seed, tag), and perm lists the indices by
+// ascending (key, index). keys: n words of scratch. 1 <= n <= kMaxPermDim
+// (returns false otherwise).
+constexpr int64_t kMaxPermDim = int64_t(1) << 20;
+bool sample_perm(int64_t n, uint64_t seed, uint64_t tag, uint64_t draw, int32_t* perm, uint64_t* keys,
+                 hipStream_t stream);
+
 }  // namespace poetx

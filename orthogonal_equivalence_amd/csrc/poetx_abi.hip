@@ -275,6 +275,9 @@ size_t cnp_build_bytes(const poetx_layer* L) {
 // X1 (T x m) then Y1 (T x n), activation dtype: the forward's saved tensors
 int64_t saved_region(const poetx_layer* L, int64_t T) { return T * (L->m + L->n) * act_size(L); }
 
+// Scratch of one permutation draw: one packed 64-bit key per index.
+size_t perm_ws_bytes(int64_t dim) { return static_cast<size_t>(dim) * sizeof(uint64_t); }
+
 size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
   Carve c(nullptr);
   switch (op) {
@@ -298,6 +301,7 @@ size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
       plan_bwd(L, T, b);
       return std::max(f.off, b.off);
     }
+    case POETX_OP_SAMPLE_PERM: return perm_ws_bytes(std::max(L->m, L->n));
     default: return 0;
   }
 }
@@ -1039,6 +1043,20 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
     fill_zero_f32(q_p, packed_len(P), stream);
   }
   if (!ok) return POETX_EUNSUPPORTED;
+  return launch_status();
+}
+
+int poetx_sample_perm(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw, int32_t* perm, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  if (dim < 1 || !perm || !aligned16(perm)) return POETX_EINVAL;
+  if (dim > kMaxPermDim) return POETX_EUNSUPPORTED;
+  if (ws_bytes < perm_ws_bytes(dim)) return POETX_EWORKSPACE;
+  if (!ws || !aligned16(ws)) return POETX_EINVAL;
+  clear_pending_error();
+  {
+    ProfScope p("sample_perm", stream);
+    if (!sample_perm(dim, seed, tag, draw, perm, static_cast<uint64_t*>(ws), stream)) return POETX_EUNSUPPORTED;
+  }
   return launch_status();
 }
 

@@ -70,7 +70,7 @@ class DeviceLayer:
         self.T_max = max(T, self.T_max)
         self.saved = torch.empty(max(px.poetx_saved_bytes(self.L, self.T_max), 16), dtype=torch.uint8,
                                  device=self.device)
-        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(7))
+        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(8))
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
 
@@ -154,3 +154,24 @@ class DeviceLayer:
     def merge(self, stream=None):
         px.poetx_merge(self.L, self.wp, self.perm_r, self.perm_p, self.g_r, self.g_p, self.w0,
                        self.w_scale if self.weight == "i8" else None, self.q_r, self.q_p, self.ws, None, stream)
+
+    def resample(self, seed, tag, draw, stream=None):
+        """Draw both permutations again: draw ``draw`` of Psi under tag 2*tag
+        and of Phi under tag 2*tag + 1 (``tag`` names the layer)."""
+        px.poetx_sample_perm(self.m, seed, 2 * tag, draw, self.perm_r, self.ws, None, stream)
+        px.poetx_sample_perm(self.n, seed, 2 * tag + 1, draw, self.perm_p, self.ws, None, stream)
+
+    def merge_if_needed(self, step, interval, seed, tag, stream=None):
+        """Called after optimizer step ``step`` (counted from 0). After every
+        ``interval``-th update: CNP blocks of the current q, W0 <- R W0 P with
+        q <- 0, draw k = (step + 1) / interval of both permutations, and the
+        permuted-frame weight and CNP blocks rebuilt for them. Returns whether
+        it merged."""
+        if (step + 1) % interval:
+            return False
+        self.cnp_build(stream)
+        self.merge(stream)
+        self.resample(seed, tag, (step + 1) // interval, stream)
+        self.prepare(stream)
+        self.cnp_build(stream)
+        return True

@@ -27,13 +27,13 @@ POETX_OK, POETX_EINVAL, POETX_EUNSUPPORTED, POETX_EHIP, POETX_EWORKSPACE = 0, 1,
 POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
 POETX_SIDE_R, POETX_SIDE_P = 0, 1
 (POETX_OP_CNP_BUILD, POETX_OP_WEIGHT_PREPARE, POETX_OP_FORWARD, POETX_OP_BACKWARD,
- POETX_OP_MERGE, POETX_OP_FORWARD_MEM, POETX_OP_BACKWARD_MEM) = 0, 1, 2, 3, 4, 5, 6
+ POETX_OP_MERGE, POETX_OP_FORWARD_MEM, POETX_OP_BACKWARD_MEM, POETX_OP_SAMPLE_PERM) = range(8)
 
 EXPORTED = [
     "poetx_abi_version", "poetx_strerror", "poetx_last_hip_error", "poetx_packed_len", "poetx_gbuf_bytes",
     "poetx_saved_bytes", "poetx_wbuf_bytes", "poetx_workspace_bytes", "poetx_cnp_build",
     "poetx_weight_prepare", "poetx_forward", "poetx_backward", "poetx_forward_mem", "poetx_backward_mem",
-    "poetx_merge",
+    "poetx_merge", "poetx_sample_perm",
     "poetx_profile_enable", "poetx_profile_count", "poetx_profile_get",
 ]
 
@@ -81,6 +81,8 @@ _sig = {
     "poetx_backward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, _SZ, _P]),
     "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "poetx_sample_perm": (ctypes.c_int, [_I64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P, _P, _SZ,
+                                         _P]),
     "poetx_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "poetx_profile_count": (ctypes.c_int, []),
     "poetx_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -194,6 +196,10 @@ def poetx_backward_mem(L, T, x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt,
 def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, w_scale, q_r, q_p, ws=None, ws_bytes=None, stream=None):
     _call("poetx_merge", ctypes.byref(L), _ptr(wp), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
           _ptr(w0), _ptr(w_scale), _ptr(q_r), _ptr(q_p), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+
+
+def poetx_sample_perm(dim, seed, tag, draw, perm, ws=None, ws_bytes=None, stream=None):
+    _call("poetx_sample_perm", dim, seed, tag, draw, _ptr(perm), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
 def poetx_profile_enable(enable):

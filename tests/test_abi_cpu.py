@@ -28,7 +28,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = ctypes.CDLL(px.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -149,6 +149,22 @@ def test_argument_errors_before_any_launch():
     with pytest.raises(px.PoetxError) as e:
         px.poetx_weight_prepare(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == px.POETX_EINVAL
+
+
+def test_sample_perm_argument_errors():
+    big = 8 << 20
+    for dim, ptr, ws, ws_bytes, status in [
+            (0, FAKE, FAKE, big, px.POETX_EINVAL), (-5, FAKE, FAKE, big, px.POETX_EINVAL),
+            (16, None, FAKE, big, px.POETX_EINVAL), (16, FAKE + 4, FAKE, big, px.POETX_EINVAL),
+            ((1 << 20) + 1, FAKE, FAKE, 2 * big, px.POETX_EUNSUPPORTED),
+            (16, FAKE, FAKE, 127, px.POETX_EWORKSPACE), (16, FAKE, None, 128, px.POETX_EINVAL),
+            (16, FAKE, FAKE + 8, 128, px.POETX_EINVAL)]:
+        with pytest.raises(px.PoetxError) as e:
+            px.poetx_sample_perm(dim, 1, 2, 3, ptr, ws, ws_bytes, stream=0)
+        assert e.value.status == status, (dim, ptr, ws, ws_bytes)
+    # the layer's workspace query covers the wider side
+    L = px.make_layer(4096, 14336, 256, 256, "bf16", "bf16")
+    assert px.poetx_workspace_bytes(L, 0, px.POETX_OP_SAMPLE_PERM) == 8 * 14336
 
 
 def test_last_hip_error_without_failure():

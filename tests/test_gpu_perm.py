@@ -1,0 +1,121 @@
+"""Seeded permutation draws and the merge schedule on the GPU against the
+float64 oracle (sample_perm, merge_due, merge, forward).
+
+A draw is integer work, so the GPU's permutation must equal the oracle's bit
+for bit. The schedule test runs a few training steps with a stand-in for the
+optimizer (new seeded q every step; the update rule itself is not on the
+pages): at every step the layer's state and function must match the oracle's,
+and a merge must leave the layer's function unchanged.
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from orthogonal_equivalence_amd import poetx as px  # noqa: E402
+from orthogonal_equivalence_amd import synth  # noqa: E402
+from orthogonal_equivalence_amd.device import DeviceLayer, to_device, to_host_f64  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    torch.cuda.init()
+
+
+DRAWS = [
+    (1, 0, 0, 0),
+    (3, 5, 1, 0),
+    (64, 7, 2, 1),            # one ranking workgroup exactly
+    (65, 7, 3, 1),            # a second, nearly empty workgroup
+    (511, 11, 4, 2),          # 16 waves x 32-word batches = 512 words per round
+    (512, 11, 4, 3),
+    (513, 11, 5, 4),
+    (2049, 11, 5, 5),         # ragged tails in every wave's range
+    (4096, 2024, 0, 1),       # Llama-8B hidden width
+    (14336, 2024, 1, 1),      # Llama-8B MLP width
+    (28672, 1, 2**63 + 5, 2**40),
+    (100003, 2**64 - 1, 9, 2**64 - 1),
+    (1 << 20, 3, 6, 7),       # the largest accepted dim
+]
+
+
+@pytest.mark.parametrize("dim,seed,tag,draw", DRAWS, ids=lambda v: str(v))
+def test_sample_perm_matches_the_oracle(dim, seed, tag, draw):
+    print(f"\n[gpu] sample_perm dim={dim} seed={seed} tag={tag} draw={draw}", flush=True)
+    perm = torch.full((dim,), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(8 * dim, dtype=torch.uint8, device="cuda")
+    px.poetx_sample_perm(dim, seed, tag, draw, perm, ws)
+    torch.cuda.synchronize()
+    got = perm.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, O.sample_perm(dim, seed, tag, draw))
+
+
+def test_sample_perm_on_a_side_stream_and_repeated():
+    s = torch.cuda.Stream()
+    a = torch.empty(4096, dtype=torch.int32, device="cuda")
+    b = torch.empty(4096, dtype=torch.int32, device="cuda")
+    ws = torch.empty(8 * 4096, dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(s):
+        px.poetx_sample_perm(4096, 5, 6, 7, a, ws, stream=s)
+        px.poetx_sample_perm(4096, 5, 6, 7, b, ws, stream=s)
+    s.synchronize()
+    assert torch.equal(a, b)
+    assert np.array_equal(a.cpu().numpy().astype(np.int64), O.sample_perm(4096, 5, 6, 7))
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+SCHEDULES = [
+    synth.LayerConfig("sched_f32", 61, 96, 256, 384, 64, 64, "f32", "f32"),
+    synth.LayerConfig("sched_bf16", 62, 128, 512, 768, 256, 256, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", SCHEDULES, ids=lambda c: c.name)
+def test_merge_schedule_matches_the_oracle(cfg):
+    print(f"\n[gpu] {cfg.name} m={cfg.m} n={cfg.n} b={cfg.b_r}", flush=True)
+    tol = 1e-5 if cfg.act == "f32" else 2e-2
+    L = synth.make_layer(cfg, 0)
+    A = synth.make_activations(cfg, 0)
+    dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
+    dl.load(L)
+    x = to_device(A["X_raw"], cfg.act)
+    seed, tag, interval = 77, 3, 2
+    W = L["W0"].astype(np.float64)
+    perm_r, perm_p = L["perm_r"], L["perm_p"]
+    rng = np.random.default_rng([cfg.cfg_id, 1])
+    for step in range(5):
+        # stand-in for an optimizer update of the packed parameters
+        q_r = (rng.standard_normal(len(L["q_r"])) * 1e-2).astype(np.float32)
+        q_p = (rng.standard_normal(len(L["q_p"])) * 1e-2).astype(np.float32)
+        dl.q_r.copy_(torch.from_numpy(q_r))
+        dl.q_p.copy_(torch.from_numpy(q_p))
+        dl.cnp_build()
+        dl.prepare()
+        z_before = to_host_f64(dl.forward(x))
+        merged = dl.merge_if_needed(step, interval, seed, tag)
+        assert merged == O.merge_due(step, interval), step
+        if merged:
+            k = (step + 1) // interval
+            W = O.merge(W, q_r, q_p, perm_r, perm_p, cfg.b_r, cfg.b_p)
+            perm_r = O.sample_perm(cfg.m, seed, 2 * tag, k)
+            perm_p = O.sample_perm(cfg.n, seed, 2 * tag + 1, k)
+            q_r, q_p = np.zeros_like(q_r), np.zeros_like(q_p)
+        z_after = to_host_f64(dl.forward(x))
+        torch.cuda.synchronize()
+        assert np.array_equal(dl.perm_r.cpu().numpy().astype(np.int64), perm_r), step
+        assert np.array_equal(dl.perm_p.cpu().numpy().astype(np.int64), perm_p), step
+        assert np.array_equal(dl.q_r.cpu().numpy(), q_r) and np.array_equal(dl.q_p.cpu().numpy(), q_p), step
+        w_err = _rel(to_host_f64(dl.w0), W)
+        z_ref = O.forward(A["X"], W, q_r, q_p, perm_r, perm_p, cfg.b_r, cfg.b_p)["Z"]
+        errs = (w_err, _rel(z_after, z_ref), _rel(z_after, z_before))
+        print(f"step {step} merged={merged} W0 {errs[0]:.2e} z {errs[1]:.2e} z vs before {errs[2]:.2e}",
+              flush=True)
+        assert max(errs) <= tol, (step, errs)
