@@ -209,6 +209,8 @@ def main():
     ap.add_argument("--no-yardstick", action="store_true")
     ap.add_argument("--no-mem-variant", action="store_true",
                     help="skip the memory variant's timed pass (profiling runs)")
+    ap.add_argument("--no-spread", action="store_true",
+                    help="skip the per-step warm and cold spread passes (profiling runs)")
     ap.add_argument("--merge", action="store_true",
                     help="include one merge and the weight rebuild in every step (the 8B MLP-up workload always does)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -321,6 +323,31 @@ def main():
                        "activation_bytes_kept_per_layer": 0,
                        "saving_variant_activation_bytes_per_layer": px.poetx_saved_bytes(dl.L, cfg.T)}
 
+    # pass 4: spread of single-step times, warm (back to back) and cold (a
+    # 1 GiB write before each step evicts the 256 MB last-level cache and
+    # every L2, so the step starts with nothing of its inputs cached)
+    def step_spread(steps, before):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            if before is not None:
+                before()
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        at = lambda f: ms[int(round(f * (len(ms) - 1)))]  # noqa: E731
+        return {"median_ms": round(at(0.5), 4), "p10_ms": round(at(0.1), 4), "p90_ms": round(at(0.9), 4)}
+
+    spread = None
+    if not args.no_spread:
+        evict = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        spread = {"warm": step_spread(args.steps, None), "cold": step_spread(args.steps, evict.zero_),
+                  "cold_evict_bytes": evict.numel() * 4}
+        del evict
+        log(f"[bench] step spread: {json.dumps(spread)}")
+
     flops_gemm = 2.0 * cfg.T * cfg.m * cfg.n
     g = [per[k] for k in ("gemm_dense_fwd", "gemm_dense_bwd") if k in per]
     g_ms = sum(v[0] for v in g) / max(sum(v[1] for v in g), 1)
@@ -378,6 +405,7 @@ def main():
         "fwd_bwd_tokens_per_s": round(cfg.T / (ms_fwd_bwd * 1e-3), 1),
         "merge_cycle_ms": round(ms_merge, 4),
         "tokens_per_s_merge_every_200": round(cfg.T / ((ms_fwd_bwd + ms_merge / 200) * 1e-3), 1),
+        "step_spread": spread,
         "variant_mem": variant_mem,
         "kernels_ms": kernels,
         "kernel_roofline": kernel_roofline(cfg, per),
