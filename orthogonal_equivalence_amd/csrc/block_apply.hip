@@ -8,7 +8,11 @@
 // gfx950 design: one workgroup owns one block and a contiguous run of
 // tokens. Each of its b/32 waves keeps its 32 output columns of B_j resident
 // in registers as MFMA fragments for the whole run, so B_j is read once per
-// workgroup. 32-token sub-tiles stream global -> LDS with
+// workgroup. A 512 x 512 plane would fill a CU's whole register file, so for
+// b = 512 two workgroups share a block and a token run, each owning 256 of
+// its output columns (8 waves of 128 fragment registers) and staging the
+// full 512-column input; the two are issued 8 workgroups apart so that they
+// land on the same XCD and the second read of the input hits its L2. 32-token sub-tiles stream global -> LDS with
 // global_load_lds_dwordx4 into two swizzled stages (the next sub-tile is in
 // flight while the current one is multiplied); v_mfma_f32_32x32x16_bf16 does
 // the product; a per-wave LDS slab turns the accumulator into rows, where the
@@ -33,23 +37,39 @@ __device__ __forceinline__ int swz_row(int r) {
   else return (r >> 1) & 7;
 }
 
-// two workgroups per CU: 2 * (waves per SIMD of one workgroup) waves per SIMD
+// workgroups of 8 waves and b <= 256: two per CU, 4 waves per SIMD; b = 512:
+// one per CU (its fragments take 128 registers per lane), 2 waves per SIMD
 template <int B>
-__global__ void __launch_bounds__(64 * (B / 32), (B >= 256 ? 4 : 2))
+__global__ void __launch_bounds__(64 * ((B > 256 ? 256 : B) / 32), (B > 256 ? 2 : (B >= 256 ? 4 : 2)))
 k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t ld, const bf16_t* __restrict__ plane,
-              const float* __restrict__ scale, int64_t T, int64_t dim, int tokens_per_wg, int wgs_per_block) {
-  constexpr int NW = B / 32;
+              const float* __restrict__ scale, int64_t T, int64_t dim, int tokens_per_wg, int wgs_per_block,
+              int npairs) {
+  constexpr int NH = B > 256 ? 2 : 1;  // workgroups sharing a block (column halves)
+  constexpr int NW = B / NH / 32;      // waves, 32 output columns each
   constexpr int ROWB = B * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int STAGE = TT * ROWB;
+  constexpr int LPW = STAGE / 1024 / NW;  // 1 KB direct loads per wave and stage
   constexpr int KS = B / 16;
   constexpr int SLAB = 32 * 33 * 4;  // per wave: 32 rows x 32 fp32 columns (+1 pad)
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + NW * SLAB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int blk = blockIdx.x / wgs_per_block;
-  const int part = blockIdx.x % wgs_per_block;
+  int blk, part, cofs = 0;  // cofs: first output column of this workgroup within the block
+  if constexpr (NH == 2) {
+    // in each run of 16 workgroups, the first 8 take half 0 of 8 (block,
+    // token run) pairs and the next 8 take half 1 of the same pairs
+    const int idx = static_cast<int>(blockIdx.x);
+    const int pair = ((idx >> 4) << 3) | (idx & 7);
+    if (pair >= npairs) return;
+    blk = pair / wgs_per_block;
+    part = pair % wgs_per_block;
+    cofs = ((idx >> 3) & 1) * (B / NH);
+  } else {
+    blk = blockIdx.x / wgs_per_block;
+    part = blockIdx.x % wgs_per_block;
+  }
   const int64_t col0 = static_cast<int64_t>(blk) * B;
   const int width = static_cast<int>(min(static_cast<int64_t>(B), dim - col0));  // short last block
   const int cmax = width / 8 - 1;                                                  // last valid chunk
@@ -60,17 +80,17 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
 
   // this wave's 32 columns of B_j as MFMA B-operand fragments (column n, 8 k's)
   const int lcol = lane & 31;
-  const int ncol = wave * 32 + lcol;
+  const int ncol = cofs + wave * 32 + lcol;
   const bf16_t* brow = plane + static_cast<int64_t>(blk) * B * B + static_cast<int64_t>(ncol) * B + (lane >> 5) * 8;
   bf16x8_t gfrag[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) gfrag[kk] = *reinterpret_cast<const bf16x8_t*>(brow + kk * 16);
 
-  // direct loads: each wave fills 2 x 1 KB of a stage
+  // direct loads: each wave fills LPW x 1 KB of a stage
   auto issue = [&](int sub, int stage) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = (wave * 2 + i) * 64 + lane;
+    for (int i = 0; i < LPW; ++i) {
+      const int q = (wave * LPW + i) * 64 + lane;
       const int row = q / CPR, slot = q % CPR;
       int c = slot ^ swz_row<B>(row);
       c = c < cmax ? c : cmax;
@@ -78,7 +98,7 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
       t = t < t_end ? t : t_end - 1;
       const bf16_t* src = in + t * ld + col0 + c * 8;
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       (lds_void_t)(smem + stage * STAGE + (wave * 2 + i) * 1024), 16, 0, 0);
+                                       (lds_void_t)(smem + stage * STAGE + (wave * LPW + i) * 1024), 16, 0, 0);
     }
   };
 
@@ -111,7 +131,7 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
       const int q = lane + i * 64;
       const int row = q >> 2, c4 = q & 3;
       const int64_t t = t_begin + static_cast<int64_t>(s) * TT + row;
-      const int col = wave * 32 + c4 * 8;
+      const int col = cofs + wave * 32 + c4 * 8;
       const int chunk = col >> 3;
       const uint4 xr = *reinterpret_cast<const uint4*>(st + row * ROWB + ((chunk ^ swz_row<B>(row)) << 4));
       const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
@@ -275,29 +295,39 @@ bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const 
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
                       int64_t T, int64_t dim, int b, hipStream_t s) {
   if (T <= 0) return true;
-  if (b != 64 && b != 128 && b != 256) return false;
+  if (b != 64 && b != 128 && b != 256 && b != 512) return false;
   const int nblk = static_cast<int>((dim + b - 1) / b);
-  // Workgroups resident at once on the 256 CUs: b = 256 is limited to two per
-  // CU by registers (8 waves of up to 128 VGPRs), b = 128 to four (registers
-  // and LDS), b = 64 to nine by LDS (eight used). Every workgroup streams the same number of tokens, and one
-  // more than fits would cost a whole second round: floor(resident / blocks)
-  // workgroups per block.
-  const int64_t resident = 256 * (b == 256 ? 2 : (b == 128 ? 4 : 8));
-  int64_t wpb = std::max<int64_t>(1, resident / nblk);
+  const int nh = b == 512 ? 2 : 1;  // workgroups per block and token run
+  // Workgroups resident at once on the 256 CUs: b = 512 takes a CU alone
+  // (8 waves of up to 256 registers), b = 256 is limited to two per CU by
+  // registers (8 waves of up to 128 VGPRs), b = 128 to four (registers and
+  // LDS), b = 64 to nine by LDS (eight used). Every workgroup streams the
+  // same number of tokens, and one more than fits would cost a whole second
+  // round: floor(resident / (blocks x nh)) token runs per block.
+  const int64_t resident = 256 * (b == 512 ? 1 : (b == 256 ? 2 : (b == 128 ? 4 : 8)));
+  int64_t wpb = std::max<int64_t>(1, resident / (static_cast<int64_t>(nblk) * nh));
   int64_t tpw = (T + wpb - 1) / wpb;
   tpw = (tpw + TT - 1) / TT * TT;
   wpb = (T + tpw - 1) / tpw;
-  const dim3 grid(static_cast<unsigned>(nblk * wpb));
-  const int itpw = static_cast<int>(tpw), iwpb = static_cast<int>(wpb);
+  const int64_t npairs = nblk * wpb;
+  const int itpw = static_cast<int>(tpw), iwpb = static_cast<int>(wpb), inp = static_cast<int>(npairs);
   switch (b) {
     case 64:
-      hipLaunchKernelGGL(k_block_apply<64>, grid, dim3(128), 0, s, in, out, ld, plane, scale, T, dim, itpw, iwpb);
+      hipLaunchKernelGGL(k_block_apply<64>, dim3(static_cast<unsigned>(npairs)), dim3(128), 0, s, in, out, ld, plane,
+                         scale, T, dim, itpw, iwpb, inp);
       break;
     case 128:
-      hipLaunchKernelGGL(k_block_apply<128>, grid, dim3(256), 0, s, in, out, ld, plane, scale, T, dim, itpw, iwpb);
+      hipLaunchKernelGGL(k_block_apply<128>, dim3(static_cast<unsigned>(npairs)), dim3(256), 0, s, in, out, ld, plane,
+                         scale, T, dim, itpw, iwpb, inp);
+      break;
+    case 256:
+      hipLaunchKernelGGL(k_block_apply<256>, dim3(static_cast<unsigned>(npairs)), dim3(512), 0, s, in, out, ld, plane,
+                         scale, T, dim, itpw, iwpb, inp);
       break;
     default:
-      hipLaunchKernelGGL(k_block_apply<256>, grid, dim3(512), 0, s, in, out, ld, plane, scale, T, dim, itpw, iwpb);
+      // both halves of every pair, in runs of 16 workgroups (8 pairs each)
+      hipLaunchKernelGGL(k_block_apply<512>, dim3(static_cast<unsigned>((npairs + 7) / 8 * 16)), dim3(512), 0, s, in,
+                         out, ld, plane, scale, T, dim, itpw, iwpb, inp);
       break;
   }
   return true;

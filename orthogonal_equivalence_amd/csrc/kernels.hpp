@@ -75,7 +75,7 @@ void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16
 // plane[j][c][k]) * scale[j*b + c] (scale optional), for the ceil(dim/b)
 // blocks of a row of width dim (row stride ld). plane holds b x b bfloat16
 // blocks, zero outside a short last block. Returns false unless b is 64,
-// 128 or 256.
+// 128, 256 or 512.
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
                       int64_t T, int64_t dim, int b, hipStream_t stream);
 

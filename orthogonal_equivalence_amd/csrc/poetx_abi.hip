@@ -376,7 +376,7 @@ const void* plane(const poetx_layer* L, const void* g, const Side& s, int p) {
 // (plane 1 gives in G, plane 0 gives in G^T), optional per-column scale.
 bool block_apply(const poetx_layer* L, const Side& s, int64_t T, const void* in, void* out, const void* gbuf,
                  int p, const float* colscale, hipStream_t st) {
-  if (is_bf16(L) && (s.b == 64 || s.b == 128 || s.b == 256))
+  if (is_bf16(L) && (s.b == 64 || s.b == 128 || s.b == 256 || s.b == 512))
     return block_apply_bf16(static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), s.dim,
                             static_cast<const uint16_t*>(plane(L, gbuf, s, p)), colscale, T, s.dim, s.b, st);
   GemmDesc d;

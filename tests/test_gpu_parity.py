@@ -110,6 +110,9 @@ SMALL = [
     _cfg("bf16_b1024", 200, 2048, 1024, 1024, 1024, "bf16", "bf16", 28),
     # b = 512 with a short last block on R (1280 = 2*512 + 256)
     _cfg("bf16_b512_ragged", 260, 1280, 1024, 512, 512, "bf16", "bf16", 29),
+    # b = 512 with a last P block shorter than half a block (1672 = 3*512 + 136)
+    # and a ragged token count
+    _cfg("bf16_b512_ragged_p", 97, 1024, 1672, 512, 512, "bf16", "bf16", 35),
     # b = 128 with short last blocks on both sides (704 = 5*128 + 64, 392 = 3*128 + 8)
     _cfg("bf16_b128_ragged", 150, 704, 392, 128, 128, "bf16", "bf16", 32),
     # shallowest dense products: K = 64 forward (one K step), K = 128 backward (two)
