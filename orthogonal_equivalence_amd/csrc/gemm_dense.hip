@@ -17,6 +17,15 @@
 //    LDS serves 8 or 16 lanes of a 16-byte read per cycle.
 //  * Output tiles are ordered so that each XCD works on one contiguous band
 //    of tiles (shared A/B panels stay in that XCD's L2).
+//  * When the tiles do not fill a whole number of rounds over the 256 CUs,
+//    the tiles of the last, partial round are split along K into k parts
+//    (k * tail <= 256), so that round runs on (nearly) every CU. Every part
+//    writes its fp32 partial tile, row-major, to the workspace; a second
+//    kernel adds the k partials of each tile in part order, applies the
+//    column scale and stores bfloat16. The kernel boundary makes the
+//    partials visible across XCDs; a hand-off inside the kernel would need
+//    device-scope fences, which write back and invalidate a whole XCD's L2
+//    under every other workgroup streaming from it.
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -98,7 +107,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n) {
+// Tiles [0, full) run whole; tile full + u / k is computed as part u % k
+// (of k) by workgroup full + u. part: the tail tiles' partials,
+// [tail][k][BM][BN] floats.
+struct DenseSplit {
+  float* part;
+  int full;
+  int k;
+};
+
+// Output tile (tm, tn) of tile index pid: groups of GM tile rows, walked
+// column by column, so that neighbouring pids share A or B panels.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int group = GM * tiles_n;
+  const int first_m = (pid / group) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  tm = first_m + (pid % group) % gsz;
+  tn = (pid % group) / gsz;
+}
+
+__global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n, DenseSplit sp) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -106,18 +135,25 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
 
-  constexpr int GM = 8;
-  const int pid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
-  const int group = GM * tiles_n;
-  const int first_m = (pid / group) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (pid % group) % gsz;
-  const int tn = (pid % group) / gsz;
+  const int bid = static_cast<int>(blockIdx.x);
+  int pid, part = 0;
+  if (bid < sp.full) {
+    pid = xcd_remap(bid, sp.full);
+  } else {
+    pid = sp.full + (bid - sp.full) / sp.k;
+    part = (bid - sp.full) % sp.k;
+  }
+  int tm, tn;
+  tile_coords(pid, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const bf16_t* A = static_cast<const bf16_t*>(d.A);
   const bf16_t* B = static_cast<const bf16_t*>(d.B);
-  const int nk = d.K / BK;
+  // this workgroup's K steps: [kb, kb + nk) (all of them for a whole tile)
+  const int nk_all = d.K / BK;
+  const int nparts = bid < sp.full ? 1 : sp.k;
+  const int kb = part * nk_all / nparts;
+  const int nk = (part + 1) * nk_all / nparts - kb;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -141,8 +177,8 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p) {
     if (p < nk) {
-      load_tile(A, d.lda, m0, d.M, p * BK, smem + p * kStageBytes, wave, lane);
-      load_tile(B, d.ldb, n0, d.N, p * BK, smem + p * kStageBytes + kTileBytes, wave, lane);
+      load_tile(A, d.lda, m0, d.M, (kb + p) * BK, smem + p * kStageBytes, wave, lane);
+      load_tile(B, d.ldb, n0, d.N, (kb + p) * BK, smem + p * kStageBytes + kTileBytes, wave, lane);
     }
   }
 
@@ -158,7 +194,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
     __syncthreads();
     const int pf = it + NSTAGE - 1;
     char* nxt = smem + (pf % NSTAGE) * kStageBytes;
-    const int kpf = min(pf, nk - 1) * BK;
+    const int kpf = (kb + min(pf, nk - 1)) * BK;
     const char* st = smem + (it % NSTAGE) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -189,9 +225,14 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   // the last iteration's re-load of the idle stage must land before the
   // slabs reuse that LDS
   wait_vmcnt<0>();
+
   // epilogue through per-wave LDS slabs (32 rows x 64 columns), 16-byte stores
+  // (a part of a split tile stores its fp32 rows to its partial tile instead)
   bf16_t* C = static_cast<bf16_t*>(d.C);
   const float* S = d.scale;
+  float* P = bid >= sp.full
+                 ? sp.part + (static_cast<int64_t>(pid - sp.full) * sp.k + part) * (BM * BN)
+                 : nullptr;
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * kSlabStride;
   constexpr int kChunksPerRow = WTN / 8;
   constexpr int kChunksPerLane = 32 * kChunksPerRow / 64;
@@ -210,7 +251,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
       const int row = ch / kChunksPerRow, col = (ch % kChunksPerRow) * 8;
       const int m = m0 + wm * WTM + i * 32 + row;
       const int n = n0 + wn * WTN + col;
-      if (m < d.M && n < d.N) {
+      if (P) {
+        float* dst = P + (wm * WTM + i * 32 + row) * BN + wn * WTN + col;
+        *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(slab + row * kSlabStride + col);
+        *reinterpret_cast<float4*>(dst + 4) = *reinterpret_cast<const float4*>(slab + row * kSlabStride + col + 4);
+      } else if (m < d.M && n < d.N) {
         const float4 p0 = *reinterpret_cast<const float4*>(slab + row * kSlabStride + col);
         const float4 p1 = *reinterpret_cast<const float4*>(slab + row * kSlabStride + col + 4);
         float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -228,13 +273,80 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   }
 }
 
+// Sum of the k partial tiles of each split tile, in part order, times the
+// column scale, to bfloat16: one thread per 8 consecutive columns of a row.
+__global__ void __launch_bounds__(256) k_dense_split_sum(const GemmDesc d, int tiles_m, int tiles_n,
+                                                         DenseSplit sp) {
+  const int slot = blockIdx.x / (BM * BN / 8 / 256);
+  const int e = (blockIdx.x % (BM * BN / 8 / 256)) * 256 + threadIdx.x;  // chunk of 8 in the tile
+  const int row = e / (BN / 8), col = (e % (BN / 8)) * 8;
+  int tm, tn;
+  tile_coords(sp.full + slot, tiles_m, tiles_n, tm, tn);
+  const int m = tm * BM + row, n = tn * BN + col;
+  if (m >= d.M || n >= d.N) return;
+  const float* src = sp.part + static_cast<int64_t>(slot) * sp.k * (BM * BN) + row * BN + col;
+  float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+  for (int p = 1; p < sp.k; ++p) {
+    const float4 u = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(p) * (BM * BN));
+    const float4 w = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(p) * (BM * BN) + 4);
+    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    b.x += w.x; b.y += w.y; b.z += w.z; b.w += w.w;
+  }
+  float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if (d.scale) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= d.scale[n + i];
+  }
+  bf16_t* C = static_cast<bf16_t*>(d.C);
+  *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * d.ldc + n) =
+      make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
 }  // namespace
 
-bool gemm_dense_bf16(const GemmDesc& d, hipStream_t s) {
+namespace {
+
+constexpr int kCUs = 256;
+
+// Tiles run whole and the split of the last, partial round: k parts per
+// tail tile with k * tail <= 256 CUs and at least 8 K steps per part.
+struct SplitPlan {
+  int tiles, full, k;
+};
+
+SplitPlan split_plan(int M, int N, int K) {
+  SplitPlan p;
+  p.tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int tail = p.tiles % kCUs;
+  const int nk = K / BK;
+  p.k = 1;
+  while (tail > 0 && p.k < 4 && 2 * p.k * tail <= kCUs && nk / (2 * p.k) >= 8) p.k *= 2;
+  p.full = p.k > 1 ? p.tiles - tail : p.tiles;
+  return p;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t gemm_dense_split_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const SplitPlan p = split_plan(M, N, K);
+  if (p.k == 1) return 0;
+  return align256(static_cast<size_t>(p.tiles - p.full) * p.k * BM * BN * sizeof(float));
+}
+
+bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s) {
   if (d.M <= 0 || d.N <= 0) return true;
   if (d.K % 64 != 0 || d.K <= 0 || d.N % 8 != 0) return false;
   const int tm = (d.M + BM - 1) / BM, tn = (d.N + BN - 1) / BN;
-  hipLaunchKernelGGL(k_gemm_dense, dim3(tm * tn), dim3(NT), 0, s, d, tm, tn);
+  SplitPlan p = split_plan(d.M, d.N, d.K);
+  if (!split_ws) p = SplitPlan{p.tiles, p.tiles, 1};
+  const DenseSplit sp{static_cast<float*>(split_ws), p.full, p.k};
+  const int tail = p.tiles - p.full;
+  hipLaunchKernelGGL(k_gemm_dense, dim3(p.full + tail * p.k), dim3(NT), 0, s, d, tm, tn, sp);
+  if (tail > 0)
+    hipLaunchKernelGGL(k_dense_split_sum, dim3(tail * (BM * BN / 8 / 256)), dim3(256), 0, s, d, tm, tn, sp);
   return true;
 }
 

@@ -190,12 +190,17 @@ CnpBwdWs plan_cnp_bwd(const poetx_layer* L, int64_t bb, Carve& c) {
 struct FwdWs {
   void* buf;
   int32_t* inv_p;
+  void* split;  // the dense product's split of a partial last round (or null)
 };
+
+size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K);
 
 FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
   FwdWs w;
   w.buf = c.take<char>(T * std::max(L->m, L->n) * act_size(L));
   w.inv_p = c.take<int32_t>(L->n);
+  const size_t sb = dense_split_bytes(L, T, L->n, L->m);
+  w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
   return w;
 }
 
@@ -206,6 +211,7 @@ struct BwdWs {
   float *part_r, *part_p;
   float *Us, *Uk;     // symmetric / skew parts of dG (side R) and dH (side P)
   uint16_t *Ush, *Ukh;
+  void* split;        // the dense product's split of a partial last round (or null)
   size_t cnp_off;     // the CNP adjoint scratch starts here
 };
 
@@ -230,6 +236,8 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.Uk = c.take<float>(all);
   w.Ush = c.take<uint16_t>(all);
   w.Ukh = c.take<uint16_t>(all);
+  const size_t sb = dense_split_bytes(L, T, L->m, L->n);
+  w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
   w.cnp_off = c.off;
   Carve m(nullptr);
   plan_cnp_bwd(L, cnp_batch_elems(L), m);
@@ -362,8 +370,18 @@ bool gemm(const poetx_layer* L, const GemmDesc& d, int am, int bm, int ct, hipSt
 
 // The dense W0 product: the specialised kernel when its shape constraints
 // hold, else the general engine.
-bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, hipStream_t st) {
-  if (is_bf16(L) && !i8 && d.K % 64 == 0 && d.N % 8 == 0) return gemm_dense_bf16(d, st);
+bool dense_kernel_applies(const poetx_layer* L, int N, int K) {
+  return is_bf16(L) && L->w_dtype != POETX_I8 && K % 64 == 0 && N % 8 == 0;
+}
+
+// Workspace of the dense kernel's split of a partial last round of tiles.
+size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K) {
+  if (!dense_kernel_applies(L, static_cast<int>(N), static_cast<int>(K))) return 0;
+  return gemm_dense_split_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+}
+
+bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, void* split_ws, hipStream_t st) {
+  if (!i8 && dense_kernel_applies(L, d.N, d.K)) return gemm_dense_bf16(d, split_ws, st);
   return gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
 }
 
@@ -649,7 +667,7 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   d.K = static_cast<int>(L->m);
   {
     ProfScope p(recompute ? "recompute_gemm_dense" : "gemm_dense_fwd", stream);
-    ok = ok && dense_product(L, d, i8, stream);
+    ok = ok && dense_product(L, d, i8, w.split, stream);
   }
   if (!z) return ok;
   {
@@ -711,7 +729,7 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   d.K = static_cast<int>(L->n);
   {
     ProfScope p("gemm_dense_bwd", stream);
-    ok = ok && dense_product(L, d, i8, stream);
+    ok = ok && dense_product(L, d, i8, w.split, stream);
   }
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {

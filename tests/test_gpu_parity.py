@@ -119,6 +119,9 @@ SMALL = [
     _cfg("bf16_k64", 300, 64, 128, 32, 64, "bf16", "bf16", 33),
     # ragged token count and output width across several 256 x 256 output tiles
     _cfg("bf16_ragged_tiles", 1100, 320, 1800, 64, 64, "bf16", "bf16", 34),
+    # fewer output tiles than CUs and K >= 2048: both dense products split
+    # every tile into four K parts summed by the last part to finish
+    _cfg("bf16_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 36),
 ]
 
 
@@ -309,14 +312,21 @@ def test_permutations_bit_exact(act, b, T):
 # determinism, empty input, token-shard linearity
 # ---------------------------------------------------------------------------
 
-def test_backward_is_deterministic():
-    cfg = _cfg("determinism", 1024, 512, 768, 128, 128, "bf16", "bf16", 28)
+@pytest.mark.parametrize("cfg", [
+    _cfg("determinism", 1024, 512, 768, 128, 128, "bf16", "bf16", 28),
+    # dense products split along K (the order in which parts finish varies)
+    _cfg("determinism_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 36),
+], ids=lambda c: c.name)
+def test_layer_is_deterministic(cfg):
     _, A, out1, dl = _run(cfg)
-    dq_r, dq_p, dx = dl.backward(to_device(A["dZ_raw"], cfg.act))
-    torch.cuda.synchronize()
-    assert np.array_equal(to_host_f64(dq_r), out1["dq_r"])
-    assert np.array_equal(to_host_f64(dq_p), out1["dq_p"])
-    assert np.array_equal(to_host_f64(dx), out1["dx"])
+    for _ in range(2):
+        z = dl.forward(to_device(A["X_raw"], cfg.act))
+        dq_r, dq_p, dx = dl.backward(to_device(A["dZ_raw"], cfg.act))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_f64(z), out1["z"])
+        assert np.array_equal(to_host_f64(dq_r), out1["dq_r"])
+        assert np.array_equal(to_host_f64(dq_p), out1["dq_p"])
+        assert np.array_equal(to_host_f64(dx), out1["dx"])
 
 
 def test_zero_tokens():
