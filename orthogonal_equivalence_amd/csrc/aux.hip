@@ -294,6 +294,26 @@ __global__ void k_dequant_i8_cols(const int8_t* __restrict__ wq, const float* __
   o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// bfloat16 copy of int8 weight codes: every code (|c| <= 127) is exact in
+// bfloat16. One thread per 8 codes: an 8-byte load, a 16-byte store.
+__global__ void k_i8_to_bf16(const int8_t* __restrict__ in, uint16_t* __restrict__ out, int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n8) return;
+  const uint2 q = reinterpret_cast<const uint2*>(in)[i];
+  const uint32_t w[2] = {q.x, q.y};
+  uint32_t o[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float a = static_cast<float>(static_cast<int8_t>((w[h] >> (16 * e)) & 0xff));
+      const float b = static_cast<float>(static_cast<int8_t>((w[h] >> (16 * e + 8)) & 0xff));
+      o[2 * h + e] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    }
+  }
+  reinterpret_cast<uint4*>(out)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ void k_bf16_to_f32(const bf16_t* __restrict__ in, float* __restrict__ out, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (i < n) out[i] = bf16_to_f32(in[i]);
@@ -746,6 +766,13 @@ bool dequant_i8_cols(const int8_t* wq, const float* scale, const int32_t* cmap, 
   if (cols % 8 != 0) return false;
   hipLaunchKernelGGL(k_dequant_i8_cols, dim3(grid1(rows * (cols / 8))), dim3(kThreads), 0, s, wq, scale, cmap, out,
                      rows, cols);
+  return true;
+}
+
+bool i8_to_bf16(const int8_t* in, uint16_t* out, int64_t n, hipStream_t s) {
+  if (n % 8 != 0) return false;
+  const int64_t n8 = n / 8;
+  if (n8 > 0) hipLaunchKernelGGL(k_i8_to_bf16, dim3(grid1(n8)), dim3(kThreads), 0, s, in, out, n8);
   return true;
 }
 

@@ -33,6 +33,8 @@ bool dequant_i8_cols(const int8_t* wq, const float* scale, const int32_t* cmap, 
                      int64_t cols, hipStream_t stream);
 // out[i] = in[i] widened from bfloat16;
 void bf16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t stream);
+// out[i] = the int8 code in[i] as bfloat16 (exact), n % 8 == 0 (else false);
+bool i8_to_bf16(const int8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
 // and the storage again: scale[c] = max_r |w[r][c]| / 127 (1 for a zero
 // column), wq = clamp(rint(w / scale), -127, 127); amax: cols words of
 // scratch (cols % 8 == 0).

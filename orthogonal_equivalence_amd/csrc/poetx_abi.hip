@@ -191,9 +191,11 @@ struct FwdWs {
   void* buf;
   int32_t* inv_p;
   void* split;  // the dense product's split of a partial last round (or null)
+  void* wdeq;   // int8 weight: bfloat16 copy of Wp^T's codes (or null)
 };
 
 size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K);
+bool i8_staging(const poetx_layer* L);
 
 FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
   FwdWs w;
@@ -201,6 +203,7 @@ FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.inv_p = c.take<int32_t>(L->n);
   const size_t sb = dense_split_bytes(L, T, L->n, L->m);
   w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
+  w.wdeq = i8_staging(L) ? c.take<uint16_t>(L->m * L->n) : nullptr;
   return w;
 }
 
@@ -212,6 +215,7 @@ struct BwdWs {
   float *Us, *Uk;     // symmetric / skew parts of dG (side R) and dH (side P)
   uint16_t *Ush, *Ukh;
   void* split;        // the dense product's split of a partial last round (or null)
+  void* wdeq;         // int8 weight: bfloat16 copy of Wp's codes (or null)
   size_t cnp_off;     // the CNP adjoint scratch starts here
 };
 
@@ -238,6 +242,7 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.Ukh = c.take<uint16_t>(all);
   const size_t sb = dense_split_bytes(L, T, L->m, L->n);
   w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
+  w.wdeq = i8_staging(L) ? c.take<uint16_t>(L->m * L->n) : nullptr;
   w.cnp_off = c.off;
   Carve m(nullptr);
   plan_cnp_bwd(L, cnp_batch_elems(L), m);
@@ -369,9 +374,20 @@ bool gemm(const poetx_layer* L, const GemmDesc& d, int am, int bm, int ct, hipSt
 }
 
 // The dense W0 product: the specialised kernel when its shape constraints
-// hold, else the general engine.
+// hold, else the general engine. An int8 weight goes through it too, as a
+// bfloat16 copy of its codes made just before the product (see i8_staging).
 bool dense_kernel_applies(const poetx_layer* L, int N, int K) {
-  return is_bf16(L) && L->w_dtype != POETX_I8 && K % 64 == 0 && N % 8 == 0;
+  return is_bf16(L) && K % 64 == 0 && N % 8 == 0;
+}
+
+// The quantised variant stores the base weight as int8 and dequantises it at
+// run time (section "POET-XQ"): the codes are copied to bfloat16 (exact)
+// into the workspace right before each dense product, whose epilogue (or the
+// preceding apply, in the backward) applies the column scales. The stored
+// weight stays int8; the copy is transient scratch.
+bool i8_staging(const poetx_layer* L) {
+  return L->w_dtype == POETX_I8 && dense_kernel_applies(L, static_cast<int>(L->n), static_cast<int>(L->m)) &&
+         dense_kernel_applies(L, static_cast<int>(L->m), static_cast<int>(L->n));
 }
 
 // Workspace of the dense kernel's split of a partial last round of tiles.
@@ -665,9 +681,14 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   d.M = static_cast<int>(T);
   d.N = static_cast<int>(L->n);
   d.K = static_cast<int>(L->m);
+  if (w.wdeq) {
+    ProfScope p(recompute ? "recompute_dequant_w" : "dequant_w_fwd", stream);
+    ok = ok && i8_to_bf16(static_cast<const int8_t*>(wpt), static_cast<uint16_t*>(w.wdeq), L->m * L->n, stream);
+    d.B = w.wdeq;
+  }
   {
     ProfScope p(recompute ? "recompute_gemm_dense" : "gemm_dense_fwd", stream);
-    ok = ok && dense_product(L, d, i8, w.split, stream);
+    ok = ok && dense_product(L, d, i8 && !w.wdeq, w.split, stream);
   }
   if (!z) return ok;
   {
@@ -727,9 +748,14 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   d.M = static_cast<int>(T);
   d.N = static_cast<int>(L->m);
   d.K = static_cast<int>(L->n);
+  if (w.wdeq) {
+    ProfScope p("dequant_w_bwd", stream);
+    ok = ok && i8_to_bf16(static_cast<const int8_t*>(d.B), static_cast<uint16_t*>(w.wdeq), L->m * L->n, stream);
+    d.B = w.wdeq;
+  }
   {
     ProfScope p("gemm_dense_bwd", stream);
-    ok = ok && dense_product(L, d, i8, w.split, stream);
+    ok = ok && dense_product(L, d, i8 && !w.wdeq, w.split, stream);
   }
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {
