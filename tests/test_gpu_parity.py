@@ -122,6 +122,9 @@ SMALL = [
     # fewer output tiles than CUs and K >= 2048: both dense products split
     # every tile into four K parts summed by the last part to finish
     _cfg("bf16_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 36),
+    # the same with an int8 weight: codes copied to bfloat16, column scales in
+    # the split sum's epilogue
+    _cfg("xq_split_k", 300, 2048, 2304, 256, 256, "bf16", "i8", 39),
 ]
 
 
