@@ -221,7 +221,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs the layer on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
               "the multi-GPU path (data parallel over token shards with one all-reduce of the packed "
-              "gradients) is not part of this build", file=sys.stderr)
+              "gradients) is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch

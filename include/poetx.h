@@ -58,7 +58,7 @@ extern "C" {
 enum {
   POETX_OK = 0,
   POETX_EINVAL = 1,        /* bad pointer, shape, dtype or size */
-  POETX_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+  POETX_EUNSUPPORTED = 2,  /* valid request the library does not implement */
   POETX_EHIP = 3,          /* a HIP launch failed */
   POETX_EWORKSPACE = 4     /* ws_bytes smaller than poetx_workspace_bytes() */
 };

@@ -348,8 +348,8 @@ def merge(W0, q_r, q_p, perm_r, perm_p, b_r, b_p):
 
 
 def requantize_int8_per_col(W):
-    """Per-output-column int8 storage of a float weight [XQ], as this build
-    reads the page's quantized base weight: scale[c] = max_r |W[r, c]| / 127,
+    """Per-output-column int8 storage of a float weight [XQ], in the reading
+    taken of the page's quantized base weight: scale[c] = max_r |W[r, c]| / 127,
     code = clip(rint(W / scale), -127, 127) with rint rounding half to even,
     and a zero column stored with scale 1. The page fixes no precision for
     the decision, so it is taken in float32, the kernels' precision."""

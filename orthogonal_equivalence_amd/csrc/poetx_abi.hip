@@ -808,7 +808,7 @@ const char* poetx_strerror(int status) {
   switch (status) {
     case POETX_OK: return "ok";
     case POETX_EINVAL: return "invalid argument (pointer, alignment, shape, dtype or size)";
-    case POETX_EUNSUPPORTED: return "valid request not supported by this build";
+    case POETX_EUNSUPPORTED: return "valid request the library does not implement";
     case POETX_EHIP: return "HIP kernel launch failed";
     case POETX_EWORKSPACE: return "workspace smaller than poetx_workspace_bytes()";
     default: return "unknown status";
