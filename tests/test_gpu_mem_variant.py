@@ -44,6 +44,11 @@ CASES = [
     _cfg("mem_xq", 300, 512, 768, 128, 128, "bf16", "i8", 43),
     # the Llama-8B MLP up-projection itself
     synth.CONFIGS["llama8b_mlp_up"],
+    # fewer output tiles than CUs and K >= 2048: both dense products split
+    # along K, their partials in the workspace the recompute shares
+    _cfg("mem_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 45),
+    # the same with an int8 weight (its bfloat16 code copy is workspace too)
+    _cfg("mem_xq_split_k", 300, 2048, 2304, 256, 256, "bf16", "i8", 46),
 ]
 
 
