@@ -125,6 +125,10 @@ SMALL = [
     # the same with an int8 weight: codes copied to bfloat16, column scales in
     # the split sum's epilogue
     _cfg("xq_split_k", 300, 2048, 2304, 256, 256, "bf16", "i8", 39),
+    # one block per side: R's block size exceeds m (a single short block of
+    # 64), P is exactly one block
+    _cfg("f32_single_block", 50, 64, 128, 128, 128, "f32", "f32", 47),
+    _cfg("bf16_single_block", 130, 192, 256, 256, 256, "bf16", "bf16", 48),
 ]
 
 
