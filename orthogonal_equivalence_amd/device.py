@@ -161,6 +161,30 @@ class DeviceLayer:
         px.poetx_sample_perm(self.m, seed, 2 * tag, draw, self.perm_r, self.ws, None, stream)
         px.poetx_sample_perm(self.n, seed, 2 * tag + 1, draw, self.perm_p, self.ws, None, stream)
 
+    def merge_cycle(self, seed, tag, draw, stream=None):
+        """W0 <- R W0 P with q <- 0, draw ``draw`` of both permutations, and
+        the permuted-frame weight rebuilt for them. The draws do not depend on
+        the merge, so they run on a second stream (default priority) into
+        spare permutation buffers, with a small workspace of their own, while
+        the merge runs; the stream joins them before the rebuild, and the
+        buffers swap."""
+        main = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if not hasattr(self, "_side"):
+            self._side = torch.cuda.Stream(device=self.device)
+            self._next_r = torch.empty_like(self.perm_r)
+            self._next_p = torch.empty_like(self.perm_p)
+            need = px.poetx_workspace_bytes(self.L, 0, px.POETX_OP_SAMPLE_PERM)
+            self._draw_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+        # the spare buffers' earlier readers are on the main stream
+        self._side.wait_stream(main)
+        px.poetx_sample_perm(self.m, seed, 2 * tag, draw, self._next_r, self._draw_ws, None, self._side)
+        px.poetx_sample_perm(self.n, seed, 2 * tag + 1, draw, self._next_p, self._draw_ws, None, self._side)
+        self.merge(main)
+        main.wait_stream(self._side)
+        self.perm_r, self._next_r = self._next_r, self.perm_r
+        self.perm_p, self._next_p = self._next_p, self.perm_p
+        self.prepare(main)
+
     def merge_if_needed(self, step, interval, seed, tag, stream=None):
         """Called after optimizer step ``step`` (counted from 0). After every
         ``interval``-th update: CNP blocks of the current q, W0 <- R W0 P with
@@ -170,8 +194,6 @@ class DeviceLayer:
         if (step + 1) % interval:
             return False
         self.cnp_build(stream)
-        self.merge(stream)
-        self.resample(seed, tag, (step + 1) // interval, stream)
-        self.prepare(stream)
+        self.merge_cycle(seed, tag, (step + 1) // interval, stream)
         self.cnp_build(stream)
         return True
