@@ -46,11 +46,21 @@ def cpu_baseline(cfg, budget_s=30.0):
     import numpy as np
     import oracle as O
     from orthogonal_equivalence_amd import synth
+    blas = "unknown"
     try:
         import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                                 for i in info if i.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover - informational only
         threads = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:  # pragma: no cover - informational only
+        pass
     L = synth.make_layer(cfg, 0)
     W0 = O.dequantize(L["W0_raw"], L["w_scale"]) if cfg.weight == "i8" else L["W0"].astype(np.float64)
     args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
@@ -87,7 +97,8 @@ def cpu_baseline(cfg, budget_s=30.0):
         sample = (f"float64 oracle fwd+bwd on {t_small} and {t_big} tokens of the {cfg.name} workload"
                   f"{' plus one full merge' if cfg.merge else ''}, extrapolated linearly in T to "
                   f"{cfg.T} tokens ({step:.1f} s per step; {sum(times.values()) + t_merge:.1f} s measured)")
-    return {"value": cfg.T / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "sample": sample}
+    return {"value": cfg.T / step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "sample": sample,
+            "cpu_model": cpu_model, "blas": blas}
 
 
 GEMM_SOURCES = ("gemm_dense.hip", "gemm.hpp", "common.hpp")
