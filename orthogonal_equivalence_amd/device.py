@@ -3,7 +3,9 @@
 Holds the torch device buffers one layer needs (base weight, its permuted
 frame, packed parameters, permutations, CNP block buffers, saved activations
 and a workspace sized by poetx_workspace_bytes) and calls the ABI entry points
-in order. It allocates and marshals; all arithmetic runs in libpoetx.so.
+in order, including the merge schedule a training loop runs (merge, new
+permutation draws, weight rebuild). It allocates, marshals and orders work on
+streams; all arithmetic runs in libpoetx.so.
 """
 
 import numpy as np
@@ -60,6 +62,9 @@ class DeviceLayer:
         self.T_max = 0
         self.saved = None
         self.ws = torch.empty(0, dtype=u8, device=dev)
+        # merge cycle: second stream, spare permutations and the draws' own workspace
+        self._side = None
+        self._next_r = self._next_p = self._draw_ws = None
         self.reserve(T_max)
 
     # -- buffers --------------------------------------------------------------
@@ -169,7 +174,7 @@ class DeviceLayer:
         the merge runs; the stream joins them before the rebuild, and the
         buffers swap."""
         main = stream if stream is not None else torch.cuda.current_stream(self.device)
-        if not hasattr(self, "_side"):
+        if self._side is None:
             self._side = torch.cuda.Stream(device=self.device)
             self._next_r = torch.empty_like(self.perm_r)
             self._next_p = torch.empty_like(self.perm_p)
