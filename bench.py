@@ -178,8 +178,9 @@ def algorithmic_work(cfg):
 
 
 def kernel_roofline(cfg, per):
-    """Per profiled step: time, algorithmic rates and the fraction of the
-    binding roof, t_roof / t with t_roof = max(flops / MFMA peak, bytes / HBM peak)."""
+    """Per profiled step: time, algorithmic rates, the fraction of the binding
+    roof, t_roof / t with t_roof = max(flops / MFMA peak, bytes / HBM peak), and
+    the fractions of the HBM and of the MFMA peak separately."""
     peak_f = (PEAK_BF16_TFLOPS if cfg.act == "bf16" else PEAK_F32_TFLOPS) * 1e12
     peak_b = PEAK_HBM_GBS * 1e9
     work = algorithmic_work(cfg)
@@ -192,7 +193,8 @@ def kernel_roofline(cfg, per):
         t_roof = max(flops / peak_f, nbytes / peak_b)
         out[name] = {"ms": round(t * 1e3, 4), "bound": "mfma" if flops / peak_f > nbytes / peak_b else "hbm",
                      "GB/s": round(nbytes / t / 1e9, 1), "TFLOP/s": round(flops / t / 1e12, 1),
-                     "frac": round(t_roof / t, 4)}
+                     "frac": round(t_roof / t, 4), "frac_hbm": round(nbytes / t / peak_b, 4),
+                     "frac_mfma": round(flops / t / peak_f, 4)}
     return out
 
 
