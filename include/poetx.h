@@ -150,7 +150,9 @@ POETX_API int poetx_weight_prepare(const poetx_layer* L, const void* w0, const f
  *   wpt: permuted-frame transposed weight from poetx_weight_prepare;
  *   wscale_p: its permuted scales (I8 only, else ignored).
  *   saved: poetx_saved_bytes(L, T) bytes, overwritten with X1 and Y1.
- * T == 0 launches nothing. */
+ * An int8 weight is dequantised at run time (section "POET-XQ"): its codes are
+ * copied to bfloat16 (exact) in the workspace and the dense product applies
+ * the column scales in its epilogue. T == 0 launches nothing. */
 POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
                   const int32_t* perm_r, const int32_t* perm_p,
                   const void* g_r, const void* g_p,
@@ -167,7 +169,9 @@ POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
  * accumulated; T == 0 writes zero gradients. When the weight is not int8 and
  * m < T, the P-side product dY1 = dY2 H^T is not formed: the dense product
  * takes dY2 and the weight Wp H (built in the workspace), which is the same
- * dX2 = dY2 H^T Wp^T with fewer bytes moved. */
+ * dX2 = dY2 H^T Wp^T with fewer bytes moved. For an int8 weight, dY1 takes the
+ * column scales and the dense product reads a bfloat16 copy of Wp's codes made
+ * in the workspace. */
 POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const void* dz,
                    const int32_t* perm_r, const int32_t* perm_p,
                    const float* q_r, const float* q_p,
