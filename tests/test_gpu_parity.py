@@ -129,6 +129,10 @@ SMALL = [
     # 64), P is exactly one block
     _cfg("f32_single_block", 50, 64, 128, 128, 128, "f32", "f32", 47),
     _cfg("bf16_single_block", 130, 192, 256, 256, 256, "bf16", "bf16", 48),
+    # block sizes that are multiples of 8 but not powers of two, with short
+    # last blocks (general engine for applies, token sums and CNP products)
+    _cfg("bf16_b96_b40", 210, 480, 600, 96, 40, "bf16", "bf16", 49),
+    _cfg("f32_b24_b56", 70, 120, 200, 24, 56, "f32", "f32", 53),
 ]
 
 
