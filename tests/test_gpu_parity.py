@@ -133,6 +133,9 @@ SMALL = [
     # last blocks (general engine for applies, token sums and CNP products)
     _cfg("bf16_b96_b40", 210, 480, 600, 96, 40, "bf16", "bf16", 49),
     _cfg("f32_b24_b56", 70, 120, 200, 24, 56, "f32", "f32", 53),
+    # the smallest block size the library takes, b = 8
+    _cfg("f32_b8", 40, 48, 64, 8, 8, "f32", "f32", 54),
+    _cfg("bf16_b8", 40, 48, 64, 8, 8, "bf16", "bf16", 55),
 ]
 
 
