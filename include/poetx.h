@@ -31,7 +31,10 @@
  *    F32 activations, POETX_BF16 or POETX_I8 with BF16 activations (I8 = int8
  *    weight with one float scale per output column: W0[r][c] = s[c] * q[r][c],
  *    the quantised-base-weight variant POET-XQ of section "POET-XQ").
- *  - Shapes: m, n, b_r, b_p multiples of 8; 8 <= b <= 1024; T >= 0.
+ *  - Shapes: m, n, b_r, b_p multiples of 8; 8 <= b <= 1024; m, n <= 2^24;
+ *    ceil(m / b_r) + ceil(n / b_p) <= 65535 blocks; 0 <= T <= 2^30 tokens.
+ *    Outside these the entry points return POETX_EINVAL and the size queries
+ *    return 0.
  *  - Permutations must be permutations of [0, dim). Out-of-range entries are
  *    not reported, but every index is clamped, so a bad permutation gives
  *    wrong values, never an access outside the buffers.

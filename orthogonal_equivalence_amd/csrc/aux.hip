@@ -10,6 +10,12 @@ namespace poetx {
 namespace {
 
 constexpr int kThreads = 256;
+// Grid limits kept by every launch here: one-dimensional element-wise grids
+// stop at kMaxGrid1 workgroups (2^28 threads, well inside the 2^32 work-items
+// a dimension holds) and loop over the rest; y and z stop at the 65535 the
+// runtime reports, with a loop where a size could exceed it.
+constexpr int64_t kMaxGrid1 = int64_t(1) << 20;
+constexpr int64_t kMaxGridYZ = 65535;
 #ifndef POETX_GATHER_LDS_KB
 #define POETX_GATHER_LDS_KB 32
 #endif
@@ -194,23 +200,27 @@ __global__ void __launch_bounds__(kThreads)
 k_gather_cols_direct(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
                      T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
                      const int32_t* __restrict__ cidx, int64_t ncols, int64_t nrows) {
-  const int64_t r = blockIdx.y;
-  const int64_t src = rmap_in ? clamp_index(rmap_in[r], nrows) : r;
-  const int64_t dst = rmap_out ? clamp_index(rmap_out[r], nrows) : r;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < ncols;
-       i += static_cast<int64_t>(gridDim.x) * kThreads)
-    out[dst * ld_out + i] = in[src * ld_in + clamp_index(cidx[i], ncols)];
+  for (int64_t r = blockIdx.y; r < nrows; r += gridDim.y) {
+    const int64_t src = rmap_in ? clamp_index(rmap_in[r], nrows) : r;
+    const int64_t dst = rmap_out ? clamp_index(rmap_out[r], nrows) : r;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < ncols;
+         i += static_cast<int64_t>(gridDim.x) * kThreads)
+      out[dst * ld_out + i] = in[src * ld_in + clamp_index(cidx[i], ncols)];
+  }
 }
 
+// i = this thread's first element; the loop steps by the whole grid
+#define POETX_GRID_STRIDE(i, n)                                                          \
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < (n); \
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+
 __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __restrict__ inv, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
+  POETX_GRID_STRIDE(i, n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
 }
 
 __global__ void k_gather_f32(const float* __restrict__ in, const int32_t* __restrict__ idx, float* __restrict__ out,
                              int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n) out[i] = in[clamp_index(idx[i], n)];
+  POETX_GRID_STRIDE(i, n) out[i] = in[clamp_index(idx[i], n)];
 }
 
 // Transpose through a 64 x 64 LDS tile with 16-byte global accesses on both
@@ -223,44 +233,46 @@ __global__ void __launch_bounds__(kThreads) k_transpose(const T* __restrict__ in
   constexpr int V = 16 / sizeof(T);
   constexpr int CPR = 64 / V;  // 16-byte chunks per 64-element row
   __shared__ T tile[64][64 + 1];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const bool full = (r0 + 64 <= rows) && (c0 + 64 <= cols);
-  for (int q = threadIdx.x; q < 64 * CPR; q += kThreads) {
-    const int i = q / CPR, j = (q % CPR) * V;
-    const int64_t r = r0 + i, c = c0 + j;
-    T v[V];
-    if (full) {
-      const uint4 w = *reinterpret_cast<const uint4*>(in + r * cols + c);
-      __builtin_memcpy(v, &w, 16);
-    } else {
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64; r0 < rows; r0 += static_cast<int64_t>(gridDim.y) * 64) {
+    const bool full = (r0 + 64 <= rows) && (c0 + 64 <= cols);
+    for (int q = threadIdx.x; q < 64 * CPR; q += kThreads) {
+      const int i = q / CPR, j = (q % CPR) * V;
+      const int64_t r = r0 + i, c = c0 + j;
+      T v[V];
+      if (full) {
+        const uint4 w = *reinterpret_cast<const uint4*>(in + r * cols + c);
+        __builtin_memcpy(v, &w, 16);
+      } else {
 #pragma unroll
-      for (int e = 0; e < V; ++e) v[e] = (r < rows && c + e < cols) ? in[r * cols + c + e] : T(0);
+        for (int e = 0; e < V; ++e) v[e] = (r < rows && c + e < cols) ? in[r * cols + c + e] : T(0);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) tile[i][j + e] = v[e];
     }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 64 * CPR; q += kThreads) {
+      const int i = q / CPR, j = (q % CPR) * V;  // output row c0 + i, columns r0 + j ..
+      const int64_t c = c0 + i, r = r0 + j;
+      T v[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) tile[i][j + e] = v[e];
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < 64 * CPR; q += kThreads) {
-    const int i = q / CPR, j = (q % CPR) * V;  // output row c0 + i, columns r0 + j ..
-    const int64_t c = c0 + i, r = r0 + j;
-    T v[V];
+      for (int e = 0; e < V; ++e) v[e] = tile[j + e][i];
+      if (full) {
+        uint4 w;
+        __builtin_memcpy(&w, v, 16);
+        *reinterpret_cast<uint4*>(out + c * rows + r) = w;
+      } else {
 #pragma unroll
-    for (int e = 0; e < V; ++e) v[e] = tile[j + e][i];
-    if (full) {
-      uint4 w;
-      __builtin_memcpy(&w, v, 16);
-      *reinterpret_cast<uint4*>(out + c * rows + r) = w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e)
-        if (c < cols && r + e < rows) out[c * rows + r + e] = v[e];
+        for (int e = 0; e < V; ++e)
+          if (c < cols && r + e < rows) out[c * rows + r + e] = v[e];
+      }
     }
+    __syncthreads();  // the next tile row overwrites the tile
   }
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+  POETX_GRID_STRIDE(i, n) p[i] = 0.f;
 }
 
 // ---- int8 base weight around a merge ----------------------------------------
@@ -269,54 +281,53 @@ __global__ void k_fill_zero(float* p, int64_t n) {
 __global__ void k_dequant_i8_cols(const int8_t* __restrict__ wq, const float* __restrict__ scale,
                                   const int32_t* __restrict__ cmap, float* __restrict__ out, int64_t rows,
                                   int64_t cols) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // 8-column group
   const int64_t per_row = cols >> 3;
-  if (g >= rows * per_row) return;
-  const int64_t r = g / per_row, c0 = (g % per_row) * 8;
-  const uint2 q = *reinterpret_cast<const uint2*>(wq + r * cols + c0);
-  const uint32_t w[2] = {q.x, q.y};
-  float sc[8];
-  if (cmap) {
+  POETX_GRID_STRIDE(g, rows * per_row) {  // g: 8-column group
+    const int64_t r = g / per_row, c0 = (g % per_row) * 8;
+    const uint2 q = *reinterpret_cast<const uint2*>(wq + r * cols + c0);
+    const uint32_t w[2] = {q.x, q.y};
+    float sc[8];
+    if (cmap) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = scale[clamp_index(cmap[c0 + e], cols)];
-  } else {
-    const float4 s0 = *reinterpret_cast<const float4*>(scale + c0);
-    const float4 s1 = *reinterpret_cast<const float4*>(scale + c0 + 4);
-    sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
-    sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+      for (int e = 0; e < 8; ++e) sc[e] = scale[clamp_index(cmap[c0 + e], cols)];
+    } else {
+      const float4 s0 = *reinterpret_cast<const float4*>(scale + c0);
+      const float4 s1 = *reinterpret_cast<const float4*>(scale + c0 + 4);
+      sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+      sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = static_cast<float>(static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xffu)) * sc[e];
+    float4* o = reinterpret_cast<float4*>(out + r * cols + c0);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    v[e] = static_cast<float>(static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xffu)) * sc[e];
-  float4* o = reinterpret_cast<float4*>(out + r * cols + c0);
-  o[0] = make_float4(v[0], v[1], v[2], v[3]);
-  o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 // bfloat16 copy of int8 weight codes: every code (|c| <= 127) is exact in
 // bfloat16. One thread per 8 codes: an 8-byte load, a 16-byte store.
 __global__ void k_i8_to_bf16(const int8_t* __restrict__ in, uint16_t* __restrict__ out, int64_t n8) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= n8) return;
-  const uint2 q = reinterpret_cast<const uint2*>(in)[i];
-  const uint32_t w[2] = {q.x, q.y};
-  uint32_t o[4];
+  POETX_GRID_STRIDE(i, n8) {
+    const uint2 q = reinterpret_cast<const uint2*>(in)[i];
+    const uint32_t w[2] = {q.x, q.y};
+    uint32_t o[4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float a = static_cast<float>(static_cast<int8_t>((w[h] >> (16 * e)) & 0xff));
-      const float b = static_cast<float>(static_cast<int8_t>((w[h] >> (16 * e + 8)) & 0xff));
-      o[2 * h + e] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+      for (int e = 0; e < 2; ++e) {
+        const float a = static_cast<float>(static_cast<int8_t>((w[h] >> (16 * e)) & 0xff));
+        const float b = static_cast<float>(static_cast<int8_t>((w[h] >> (16 * e + 8)) & 0xff));
+        o[2 * h + e] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+      }
     }
+    reinterpret_cast<uint4*>(out)[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  reinterpret_cast<uint4*>(out)[i] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __global__ void k_bf16_to_f32(const bf16_t* __restrict__ in, float* __restrict__ out, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i < n) out[i] = bf16_to_f32(in[i]);
+  POETX_GRID_STRIDE(i, n) out[i] = bf16_to_f32(in[i]);
 }
 
 // amax[c] = max over rows of |w[r][c]|: blockIdx.y takes a band of rows, one
@@ -327,10 +338,11 @@ __global__ void k_col_absmax(const float* __restrict__ w, int64_t rows, int64_t 
                              unsigned int* __restrict__ amax) {
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (c >= cols) return;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * band;
-  const int64_t r1 = r0 + band < rows ? r0 + band : rows;
   float m = 0.f;
-  for (int64_t r = r0; r < r1; ++r) m = fmaxf(m, fabsf(w[r * cols + c]));
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.y) * band; r0 < rows; r0 += static_cast<int64_t>(gridDim.y) * band) {
+    const int64_t r1 = r0 + band < rows ? r0 + band : rows;
+    for (int64_t r = r0; r < r1; ++r) m = fmaxf(m, fabsf(w[r * cols + c]));
+  }
   atomicMax(amax + c, __float_as_uint(m));
 }
 
@@ -339,21 +351,21 @@ __global__ void k_col_absmax(const float* __restrict__ w, int64_t rows, int64_t 
 // division is the correctly rounded float32 one.
 __global__ void k_quant_i8_cols(const float* __restrict__ w, const unsigned int* __restrict__ amax,
                                 int8_t* __restrict__ wq, float* __restrict__ scale, int64_t rows, int64_t cols) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // 8-column group
   const int64_t per_row = cols >> 3;
-  if (g >= rows * per_row) return;
-  const int64_t r = g / per_row, c0 = (g % per_row) * 8;
-  uint32_t out[2] = {0u, 0u};
+  POETX_GRID_STRIDE(g, rows * per_row) {  // g: 8-column group
+    const int64_t r = g / per_row, c0 = (g % per_row) * 8;
+    uint32_t out[2] = {0u, 0u};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t c = c0 + e;
-    float sc = __uint_as_float(amax[c]) / 127.f;
-    sc = sc > 0.f ? sc : 1.f;
-    if (r == 0) scale[c] = sc;
-    const float q = fminf(fmaxf(rintf(w[r * cols + c] / sc), -127.f), 127.f);
-    out[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu) << (8 * (e & 3));
+    for (int e = 0; e < 8; ++e) {
+      const int64_t c = c0 + e;
+      float sc = __uint_as_float(amax[c]) / 127.f;
+      sc = sc > 0.f ? sc : 1.f;
+      if (r == 0) scale[c] = sc;
+      const float q = fminf(fmaxf(rintf(w[r * cols + c] / sc), -127.f), 127.f);
+      out[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu) << (8 * (e & 3));
+    }
+    *reinterpret_cast<uint2*>(wq + r * cols + c0) = make_uint2(out[0], out[1]);
   }
-  *reinterpret_cast<uint2*>(wq + r * cols + c0) = make_uint2(out[0], out[1]);
 }
 
 // packed index of (i, l), i < l, in a block of size r
@@ -507,11 +519,11 @@ __global__ void __launch_bounds__(kThreads) k_unpack_skew64(const Seg2 sg, int b
 
 __global__ void k_cnp_mid(const float* __restrict__ Qf, const float* __restrict__ Q2f, uint16_t* __restrict__ Sh,
                           float* __restrict__ Sf, int64_t n) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n) return;
-  const float s = 2.f * Qf[e] + Q2f[e];
-  if (Sh) Sh[e] = f32_to_bf16(s);
-  if (Sf) Sf[e] = s;
+  POETX_GRID_STRIDE(e, n) {
+    const float s = 2.f * Qf[e] + Q2f[e];
+    if (Sh) Sh[e] = f32_to_bf16(s);
+    if (Sf) Sf[e] = s;
+  }
 }
 
 template <typename TG>
@@ -708,7 +720,8 @@ __global__ void __launch_bounds__(kThreads) k_cnp_h1(const float* __restrict__ U
   }
 }
 
-inline unsigned grid1(int64_t n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
+inline unsigned grid1(int64_t n) { return static_cast<unsigned>(std::min<int64_t>((n + kThreads - 1) / kThreads, kMaxGrid1)); }
+inline unsigned grid_yz(int64_t n) { return static_cast<unsigned>(std::min<int64_t>(n, kMaxGridYZ)); }
 
 template <typename T>
 void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
@@ -731,7 +744,7 @@ void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* 
                        static_cast<int>(ncols), nrows, rows, chunk);
   } else {
     const unsigned gx = static_cast<unsigned>(std::min<int64_t>((ncols + kThreads - 1) / kThreads, 1024));
-    hipLaunchKernelGGL(k_gather_cols_direct<T>, dim3(gx, static_cast<unsigned>(nrows)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(k_gather_cols_direct<T>, dim3(gx, grid_yz(nrows)), dim3(kThreads), 0, s,
                        static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
                        ncols, nrows);
   }
@@ -786,7 +799,7 @@ bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scal
   if (cols % 8 != 0) return false;
   fill_zero_f32(reinterpret_cast<float*>(amax), cols, s);  // bit pattern 0 = +0.0
   const int64_t band = 64;
-  const dim3 g(static_cast<unsigned>((cols + kThreads - 1) / kThreads), static_cast<unsigned>((rows + band - 1) / band));
+  const dim3 g(static_cast<unsigned>((cols + kThreads - 1) / kThreads), grid_yz((rows + band - 1) / band));
   hipLaunchKernelGGL(k_col_absmax, g, dim3(kThreads), 0, s, w, rows, cols, band, amax);
   hipLaunchKernelGGL(k_quant_i8_cols, dim3(grid1(rows * (cols / 8))), dim3(kThreads), 0, s, w, amax, wq, scale,
                      rows, cols);
@@ -795,7 +808,7 @@ bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scal
 
 bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return true;
-  const dim3 g(static_cast<unsigned>((cols + 63) / 64), static_cast<unsigned>((rows + 63) / 64));
+  const dim3 g(static_cast<unsigned>((cols + 63) / 64), grid_yz((rows + 63) / 64));
   switch (esize) {
     case 1: hipLaunchKernelGGL(k_transpose<uint8_t>, g, dim3(kThreads), 0, s, static_cast<const uint8_t*>(in),
                                static_cast<uint8_t*>(out), rows, cols); return true;

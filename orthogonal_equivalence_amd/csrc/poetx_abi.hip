@@ -46,12 +46,22 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
   return true;
 }
 
+// Size limits. Tokens: every token count the kernels form (T rounded up to a
+// tile, a split's share) stays an int. Blocks: the CNP launches put the
+// blocks of both sides in one grid dimension, whose reported limit is 65535.
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+constexpr int64_t kMaxFeatures = int64_t(1) << 24;
+constexpr int64_t kMaxBlocks = 65535;
+
+bool tokens_ok(int64_t T) { return T >= 0 && T <= kMaxTokens; }
+
 bool layer_ok(const poetx_layer* L) {
   if (!L) return false;
   if (L->m < 8 || L->n < 8 || L->m % 8 || L->n % 8) return false;
-  if (L->m > (1 << 24) || L->n > (1 << 24)) return false;
+  if (L->m > kMaxFeatures || L->n > kMaxFeatures) return false;
   for (int b : {L->b_r, L->b_p})
     if (b < 8 || b > 1024 || b % 8) return false;
+  if ((L->m + L->b_r - 1) / L->b_r + (L->n + L->b_p - 1) / L->b_p > kMaxBlocks) return false;
   if (L->act_dtype == POETX_F32) return L->w_dtype == POETX_F32;
   if (L->act_dtype == POETX_BF16) {
     if (L->w_dtype == POETX_BF16) return true;
@@ -826,7 +836,7 @@ size_t poetx_gbuf_bytes(const poetx_layer* L, int side) {
 }
 
 size_t poetx_saved_bytes(const poetx_layer* L, int64_t T) {
-  if (!layer_ok(L) || T < 0) return 0;
+  if (!layer_ok(L) || !tokens_ok(T)) return 0;
   return static_cast<size_t>(T * (L->m + L->n) * act_size(L));
 }
 
@@ -836,7 +846,7 @@ size_t poetx_wbuf_bytes(const poetx_layer* L) {
 }
 
 size_t poetx_workspace_bytes(const poetx_layer* L, int64_t T, int op) {
-  if (!layer_ok(L) || T < 0) return 0;
+  if (!layer_ok(L) || !tokens_ok(T)) return 0;
   return ws_bytes_for(L, T, op);
 }
 
@@ -895,7 +905,7 @@ int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_sc
 int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r, const int32_t* perm_p,
                   const void* g_r, const void* g_p, const void* wpt, const float* wscale_p, void* z, void* saved,
                   void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
   if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z, saved})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
@@ -913,7 +923,7 @@ int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t*
 int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r,
                       const int32_t* perm_p, const void* g_r, const void* g_p, const void* wpt,
                       const float* wscale_p, void* z, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
   if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
@@ -932,7 +942,7 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
                    const int32_t* perm_p, const float* q_r, const float* q_p, const void* g_r, const void* g_p,
                    const void* wp, const float* wscale_p, float* dq_r, float* dq_p, void* dx, void* ws,
                    size_t ws_bytes, hipStream_t stream) {
-  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (!ptrs_ok({dq_r, dq_p})) return POETX_EINVAL;
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   clear_pending_error();
@@ -959,7 +969,7 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
                        const int32_t* perm_p, const float* q_r, const float* q_p, const void* g_r,
                        const void* g_p, const void* wp, const void* wpt, const float* wscale_p, float* dq_r,
                        float* dq_p, void* dx, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!layer_ok(L) || T < 0 || T > (1LL << 31) - 1) return POETX_EINVAL;
+  if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (!ptrs_ok({dq_r, dq_p})) return POETX_EINVAL;
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   clear_pending_error();

@@ -78,6 +78,8 @@ def test_sizes_match_block_structure(m, n, b_r, b_p):
     dict(m=16, n=16, b_r=8, b_p=8, act="f32", weight="bf16"),
     dict(m=16, n=16, b_r=8, b_p=8, act="f32", weight="i8"),
     dict(m=24, n=32, b_r=8, b_p=8, act="bf16", weight="i8"),   # int8 rows need 16-byte multiples
+    dict(m=(1 << 24) + 8, n=16, b_r=1024, b_p=8),               # more than 2^24 features
+    dict(m=8 * 65535, n=8, b_r=8, b_p=8),                       # 65536 blocks over the two sides
 ])
 def test_invalid_layers_are_rejected(bad):
     kw = dict(act="bf16", weight="bf16")
@@ -88,6 +90,27 @@ def test_invalid_layers_are_rejected(bad):
     with pytest.raises(px.PoetxError) as e:
         px.poetx_cnp_build(L, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
     assert e.value.status == px.POETX_EINVAL
+
+
+def test_size_limits_at_their_edges():
+    # the largest accepted feature count and block count
+    L = px.make_layer(1 << 24, 8, 1024, 8, "bf16", "bf16")
+    assert px.poetx_packed_len(L, px.POETX_SIDE_R) == O.packed_len(1 << 24, 1024)
+    L = px.make_layer(8 * 65534, 8, 8, 8, "bf16", "bf16")     # 65534 + 1 blocks
+    assert px.poetx_packed_len(L, px.POETX_SIDE_R) == O.packed_len(8 * 65534, 8)
+    # tokens: up to 2^30
+    L = px.make_layer(64, 64, 16, 16, "bf16", "bf16")
+    assert px.poetx_saved_bytes(L, 1 << 30) == (1 << 30) * 128 * 2
+    assert px.poetx_workspace_bytes(L, 1 << 30, px.POETX_OP_FORWARD) > 0
+    assert px.poetx_saved_bytes(L, (1 << 30) + 1) == 0
+    assert px.poetx_workspace_bytes(L, (1 << 30) + 1, px.POETX_OP_BACKWARD) == 0
+    for call in (lambda T: px.poetx_forward(L, T, *([FAKE] * 9), FAKE, 1 << 62, stream=0),
+                 lambda T: px.poetx_backward(L, T, *([FAKE] * 13), FAKE, 1 << 62, stream=0),
+                 lambda T: px.poetx_forward_mem(L, T, *([FAKE] * 8), FAKE, 1 << 62, stream=0),
+                 lambda T: px.poetx_backward_mem(L, T, *([FAKE] * 14), FAKE, 1 << 62, stream=0)):
+        with pytest.raises(px.PoetxError) as e:
+            call((1 << 30) + 1)
+        assert e.value.status == px.POETX_EINVAL
 
 
 def test_argument_errors_before_any_launch():
