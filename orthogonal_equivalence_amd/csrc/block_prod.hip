@@ -14,7 +14,8 @@
 // S = 2Q + Q^2 in the epilogue, then G - I = 2Q + 2Q^2 + S Q^2 written as both
 // planes of the block buffer; the adjoint is three (see poetx_abi.hip).
 //
-// gfx950 design: 128 x 128 output tile per workgroup, 4 waves of 64 x 64
+// gfx950 design: 128 x 128 output tile per workgroup (the tiles of one block
+// on one XCD), 4 waves of 64 x 64
 // (2 x 2 tiles of v_mfma_f32_32x32x16_bf16), K in steps of 64 through two
 // LDS stages filled with global_load_lds_dwordx4 (128-byte rows, XOR
 // swizzle); the epilogue stages each wave's 32 x 64 band through LDS so that
@@ -70,8 +71,11 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
   const int wm = wave & 1, wn = wave >> 1;
   const int tiles = d.b / TB;
   const int per_blk = tiles * tiles;
-  const int z = blockIdx.x / per_blk;
-  const int t = blockIdx.x % per_blk;
+  // the tiles of a block run on one XCD, so its operand rows are re-read
+  // from that XCD's L2
+  const int pid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int z = pid / per_blk;
+  const int t = pid % per_blk;
   const int i0 = (t / tiles) * TB, n0 = (t % tiles) * TB;
   const int64_t zoff = static_cast<int64_t>(z) * d.b * d.b;
   // outputs of the second side start at its own block 0
