@@ -33,6 +33,7 @@ namespace poetx {
 namespace {
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef POETX_DENSE_BK
 #define POETX_DENSE_BK 64
@@ -265,9 +266,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
           v[0] *= s0.x; v[1] *= s0.y; v[2] *= s0.z; v[3] *= s0.w;
           v[4] *= s1.x; v[5] *= s1.y; v[6] *= s1.z; v[7] *= s1.w;
         }
-        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * d.ldc + n) =
-            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7]));
+        // non-temporal: the output is not read again here, and keeping it
+        // out of L2 leaves the operand panels there for the next tiles
+        const u32x4_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                           pack_bf16x2(v[6], v[7])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(m) * d.ldc + n));
       }
     }
   }
