@@ -172,8 +172,10 @@ k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int6
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 8 * 32 * 33 * 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int blk = blockIdx.x / wgs_per_block;
-  const int part = blockIdx.x % wgs_per_block;
+  // the workgroups of one block run on one XCD (one L2 holds its plane)
+  const int pid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int blk = pid / wgs_per_block;
+  const int part = pid % wgs_per_block;
   const int64_t row0 = static_cast<int64_t>(blk) * B;
   const int height = static_cast<int>(min(static_cast<int64_t>(B), rows - row0));  // short last block
   const int64_t c_begin = static_cast<int64_t>(part) * cols_per_wg;
