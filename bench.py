@@ -27,6 +27,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "POET-X layer fwd+bwd tokens/s at Llama-8B shapes; % of MFMA/HBM peak on 1 GPU"
+
+# The pages' own figures, on an H100 (zhichai.net digest of arXiv:2603.05500):
+# the CNP forward before and after its fused kernel, section "3. Cayley-Neumann
+# 参数化优化", and the single-layer latency of POET-X fast, section "4. 定制 CUDA
+# Kernel 层", for which neither the layer shape nor the passes timed are given.
+# Reported as context beside the matching figures measured here, not as targets.
+PAGES_H100 = {"cnp_forward_unfused_ms": 0.316, "cnp_forward_fused_ms": 0.107, "layer_latency_ms": 1.38}
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -440,6 +447,12 @@ def main():
         "kernels_ms": kernels,
         "kernel_roofline": kernel_roofline(cfg, per),
         "torch_linear_fwd_bwd_ms": yard,
+        "pages_context": {
+            "device": "NVIDIA H100, the pages' setting; shapes not stated",
+            **PAGES_H100,
+            "cnp_build_ms_here": kernels.get("cnp_build"),
+            "layer_fwd_bwd_ms_here": round(ms_fwd_bwd, 4),
+        },
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg)
