@@ -606,16 +606,31 @@ __global__ void __launch_bounds__(kThreads) k_pack_asym(const float* __restrict_
 // U = sum of the split partials (fixed order), written as its symmetric and
 // skew parts Us = (U + U^T) / 2, Uk = (U - U^T) / 2 (float, and bfloat16
 // copies when requested). One workgroup per tile pair (I, L), I <= L.
-__global__ void __launch_bounds__(kThreads) k_reduce_symskew(const float* __restrict__ part, int nsplit, int b,
-                                                            int64_t blocks_elems, float* __restrict__ Us,
+// Blocks [0, z_split) take their partials from side 0, the rest from side 1
+// (each side has its own split count); the outputs of both sides are one
+// array of blocks.
+struct SymSkewIn {
+  const float* part0;
+  const float* part1;
+  int64_t blocks_elems0, blocks_elems1;  // stride between splits
+  int nsplit0, nsplit1;
+  int z_split;
+};
+
+__global__ void __launch_bounds__(kThreads) k_reduce_symskew(const SymSkewIn in, int b, float* __restrict__ Us,
                                                             float* __restrict__ Uk, uint16_t* __restrict__ Ush,
                                                             uint16_t* __restrict__ Ukh) {
   __shared__ float ta[32][33];
   __shared__ float tb[32][33];
   const int z = blockIdx.y;
+  const bool hi = z >= in.z_split;
+  const float* __restrict__ part = hi ? in.part1 : in.part0;
+  const int nsplit = hi ? in.nsplit1 : in.nsplit0;
+  const int64_t blocks_elems = hi ? in.blocks_elems1 : in.blocks_elems0;
   int I, Lt;
   tile_pair(static_cast<int>(blockIdx.x), (b + 31) / 32, I, Lt);
-  const int64_t base = static_cast<int64_t>(z) * b * b;
+  const int64_t base_in = static_cast<int64_t>(hi ? z - in.z_split : z) * b * b;  // within the side's partials
+  const int64_t base = static_cast<int64_t>(z) * b * b;                          // in the outputs
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   // each thread sums 4 rows of tile (I, L) and 4 of tile (L, I) over the
   // splits, in split order; a group of 4 splits puts all 32 loads in flight
@@ -629,8 +644,8 @@ __global__ void __launch_bounds__(kThreads) k_reduce_symskew(const float* __rest
     const int l2 = Lt * 32 + k, i2 = I * 32 + tx;  // tile (L, I) row-wise
     va[k4] = i < b && l < b;
     vm[k4] = l2 < b && i2 < b;
-    oa[k4] = va[k4] ? base + static_cast<int64_t>(i) * b + l : base;
-    om[k4] = vm[k4] ? base + static_cast<int64_t>(l2) * b + i2 : base;
+    oa[k4] = va[k4] ? base_in + static_cast<int64_t>(i) * b + l : base_in;
+    om[k4] = vm[k4] ? base_in + static_cast<int64_t>(l2) * b + i2 : base_in;
     a[k4] = 0.f;
     m[k4] = 0.f;
   }
@@ -861,11 +876,14 @@ void pack_asym2(const float* E, int b, int64_t dim0, int n0, float* dq0, int64_t
                      dim3(kThreads), 0, s, E, sg, dq0, dq1, b, t);
 }
 
-void reduce_symskew(const float* part, int nsplit, int b, int nblk, float* Us, float* Uk, uint16_t* Ush,
-                    uint16_t* Ukh, hipStream_t s) {
+void reduce_symskew2(const float* part0, int nsplit0, int nblk0, const float* part1, int nsplit1, int nblk1, int b,
+                     float* Us, float* Uk, uint16_t* Ush, uint16_t* Ukh, hipStream_t s) {
+  if (nblk0 + nblk1 <= 0) return;
   const unsigned t = static_cast<unsigned>((b + 31) / 32);
-  hipLaunchKernelGGL(k_reduce_symskew, dim3(t * (t + 1) / 2, static_cast<unsigned>(nblk)), dim3(kThreads), 0, s,
-                     part, nsplit, b, static_cast<int64_t>(nblk) * b * b, Us, Uk, Ush, Ukh);
+  const int64_t bb = static_cast<int64_t>(b) * b;
+  const SymSkewIn in{part0, part1, nblk0 * bb, nblk1 * bb, nsplit0, nsplit1, nblk0};
+  hipLaunchKernelGGL(k_reduce_symskew, dim3(t * (t + 1) / 2, static_cast<unsigned>(nblk0 + nblk1)), dim3(kThreads),
+                     0, s, in, b, Us, Uk, Ush, Ukh);
 }
 
 void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16_t* Hh, hipStream_t s) {

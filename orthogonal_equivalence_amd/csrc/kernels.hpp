@@ -63,11 +63,13 @@ void cnp_finish2(const float* Qf, const float* Q2f, const float* Tf, int b, int 
 void pack_asym2(const float* E, int b, int64_t dim0, int n0, float* dq0, int64_t dim1, int n1, float* dq1,
                 hipStream_t stream);
 
-// U = sum over nsplit partials part[s][z] (fixed order) for nblk b x b blocks,
-// written as Us = (U + U^T)/2 and Uk = (U - U^T)/2 (float; bfloat16 copies if
-// Ush / Ukh are not null).
-void reduce_symskew(const float* part, int nsplit, int b, int nblk, float* Us, float* Uk, uint16_t* Ush,
-                    uint16_t* Ukh, hipStream_t stream);
+// U = sum over the partials part[s][z] (fixed order s = 0, 1, ...) of the
+// b x b blocks of two sides in one launch: nblk0 blocks with nsplit0 partials
+// from part0, then nblk1 with nsplit1 from part1 (nblk1 = 0: one side).
+// Written as Us = (U + U^T)/2 and Uk = (U - U^T)/2 for the nblk0 + nblk1
+// blocks back to back (float; bfloat16 copies if Ush / Ukh are not null).
+void reduce_symskew2(const float* part0, int nsplit0, int nblk0, const float* part1, int nsplit1, int nblk1, int b,
+                     float* Us, float* Uk, uint16_t* Ush, uint16_t* Ukh, hipStream_t stream);
 
 // H1 = 4 Uk - 2 (P1 - P1^T) per block (float and/or bfloat16 outputs).
 void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16_t* Hh, hipStream_t stream);

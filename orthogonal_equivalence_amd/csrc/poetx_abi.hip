@@ -787,10 +787,16 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
     ProfScope p("cnp_bwd", stream);
     const bool bf = is_bf16(L);
     const int64_t eR = block_elems(R);
-    reduce_symskew(w.part_r, spR.nsplit, R.b, R.nblk, w.Us, w.Uk, bf ? w.Ush : nullptr, bf ? w.Ukh : nullptr,
-                   stream);
-    reduce_symskew(w.part_p, spP.nsplit, P.b, P.nblk, w.Us + eR, w.Uk + eR, bf ? w.Ush + eR : nullptr,
-                   bf ? w.Ukh + eR : nullptr, stream);
+    // both sides' blocks in one launch when their block sizes match
+    if (R.b == P.b) {
+      reduce_symskew2(w.part_r, spR.nsplit, R.nblk, w.part_p, spP.nsplit, P.nblk, R.b, w.Us, w.Uk,
+                      bf ? w.Ush : nullptr, bf ? w.Ukh : nullptr, stream);
+    } else {
+      reduce_symskew2(w.part_r, spR.nsplit, R.nblk, nullptr, 0, 0, R.b, w.Us, w.Uk, bf ? w.Ush : nullptr,
+                      bf ? w.Ukh : nullptr, stream);
+      reduce_symskew2(w.part_p, spP.nsplit, P.nblk, nullptr, 0, 0, P.b, w.Us + eR, w.Uk + eR,
+                      bf ? w.Ush + eR : nullptr, bf ? w.Ukh + eR : nullptr, stream);
+    }
     if (R.b == P.b) {
       ok = ok && cnp_bwd_group(L, group_of(R, P), q_r, q_p, w.Us, w.Uk, w.Ush, w.Ukh, dq_r, dq_p, cnp_ws, stream);
     } else {
