@@ -275,6 +275,14 @@ __global__ void k_fill_zero(float* p, int64_t n) {
   POETX_GRID_STRIDE(i, n) p[i] = 0.f;
 }
 
+// two arrays in one launch: elements [0, n0) of p0, then [0, n1) of p1
+__global__ void k_fill_zero2(float* p0, int64_t n0, float* p1, int64_t n1) {
+  POETX_GRID_STRIDE(i, n0 + n1) {
+    if (i < n0) p0[i] = 0.f;
+    else p1[i - n0] = 0.f;
+  }
+}
+
 // ---- int8 base weight around a merge ----------------------------------------
 // out[r][c] = wq[r][c] * scale[cmap[c]] (cmap null: identity), 8 columns per
 // thread: 8-byte loads, 32-byte stores.
@@ -837,6 +845,10 @@ bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize,
 
 void fill_zero_f32(float* p, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_fill_zero, dim3(grid1(n)), dim3(kThreads), 0, s, p, n);
+}
+
+void fill_zero2_f32(float* p0, int64_t n0, float* p1, int64_t n1, hipStream_t s) {
+  if (n0 + n1 > 0) hipLaunchKernelGGL(k_fill_zero2, dim3(grid1(n0 + n1)), dim3(kThreads), 0, s, p0, n0, p1, n1);
 }
 
 void unpack_skew2(const float* q0, int64_t dim0, int n0, const float* q1, int64_t dim1, int n1, int b, float* Qf,

@@ -26,6 +26,8 @@ bool transpose(const void* in, void* out, int64_t rows, int64_t cols, int esize,
 
 // Zero n floats (a fill kernel, safe inside captured graphs).
 void fill_zero_f32(float* p, int64_t n, hipStream_t stream);
+// p0[0, n0) and p1[0, n1) set to zero in one launch
+void fill_zero2_f32(float* p0, int64_t n0, float* p1, int64_t n1, hipStream_t stream);
 
 // int8 base weight around a merge (per-output-column scales):
 // out[r][c] = wq[r][c] * scale[cmap ? cmap[c] : c] as float (cols % 8 == 0);

@@ -953,8 +953,7 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   clear_pending_error();
   if (T == 0) {
-    fill_zero_f32(dq_r, packed_len(R), stream);
-    fill_zero_f32(dq_p, packed_len(P), stream);
+    fill_zero2_f32(dq_r, packed_len(R), dq_p, packed_len(P), stream);
     return launch_status();
   }
   if (!ptrs_ok({saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, dx})) return POETX_EINVAL;
@@ -980,8 +979,7 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   clear_pending_error();
   if (T == 0) {
-    fill_zero_f32(dq_r, packed_len(R), stream);
-    fill_zero_f32(dq_p, packed_len(P), stream);
+    fill_zero2_f32(dq_r, packed_len(R), dq_p, packed_len(P), stream);
     return launch_status();
   }
   if (!ptrs_ok({x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt, dx})) return POETX_EINVAL;
@@ -1054,8 +1052,7 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
       ProfScope p("merge_requant", stream);
       ok = ok && requant_i8_cols(static_cast<const float*>(w.C2), w.amax, static_cast<int8_t*>(w0), w_scale, L->m,
                                  L->n, stream);
-      fill_zero_f32(q_r, packed_len(R), stream);
-      fill_zero_f32(q_p, packed_len(P), stream);
+      fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
     }
     if (!ok) return POETX_EUNSUPPORTED;
     return launch_status();
@@ -1099,8 +1096,7 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
     ProfScope p("merge_scatter", stream);
     inverse_perm(perm_p, w.inv_p, L->n, stream);
     ok = ok && gather_cols(M, L->n, nullptr, w0, L->n, perm_r, w.inv_p, L->n, L->m, w_size(L), stream);
-    fill_zero_f32(q_r, packed_len(R), stream);
-    fill_zero_f32(q_p, packed_len(P), stream);
+    fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
   }
   if (!ok) return POETX_EUNSUPPORTED;
   return launch_status();
