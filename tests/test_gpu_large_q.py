@@ -1,0 +1,113 @@
+"""Parity of the HIP path with the float64 oracle on layers with large
+rotations (||Q||_2 about 0.45 and 0.8; cases in large_q_cases.py).
+
+At the workloads' own sigma_q = 1e-3 the rotation is a few percent of every
+output, and the Cayley-Neumann adjoint's terms in Q^2 and Q^3 (zhichai.net
+digest of arXiv:2603.05500, section "3. Cayley-Neumann 参数化优化") sit below
+the bfloat16 tolerance. Here each of them moves dq by far more than the
+tolerance (test_adjoint_sensitivity.py shows it on the CPU for these exact
+inputs), so a wrong product in the CNP chain or its adjoint fails.
+
+Besides the whole tensors, the parts the rotations contribute are compared
+on their own, each against the oracle's value of the same part:
+  z  - X W0,   dx - dZ W0^T,   W0' - W0 (merge),
+  dq - dq0, where dq0 is the oracle's adjoint of the same block gradients
+            with Q = 0 (the Q-independent part).
+Bar: relative Frobenius error <= 1e-5 (float32) or 2e-2 (bfloat16) for every
+tensor and every delta. The rotation is at least half of each compared
+tensor in these cases, so the rounding of a bfloat16 output to storage adds
+at most about 2^-8 relative to a delta.
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from large_q_cases import CASES  # noqa: E402
+from orthogonal_equivalence_amd import synth  # noqa: E402
+from orthogonal_equivalence_amd import poetx as px  # noqa: E402
+from orthogonal_equivalence_amd.device import DeviceLayer, to_device, to_host_f64  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    torch.cuda.init()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _planes(q, dim, b):
+    G = O.cnp_blocks(q, dim, b)
+    P = np.zeros((2, len(G), b, b))
+    for j, g in enumerate(G):
+        r = g.shape[0]
+        P[0, j, :r, :r] = g - np.eye(r)
+        P[1, j, :r, :r] = (g - np.eye(r)).T
+    return P
+
+
+def _dq_without_q(q, dim, b, blocks):
+    offs, sizes = O.packed_offsets(dim, b)
+    out = []
+    for o, r, U in zip(offs, sizes, blocks):
+        out.append(O.project_to_packed(O.cnp_adjoint(np.zeros((r, r)), U)))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("cfg,strength", CASES, ids=[c.name for c, _ in CASES])
+def test_large_rotation_parity(cfg, strength):
+    print(f"\n[gpu] {cfg.name} T={cfg.T} m={cfg.m} n={cfg.n} b={cfg.b_r} {cfg.act}/{cfg.weight} "
+          f"sigma_q={cfg.sigma_q}", flush=True)
+    L = synth.make_layer(cfg, 0)
+    A = synth.make_activations(cfg, 0)
+    merge = cfg.weight != "i8"
+    dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
+    dl.load(L)
+    dl.cnp_build()
+    dl.prepare()
+    z = dl.forward(to_device(A["X_raw"], cfg.act))
+    dq_r, dq_p, dx = dl.backward(to_device(A["dZ_raw"], cfg.act))
+    got = dict(z=to_host_f64(z), dq_r=to_host_f64(dq_r), dq_p=to_host_f64(dq_p), dx=to_host_f64(dx),
+               g_r=to_host_f64(dl.g_planes(px.POETX_SIDE_R)), g_p=to_host_f64(dl.g_planes(px.POETX_SIDE_P)))
+    if merge:
+        dl.merge()
+        got["w0"] = to_host_f64(dl.w0)
+    torch.cuda.synchronize()
+
+    W0 = O.dequantize(L["W0_raw"], L["w_scale"]) if cfg.weight == "i8" else L["W0"].astype(np.float64)
+    args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
+    ref = O.backward(A["X"], A["dZ"], *args)
+    XW = A["X"].astype(np.float64) @ W0
+    dZW = A["dZ"].astype(np.float64) @ W0.T
+    dq0_r = _dq_without_q(L["q_r"], cfg.m, cfg.b_r, ref["dG"])
+    dq0_p = _dq_without_q(L["q_p"], cfg.n, cfg.b_p, ref["dH"])
+    errs = {
+        "cnp_r": rel(got["g_r"], _planes(L["q_r"], cfg.m, cfg.b_r)),
+        "cnp_p": rel(got["g_p"], _planes(L["q_p"], cfg.n, cfg.b_p)),
+        "z": rel(got["z"], ref["fwd"]["Z"]),
+        "dq_r": rel(got["dq_r"], ref["dq_r"]),
+        "dq_p": rel(got["dq_p"], ref["dq_p"]),
+        "dx": rel(got["dx"], ref["dX"]),
+        "z-XW0": rel(got["z"] - XW, ref["fwd"]["Z"] - XW),
+        "dx-dZW0^T": rel(got["dx"] - dZW, ref["dX"] - dZW),
+        "dq_r-dq0": rel(got["dq_r"] - dq0_r, ref["dq_r"] - dq0_r),
+        "dq_p-dq0": rel(got["dq_p"] - dq0_p, ref["dq_p"] - dq0_p),
+    }
+    if merge:
+        w_ref = O.merge(*args)
+        errs["merge"] = rel(got["w0"], w_ref)
+        errs["W0'-W0"] = rel(got["w0"] - W0, w_ref - W0)
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL[cfg.act]}
+    assert not bad, bad

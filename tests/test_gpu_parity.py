@@ -120,7 +120,8 @@ SMALL = [
     # ragged token count and output width across several 256 x 256 output tiles
     _cfg("bf16_ragged_tiles", 1100, 320, 1800, 64, 64, "bf16", "bf16", 34),
     # fewer output tiles than CUs and K >= 2048: both dense products split
-    # every tile into four K parts summed by the last part to finish
+    # every tile into four K parts, whose fp32 partial tiles a second kernel
+    # adds in fixed part order
     _cfg("bf16_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 36),
     # the same with an int8 weight: codes copied to bfloat16, column scales in
     # the split sum's epilogue
@@ -328,7 +329,8 @@ def test_permutations_bit_exact(act, b, T):
 
 @pytest.mark.parametrize("cfg", [
     _cfg("determinism", 1024, 512, 768, 128, 128, "bf16", "bf16", 28),
-    # dense products split along K (the order in which parts finish varies)
+    # dense products split along K: the partials are summed in part order by
+    # a second kernel, so the result must not depend on which part ends first
     _cfg("determinism_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 36),
 ], ids=lambda c: c.name)
 def test_layer_is_deterministic(cfg):
