@@ -250,6 +250,25 @@ POETX_API int poetx_merge(const poetx_layer* L, const void* wp,
 POETX_API int poetx_sample_perm(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw,
                       int32_t* perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* poetx_sample_perm without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, draw and result as poetx_sample_perm,
+ * but the keys go to a scratch array inside the library: 2^20 64-bit words
+ * (8 MiB) per device, held by each device the library runs on until the
+ * process ends. The call allocates nothing.
+ *   dim: 1 <= dim <= 2^20, the scratch's size (POETX_EUNSUPPORTED above it,
+ *       POETX_EINVAL below 1 or for a null or unaligned perm).
+ *   perm [dim] int32, overwritten.
+ * The device is the one that runs `stream` (the current device for the null
+ * stream). The first call on a device looks up the scratch's device address
+ * (POETX_EHIP if that fails); make it outside graph capture. All calls on one
+ * device share the scratch: calls that can overlap on one device (different
+ * streams without ordering between them, host threads) race and may return
+ * wrong permutations. Calls ordered on one stream are safe: nothing in the
+ * scratch carries over from one call to the next. */
+POETX_API int poetx_sample_perm_static(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw,
+                                       int32_t* perm, hipStream_t stream);
+
 /* Kernel timing log (tracing). poetx_profile_enable(1) clears the log and
  * starts recording: from then on every step of every entry point (e.g.
  * "gemm_dense_fwd", "apply_p_bwd", "grad_h", "cnp_build_r") is bracketed by a

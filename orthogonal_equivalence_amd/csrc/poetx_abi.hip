@@ -811,6 +811,53 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
 
 }  // namespace
 
+// Scratch of poetx_sample_perm_static, the draw for callers that cannot
+// allocate: one packed key per index of the largest accepted draw (2^20
+// indices, 8 MiB). Every device the library runs on holds its own copy from
+// the load of the code object until the process ends. In host code the name
+// `scratch` is only a host-side stand-in: kernels must get the device address
+// that hipGetSymbolAddress returns for the device they run on.
+static __device__ __align__(256) uint64_t scratch[kMaxPermDim];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<uint64_t*> g_scratch_ptr;  // device address of `scratch`, per device
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current.
+int static_scratch(hipStream_t stream, uint64_t** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return POETX_EHIP;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (static_cast<size_t>(dev) >= g_scratch_ptr.size()) g_scratch_ptr.resize(static_cast<size_t>(dev) + 1, nullptr);
+  if (!g_scratch_ptr[static_cast<size_t>(dev)]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess || !p) {
+      g_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return POETX_EHIP;
+    }
+    g_scratch_ptr[static_cast<size_t>(dev)] = static_cast<uint64_t*>(p);
+  }
+  *out = g_scratch_ptr[static_cast<size_t>(dev)];
+  return POETX_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int poetx_abi_version(void) { return POETX_ABI_VERSION; }
@@ -1112,6 +1159,20 @@ int poetx_sample_perm(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw, i
   {
     ProfScope p("sample_perm", stream);
     if (!sample_perm(dim, seed, tag, draw, perm, static_cast<uint64_t*>(ws), stream)) return POETX_EUNSUPPORTED;
+  }
+  return launch_status();
+}
+
+int poetx_sample_perm_static(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw, int32_t* perm,
+                             hipStream_t stream) {
+  if (dim < 1 || !perm || !aligned16(perm)) return POETX_EINVAL;
+  if (dim > kMaxPermDim) return POETX_EUNSUPPORTED;
+  clear_pending_error();
+  uint64_t* keys = nullptr;
+  if (const int e = static_scratch(stream, &keys)) return e;
+  {
+    ProfScope p("sample_perm", stream);
+    if (!sample_perm(dim, seed, tag, draw, perm, keys, stream)) return POETX_EUNSUPPORTED;
   }
   return launch_status();
 }

@@ -33,7 +33,7 @@ EXPORTED = [
     "poetx_abi_version", "poetx_strerror", "poetx_last_hip_error", "poetx_packed_len", "poetx_gbuf_bytes",
     "poetx_saved_bytes", "poetx_wbuf_bytes", "poetx_workspace_bytes", "poetx_cnp_build",
     "poetx_weight_prepare", "poetx_forward", "poetx_backward", "poetx_forward_mem", "poetx_backward_mem",
-    "poetx_merge", "poetx_sample_perm",
+    "poetx_merge", "poetx_sample_perm", "poetx_sample_perm_static",
     "poetx_profile_enable", "poetx_profile_count", "poetx_profile_get",
 ]
 
@@ -83,6 +83,8 @@ _sig = {
     "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_sample_perm": (ctypes.c_int, [_I64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P, _P, _SZ,
                                          _P]),
+    "poetx_sample_perm_static": (ctypes.c_int, [_I64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P,
+                                                _P]),
     "poetx_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "poetx_profile_count": (ctypes.c_int, []),
     "poetx_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -200,6 +202,10 @@ def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, w_scale, q_r, q_p, ws=None,
 
 def poetx_sample_perm(dim, seed, tag, draw, perm, ws=None, ws_bytes=None, stream=None):
     _call("poetx_sample_perm", dim, seed, tag, draw, _ptr(perm), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+
+
+def poetx_sample_perm_static(dim, seed, tag, draw, perm, stream=None):
+    _call("poetx_sample_perm_static", dim, seed, tag, draw, _ptr(perm), _stream(stream))
 
 
 def poetx_profile_enable(enable):

@@ -28,7 +28,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     lib = ctypes.CDLL(px.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -188,6 +188,17 @@ def test_sample_perm_argument_errors():
     # the layer's workspace query covers the wider side
     L = px.make_layer(4096, 14336, 256, 256, "bf16", "bf16")
     assert px.poetx_workspace_bytes(L, 0, px.POETX_OP_SAMPLE_PERM) == 8 * 14336
+
+
+def test_sample_perm_static_argument_errors():
+    # rejected on the host before the scratch is looked up or anything runs
+    for dim, ptr, status in [(0, FAKE, px.POETX_EINVAL), (-5, FAKE, px.POETX_EINVAL),
+                             (16, None, px.POETX_EINVAL), (16, FAKE + 4, px.POETX_EINVAL),
+                             ((1 << 20) + 1, FAKE, px.POETX_EUNSUPPORTED),
+                             (1 << 40, FAKE, px.POETX_EUNSUPPORTED)]:
+        with pytest.raises(px.PoetxError) as e:
+            px.poetx_sample_perm_static(dim, 1, 2, 3, ptr, stream=0)
+        assert e.value.status == status, (dim, ptr)
 
 
 def test_last_hip_error_without_failure():
