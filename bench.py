@@ -177,9 +177,7 @@ def algorithmic_work(cfg):
         "merge_left": (2 * wes * m * n, 2.0 * m * n * br),
         "merge_transpose": (2 * wes * m * n, 0.0),
         "merge_right": (2 * wes * m * n, 2.0 * m * n * bp),
-        "merge_scatter": (2 * wes * m * n, 0.0),
-        "prepare_permute": (2 * wes * m * n, 0.0),
-        "prepare_transpose": (2 * wes * m * n, 0.0),
+        "merge_reframe": (2 * wes * m * n, 0.0),
     }
     return w
 
@@ -269,7 +267,6 @@ def main():
     dx = dl.act_tensor(cfg.T, cfg.m)
     dq_r = torch.empty_like(dl.q_r)
     dq_p = torch.empty_like(dl.q_p)
-    dl.prepare()
     draws = itertools.count(1)
     # a merge leaves q = 0; each step starts from the seeded nonzero q (a
     # device copy standing in for the optimizer's update, inside the timed
@@ -283,9 +280,9 @@ def main():
             dl.q_p.copy_(q_step_p)
 
     def merge_cycle():
-        # what a training loop runs at a merge: W0 <- R W0 P with q <- 0, a
-        # new draw of both permutations (beside the merge, on a second
-        # stream), the permuted-frame weight rebuilt
+        # what a training loop runs at a merge: a new draw of both
+        # permutations (on a second stream, beside the merge's block
+        # products), W0 <- R W0 P with q <- 0 written into their frame
         dl.merge_cycle(MERGE_SEED, 0, next(draws))
 
     def step():
@@ -396,7 +393,7 @@ def main():
     # the merge cycle on the launch stream; the permutation draws run beside
     # the merge on a second stream, so their (overlapping) time is reported
     # on its own
-    ms_merge = sum(per[k][0] for k in per if k.startswith(("merge", "prepare"))) / args.steps
+    ms_merge = sum(per[k][0] for k in per if k.startswith("merge")) / args.steps
     ms_draws = sum(per[k][0] for k in per if k.startswith("sample_perm")) / args.steps
 
     yard = None
@@ -433,7 +430,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "m": cfg.m, "n": cfg.n, "b_r": cfg.b_r,
                    "b_p": cfg.b_p, "weight": cfg.weight,
                    "step": ("q_update(copy)+" if cfg.merge else "") + "cnp_build+forward+backward"
-                   + ("+merge+perm_draw+weight_prepare" if cfg.merge else "")},
+                   + ("+perm_draw+merge_into_new_frame" if cfg.merge else "")},
         "roofline": roofline,
         "cpu_baseline": None,
         "ms_per_step_with_kernel_log": round(ms_logged / args.steps, 4),

@@ -56,7 +56,7 @@ extern "C" {
 #define POETX_API
 #endif
 
-#define POETX_ABI_VERSION 1
+#define POETX_ABI_VERSION 2
 
 enum {
   POETX_OK = 0,
@@ -78,7 +78,8 @@ enum {
   POETX_OP_MERGE = 4,
   POETX_OP_FORWARD_MEM = 5,
   POETX_OP_BACKWARD_MEM = 6,
-  POETX_OP_SAMPLE_PERM = 7
+  POETX_OP_SAMPLE_PERM = 7,
+  POETX_OP_WEIGHT_EXPORT = 8
 };
 
 typedef struct poetx_layer {
@@ -118,12 +119,14 @@ POETX_API size_t poetx_gbuf_bytes(const poetx_layer* L, int side);
  * row-major. */
 POETX_API size_t poetx_saved_bytes(const poetx_layer* L, int64_t T);
 
-/* Bytes of permuted-frame weight (each of wp and wpt in poetx_weight_prepare):
- * m x n elements of w_dtype. */
+/* Bytes of the permuted-frame weight wp (m x n elements of w_dtype), the one
+ * copy of the base weight a layer keeps (section "1. 输入中心化架构": the
+ * method adds no second m x n weight). */
 POETX_API size_t poetx_wbuf_bytes(const poetx_layer* L);
 
 /* Workspace bytes an operation needs for T tokens (T ignored by CNP build,
- * weight preparation, merge and permutation draws). 0 means none. */
+ * weight preparation and export, merge and permutation draws). 0 means
+ * none. */
 POETX_API size_t poetx_workspace_bytes(const poetx_layer* L, int64_t T, int op);
 
 /* CNP build (section "3. Cayley-Neumann 参数化优化": G = (I+Q)(I+Q+Q^2+Q^3),
@@ -135,23 +138,33 @@ POETX_API int poetx_cnp_build(const poetx_layer* L, const float* q_r, const floa
                     void* g_r, void* g_p, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
-/* Permuted-frame base weight: wp = Psi W0 Phi^T (wp[i][c] =
- * w0[perm_r[i]][perm_p[c]], m x n) and wpt = its transpose (n x m), both in
- * w_dtype; for I8 also wscale_p[c] = w_scale[perm_p[c]] (n floats; w_scale
- * and wscale_p are ignored otherwise and may be NULL). This is the weight
- * poetx_forward (wpt) and poetx_backward (wp) consume; rebuild it whenever W0
- * or a permutation changes (after poetx_merge and resampling). */
+/* Permuted-frame base weight from W0 in the original frame (loading a
+ * weight or a checkpoint): wp = Psi W0 Phi^T, i.e. wp[i][c] =
+ * w0[perm_r[i]][perm_p[c]] (m x n, w_dtype); for I8 also wscale_p[c] =
+ * w_scale[perm_p[c]] (n floats; w_scale and wscale_p are ignored otherwise
+ * and may be NULL). wp is the weight every other entry point takes: the
+ * forward reads it N-contiguous, the backward K-contiguous, and poetx_merge
+ * rewrites it in the frame of the next permutations. w0 may be freed after
+ * the call has run. */
 POETX_API int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_scale,
                          const int32_t* perm_r, const int32_t* perm_p,
-                         void* wp, void* wpt, float* wscale_p,
-                         void* ws, size_t ws_bytes, hipStream_t stream);
+                         void* wp, float* wscale_p, hipStream_t stream);
+
+/* The inverse of poetx_weight_prepare, for checkpoints: w0[perm_r[i]][
+ * perm_p[c]] = wp[i][c] (m x n, w_dtype) and, for I8, w_scale[perm_p[c]] =
+ * wscale_p[c]. ws: poetx_workspace_bytes(L, 0, POETX_OP_WEIGHT_EXPORT)
+ * bytes (n int32). With q = 0 (right after a merge) the layer's function is
+ * x -> x w0, whatever the permutations. */
+POETX_API int poetx_weight_export(const poetx_layer* L, const void* wp, const float* wscale_p,
+                        const int32_t* perm_r, const int32_t* perm_p,
+                        void* w0, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Forward, input-centric (section "1. 输入中心化架构"): Z = X R W0 P without
  * forming R W0 P.
  *   x [T][m], act_dtype. z [T][n], act_dtype, overwritten.
  *   g_r, g_p: CNP block buffers from poetx_cnp_build.
- *   wpt: permuted-frame transposed weight from poetx_weight_prepare;
- *   wscale_p: its permuted scales (I8 only, else ignored).
+ *   wp: permuted-frame weight (poetx_weight_prepare, poetx_merge);
+ *   wscale_p: its column scales (I8 only, else ignored).
  *   saved: poetx_saved_bytes(L, T) bytes, overwritten with X1 and Y1.
  * An int8 weight is dequantised at run time (section "POET-XQ"): its codes are
  * copied to bfloat16 (exact) in the workspace and the dense product applies
@@ -159,7 +172,7 @@ POETX_API int poetx_weight_prepare(const poetx_layer* L, const void* w0, const f
 POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
                   const int32_t* perm_r, const int32_t* perm_p,
                   const void* g_r, const void* g_p,
-                  const void* wpt, const float* wscale_p,
+                  const void* wp, const float* wscale_p,
                   void* z, void* saved, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
@@ -167,7 +180,7 @@ POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
  *   dq_r, dq_p: packed gradients (float, poetx_packed_len), overwritten.
  *   dx [T][m], act_dtype, overwritten.
  *   q_r, q_p: the packed parameters the CNP buffers were built from.
- *   wp: permuted-frame weight from poetx_weight_prepare (m x n).
+ *   wp, wscale_p: the forward's permuted-frame weight (m x n).
  * No W0 gradient exists (W0 is frozen). Outputs are overwritten, not
  * accumulated; T == 0 writes zero gradients. When the weight is not int8 and
  * m < T, the P-side product dY1 = dY2 H^T is not formed: the dense product
@@ -193,42 +206,50 @@ POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved,
  *   steps, same kernels) into the workspace
  *   (poetx_workspace_bytes(L, T, POETX_OP_BACKWARD_MEM)), then runs the
  *   backward; results equal poetx_backward's for the same inputs.
- *   x [T][m], act_dtype; wpt: the forward's weight, wp: the backward's.
+ *   x [T][m], act_dtype.
  * Costs one more dense product per step and saves poetx_saved_bytes(L, T) of
  * activations per layer. */
 POETX_API int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x,
                       const int32_t* perm_r, const int32_t* perm_p,
                       const void* g_r, const void* g_p,
-                      const void* wpt, const float* wscale_p,
+                      const void* wp, const float* wscale_p,
                       void* z, void* ws, size_t ws_bytes, hipStream_t stream);
 
 POETX_API int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const void* dz,
                        const int32_t* perm_r, const int32_t* perm_p,
                        const float* q_r, const float* q_p,
                        const void* g_r, const void* g_p,
-                       const void* wp, const void* wpt, const float* wscale_p,
+                       const void* wp, const float* wscale_p,
                        float* dq_r, float* dq_p, void* dx,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Merge (section "代码与部署", merge_if_needed): W0 <- R W0 P with the current
- * permutations and blocks, then q_r, q_p <- 0.
- *   wp: poetx_weight_prepare's wp (m x n) for the current W0 and
- *       permutations.
- *   w0 [m][n], w_dtype: overwritten with R W0 P (original frame).
- *   w_scale [n] float, int8 weights only (ignored otherwise, may be NULL):
- *       in, the per-column scales W0 is stored with; out, the new scales.
+ * permutations and blocks, then q_r, q_p <- 0, with the merged weight written
+ * straight into the frame of the permutations that follow the merge (the
+ * rotations restart from Q = 0, when the layer no longer depends on the
+ * permutations, and a training loop draws new ones).
+ *   wp [m][n], w_dtype, in-out: in, the permuted-frame weight of perm_r,
+ *       perm_p; out, Psi' R W0 P Phi'^T for Psi', Phi' of perm_r_next,
+ *       perm_p_next (which may be perm_r, perm_p themselves: no new frame).
+ *   wscale_p [n] float, int8 weights only, in-out: the column scales of wp.
  *       The merged weight is stored again the way W0 was (section "POET-XQ：
  *       量化训练的额外红利" stores the base weight quantized; how a merged
- *       weight is stored again is a reading): per output column c,
- *       scale[c] = max_r |W0'[r][c]| / 127 (1 for a zero column) and
- *       W0[r][c] = clamp(rint(W0'[r][c] / scale[c]), -127, 127), rounding half
- *       to even in float32. The merge itself runs in float for int8 weights.
- * The caller then resamples the permutations (the function no longer depends
- * on them once q = 0) and calls poetx_weight_prepare again. */
-POETX_API int poetx_merge(const poetx_layer* L, const void* wp,
+ *       weight is stored again is a reading): per column c, scale[c] =
+ *       max_r |W0'[r][c]| / 127 (1 for a zero column) and code =
+ *       clamp(rint(W0'[r][c] / scale[c]), -127, 127), rounding half to even
+ *       in float32. The merge itself runs in float for int8 weights.
+ *   next_ready: NULL, or an event the stream waits for (hipStreamWaitEvent)
+ *       after the block products and before perm_r_next / perm_p_next are
+ *       read, so that their draw can run on another stream beside the block
+ *       products. If that wait cannot be enqueued, POETX_EHIP is returned
+ *       with the block products launched but wp and q untouched.
+ *   g_r, g_p: the CNP block buffers of q_r, q_p.
+ * The caller then builds the CNP blocks of q = 0 and uses perm_r_next,
+ * perm_p_next from here on. */
+POETX_API int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p,
                 const int32_t* perm_r, const int32_t* perm_p,
-                const void* g_r, const void* g_p,
-                void* w0, float* w_scale, float* q_r, float* q_p,
+                const int32_t* perm_r_next, const int32_t* perm_p_next, hipEvent_t next_ready,
+                const void* g_r, const void* g_p, float* q_r, float* q_p,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Draw of a uniformly random permutation of [0, dim) for Psi or Phi. The

@@ -218,6 +218,15 @@ __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __rest
   POETX_GRID_STRIDE(i, n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
 }
 
+__global__ void k_compose_perm(const int32_t* __restrict__ inv0, const int32_t* __restrict__ next0,
+                               int32_t* __restrict__ out0, int64_t n0, const int32_t* __restrict__ inv1,
+                               const int32_t* __restrict__ next1, int32_t* __restrict__ out1, int64_t n1) {
+  POETX_GRID_STRIDE(i, n0 + n1) {
+    if (i < n0) out0[i] = inv0[clamp_index(next0[i], n0)];
+    else out1[i - n0] = inv1[clamp_index(next1[i - n0], n1)];
+  }
+}
+
 __global__ void k_gather_f32(const float* __restrict__ in, const int32_t* __restrict__ idx, float* __restrict__ out,
                              int64_t n) {
   POETX_GRID_STRIDE(i, n) out[i] = in[clamp_index(idx[i], n)];
@@ -790,6 +799,13 @@ bool gather_cols(const void* in, int64_t ld_in, const int32_t* rmap_in, void* ou
 
 void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_inverse_perm, dim3(grid1(n)), dim3(kThreads), 0, s, perm, inv, n);
+}
+
+void compose_perm(const int32_t* inv0, const int32_t* next0, int32_t* out0, int64_t n0, const int32_t* inv1,
+                  const int32_t* next1, int32_t* out1, int64_t n1, hipStream_t s) {
+  if (n0 + n1 > 0)
+    hipLaunchKernelGGL(k_compose_perm, dim3(grid1(n0 + n1)), dim3(kThreads), 0, s, inv0, next0, out0, n0, inv1, next1,
+                       out1, n1);
 }
 
 void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipStream_t s) {

@@ -1,6 +1,8 @@
 // Dense product C = A B^T (bfloat16 in, float32 accumulate, bfloat16 out) for
-// the layer's two W0 products: Y1 = X2 Wp (B = Wp^T rows) and dX2 = dY1 Wp^T
-// (B = Wp rows). Both operands are K-contiguous.
+// the layer's two W0 products, both on the one resident weight Wp (m x n,
+// row-major): Y1 = X2 Wp reads Wp as B[k][n] (N-contiguous rows, K = m) and
+// dX2 = dY1 Wp^T reads it as B[n][k] (K-contiguous rows, K = n). A is always
+// K-contiguous.
 //
 // gfx950 design:
 //  * 256 x 256 output tile per workgroup, K in steps of 64, 8 waves (two per
@@ -15,6 +17,15 @@
 //    c ^ swz(r) with swz(r) = (r & 7) ^ ((r >> 3) & 1), which keeps the
 //    fragment reads (32 rows, same chunk) free of bank conflicts whether the
 //    LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+//  * An N-contiguous B tile is stored as it lies in memory, 64 K rows of 256
+//    columns (512 bytes), with chunk c of row r in slot c ^ 4 (r % 4). Its
+//    MFMA fragments (8 consecutive k of one column per lane) come from pairs
+//    of ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives
+//    element j % 4 of the 8 bytes addressed by lane 4e + j / 4 (e = 0..3),
+//    so with lane i addressing row k0 + i / 4 at column n0 + 4 (i % 4), lane
+//    j gets rows k0 .. k0+3 of column n0 + j. The four rows a read touches
+//    then fall in four different 64-byte quarters of the 256-byte bank
+//    window, and the 32 columns of a fragment are 64 contiguous bytes.
 //  * Output tiles are ordered so that each XCD works on one contiguous band
 //    of tiles (shared A/B panels stay in that XCD's L2).
 //  * When the tiles do not fill a whole number of rounds over the 256 CUs,
@@ -103,6 +114,29 @@ __device__ __forceinline__ void load_one(const bf16_t* __restrict__ g, int64_t l
   __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t)(lds + rbase * kRowBytes), 16, 0, 0);
 }
 
+// N-contiguous B tile (BK rows of k, BN columns): instruction i of a wave
+// covers two 512-byte rows; lane l lands in slot l % 32 of row l / 32 and
+// fetches the chunk that belongs there. Columns past `collim` re-read the
+// last chunk of the row (in bounds); they only reach outputs never stored.
+constexpr int kNcRowBytes = BN * 2;                 // 512
+constexpr int kNcChunks = kNcRowBytes / 16;         // 32
+constexpr int kNcRowsPerInst = 64 / kNcChunks;      // 2
+static_assert(BK * kNcRowBytes == kTileBytes, "N-contiguous B tile size");
+
+__device__ __forceinline__ int swz_nc(int r) { return (r & 3) << 2; }
+
+__device__ __forceinline__ void load_one_nc(const bf16_t* __restrict__ g, int64_t ld, int col0, int collim, int k0,
+                                            char* lds, int wave, int lane, int i) {
+  const int sub = lane / kNcChunks, slot = lane % kNcChunks;
+  const int rbase = (wave * kInstPerTile + i) * kNcRowsPerInst;
+  const int r = rbase + sub;
+  const int c = slot ^ swz_nc(r);
+  int col = col0 + c * 8;
+  col = col < collim ? col : collim - 8;
+  const bf16_t* src = g + static_cast<int64_t>(k0 + r) * ld + col;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t)(lds + rbase * kNcRowBytes), 16, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -128,6 +162,8 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   tn = (pid % group) / gsz;
 }
 
+// BNC: B is N-contiguous (B[k * ldb + n]) instead of K-contiguous.
+template <bool BNC>
 __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n, DenseSplit sp) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
 
@@ -173,13 +209,36 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   for (int kk = 0; kk < BK / 16; ++kk) koff[kk] = lrow * kRowBytes + (((2 * kk + (lane >> 5)) ^ sw) << 4);
   const int abase = wm * WTM * kRowBytes;
   const int bbase = kTileBytes + wn * WTN * kRowBytes;
+  // N-contiguous B: transposed-read address of this lane in the stage for
+  // column tile j, first row of K group 0. Lane group G = lane / 16 takes
+  // columns 16 (G % 2) .. of the fragment and rows 8 (G / 2) ..; lane i of
+  // the group addresses row + i / 4, column + 4 (i % 4). Rows +4 (second half
+  // of a fragment) and +16 (next K group) keep the row's swizzle, so they are
+  // 2048 and 8192 bytes further.
+  uint32_t bnc_addr[TN];
+  if constexpr (BNC) {
+    const int grp = lane >> 4, li = lane & 15;
+    const int r = 8 * (grp >> 1) + (li >> 2);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = wn * WTN + j * 32 + 16 * (grp & 1) + 4 * (li & 3);
+      bnc_addr[j] = static_cast<uint32_t>(kTileBytes + r * kNcRowBytes + (((col >> 3) ^ swz_nc(r)) << 4) +
+                                          (col & 7) * 2);
+    }
+  }
 
   // prologue: stages 0 .. NSTAGE-2 in flight
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p) {
     if (p < nk) {
       load_tile(A, d.lda, m0, d.M, (kb + p) * BK, smem + p * kStageBytes, wave, lane);
-      load_tile(B, d.ldb, n0, d.N, (kb + p) * BK, smem + p * kStageBytes + kTileBytes, wave, lane);
+      if constexpr (BNC) {
+#pragma unroll
+        for (int i = 0; i < kInstPerTile; ++i)
+          load_one_nc(B, d.ldb, n0, d.N, (kb + p) * BK, smem + p * kStageBytes + kTileBytes, wave, lane, i);
+      } else {
+        load_tile(B, d.ldb, n0, d.N, (kb + p) * BK, smem + p * kStageBytes + kTileBytes, wave, lane);
+      }
     }
   }
 
@@ -204,17 +263,41 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
 #pragma unroll
       for (int u = 0; u < 2 * kInstPerTile / (BK / 16); ++u) {
         const int i = kk * (2 * kInstPerTile / (BK / 16)) + u;
-        load_one(i < kInstPerTile ? A : B, i < kInstPerTile ? d.lda : d.ldb, i < kInstPerTile ? m0 : n0,
-                 i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
-                 i % kInstPerTile);
+        if (BNC && i >= kInstPerTile)
+          load_one_nc(B, d.ldb, n0, d.N, kpf, nxt + kTileBytes, wave, lane, i % kInstPerTile);
+        else
+          load_one(i < kInstPerTile ? A : B, i < kInstPerTile ? d.lda : d.ldb, i < kInstPerTile ? m0 : n0,
+                   i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
+                   i % kInstPerTile);
       }
       bf16x8_t af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
+      if constexpr (BNC) {
+        // from inline asm that waits for its own results: through the
+        // compiler builtin each such read gets a vmcnt(0) in front of it while
+        // the direct loads are in flight, which would drain the prefetch
+        static_assert(TN == 2, "two column tiles per wave");
+        typedef unsigned long long u64;
+        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+        const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + kk * 16 * kNcRowBytes;
+        const uint32_t a0 = sb + bnc_addr[0], a1 = sb + bnc_addr[1];
+        u64 rb[4];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n ds_read_b64_tr_b16 %1, %4 offset:2048\n"
+            "ds_read_b64_tr_b16 %2, %5\n ds_read_b64_tr_b16 %3, %5 offset:2048\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3])
+            : "v"(a0), "v"(a1)
+            : "memory");
+        bfr[0] = __builtin_bit_cast(bf16x8_t, u64x2{rb[0], rb[1]});
+        bfr[1] = __builtin_bit_cast(bf16x8_t, u64x2{rb[2], rb[3]});
+      } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
+        for (int j = 0; j < TN; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -339,7 +422,7 @@ size_t gemm_dense_split_bytes(int M, int N, int K) {
   return align256(static_cast<size_t>(p.tiles - p.full) * p.k * BM * BN * sizeof(float));
 }
 
-bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s) {
+bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s, bool b_ncontig) {
   if (d.M <= 0 || d.N <= 0) return true;
   if (d.K % 64 != 0 || d.K <= 0 || d.N % 8 != 0) return false;
   const int tm = (d.M + BM - 1) / BM, tn = (d.N + BN - 1) / BN;
@@ -347,7 +430,10 @@ bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s) {
   if (!split_ws) p = SplitPlan{p.tiles, p.tiles, 1};
   const DenseSplit sp{static_cast<float*>(split_ws), p.full, p.k};
   const int tail = p.tiles - p.full;
-  hipLaunchKernelGGL(k_gemm_dense, dim3(p.full + tail * p.k), dim3(NT), 0, s, d, tm, tn, sp);
+  if (b_ncontig)
+    hipLaunchKernelGGL(k_gemm_dense<true>, dim3(p.full + tail * p.k), dim3(NT), 0, s, d, tm, tn, sp);
+  else
+    hipLaunchKernelGGL(k_gemm_dense<false>, dim3(p.full + tail * p.k), dim3(NT), 0, s, d, tm, tn, sp);
   if (tail > 0)
     hipLaunchKernelGGL(k_dense_split_sum, dim3(tail * (BM * BN / 8 / 256)), dim3(256), 0, s, d, tm, tn, sp);
   return true;

@@ -18,6 +18,11 @@ bool gather_cols(const void* in, int64_t ld_in, const int32_t* rmap_in, void* ou
 // inv[perm[i]] = i (perm entries clamped to [0, n)).
 void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t stream);
 
+// out0[i] = inv0[next0[i]] for i < n0 and out1[i] = inv1[next1[i]] for
+// i < n1, in one launch (next entries clamped to [0, n)).
+void compose_perm(const int32_t* inv0, const int32_t* next0, int32_t* out0, int64_t n0, const int32_t* inv1,
+                  const int32_t* next1, int32_t* out1, int64_t n1, hipStream_t stream);
+
 // out[i] = in[idx[i]] (float), idx clamped to [0, n).
 void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipStream_t stream);
 

@@ -15,7 +15,10 @@
 //             dX2 = dY1 Wp^T; dX1 = dX2 G^T; dG = sum_t X1^T dX2
 //             dX = dX1 scattered by perm_r; dq = skew-packed CNP adjoint of dG, dH
 // Because Wp already carries both permutations, the two dense products need
-// no gather at all.
+// no gather at all. Wp is the only copy of the base weight the library keeps:
+// the forward reads it N-contiguous, the backward K-contiguous, and a merge
+// writes the merged weight straight into the frame of the next permutations.
+// W0 in the original frame exists only on request (poetx_weight_export).
 #include "../../include/poetx.h"
 #include "common.hpp"
 #include "gemm.hpp"
@@ -213,7 +216,7 @@ FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.inv_p = c.take<int32_t>(L->n);
   const size_t sb = dense_split_bytes(L, T, L->n, L->m);
   w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
-  w.wdeq = i8_staging(L) ? c.take<uint16_t>(L->m * L->n) : nullptr;
+  w.wdeq = L->w_dtype == POETX_I8 ? c.take<uint16_t>(L->m * L->n) : nullptr;
   return w;
 }
 
@@ -262,11 +265,11 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
 
 struct MergeWs {
   void *C1, *C2;
-  int32_t* inv_p;
+  int32_t *inv_r, *inv_p;  // inverses of the current permutations
+  int32_t *rmap, *cmap;    // merged-weight row / column for each row / column of the next frame
   // int8 weights: the merge runs in float on a float copy of both CNP buffers
   float *gr32, *gp32;
   unsigned int* amax;
-  float* scale_p;  // scale of Wp's columns: w_scale[perm_p[c]]
 };
 
 MergeWs plan_merge(const poetx_layer* L, Carve& c) {
@@ -275,16 +278,17 @@ MergeWs plan_merge(const poetx_layer* L, Carve& c) {
   const int64_t es = i8 ? 4 : w_size(L);
   w.C1 = c.take<char>(L->m * L->n * es);
   w.C2 = c.take<char>(L->m * L->n * es);
+  w.inv_r = c.take<int32_t>(L->m);
   w.inv_p = c.take<int32_t>(L->n);
+  w.rmap = c.take<int32_t>(L->m);
+  w.cmap = c.take<int32_t>(L->n);
   w.gr32 = w.gp32 = nullptr;
   w.amax = nullptr;
-  w.scale_p = nullptr;
   if (i8) {
     const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
     w.gr32 = c.take<float>(2 * block_elems(R));
     w.gp32 = c.take<float>(2 * block_elems(P));
     w.amax = c.take<unsigned int>(L->n);
-    w.scale_p = c.take<float>(L->n);
   }
   return w;
 }
@@ -306,6 +310,7 @@ size_t ws_bytes_for(const poetx_layer* L, int64_t T, int op) {
   switch (op) {
     case POETX_OP_CNP_BUILD: return cnp_build_bytes(L);
     case POETX_OP_WEIGHT_PREPARE: return 0;
+    case POETX_OP_WEIGHT_EXPORT: return static_cast<size_t>(L->n) * sizeof(int32_t);
     case POETX_OP_FORWARD: plan_fwd(L, T, c); return c.off;
     case POETX_OP_BACKWARD: plan_bwd(L, T, c); return c.off;
     case POETX_OP_MERGE: plan_merge(L, c); return c.off;
@@ -394,10 +399,11 @@ bool dense_kernel_applies(const poetx_layer* L, int N, int K) {
 // run time (section "POET-XQ"): the codes are copied to bfloat16 (exact)
 // into the workspace right before each dense product, whose epilogue (or the
 // preceding apply, in the backward) applies the column scales. The stored
-// weight stays int8; the copy is transient scratch.
+// weight stays int8; the copy is transient scratch. The forward, which reads
+// Wp N-contiguous, always makes it; the backward does when the dense kernel
+// applies, and otherwise the general engine reads the codes itself.
 bool i8_staging(const poetx_layer* L) {
-  return L->w_dtype == POETX_I8 && dense_kernel_applies(L, static_cast<int>(L->n), static_cast<int>(L->m)) &&
-         dense_kernel_applies(L, static_cast<int>(L->m), static_cast<int>(L->n));
+  return L->w_dtype == POETX_I8 && dense_kernel_applies(L, static_cast<int>(L->m), static_cast<int>(L->n));
 }
 
 // Workspace of the dense kernel's split of a partial last round of tiles.
@@ -406,8 +412,12 @@ size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K) 
   return gemm_dense_split_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
 }
 
-bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, void* split_ws, hipStream_t st) {
-  if (!i8 && dense_kernel_applies(L, d.N, d.K)) return gemm_dense_bf16(d, split_ws, st);
+// b_ncontig: B is Wp itself read as [K][N] (the forward); otherwise B rows
+// are K-contiguous (the backward). i8: B holds int8 codes (K-contiguous only).
+bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, bool b_ncontig, void* split_ws,
+                   hipStream_t st) {
+  if (!i8 && dense_kernel_applies(L, d.N, d.K)) return gemm_dense_bf16(d, split_ws, st, b_ncontig);
+  if (b_ncontig) return !i8 && gemm(L, d, A_KCONTIG, B_NCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
   return gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
 }
 
@@ -665,7 +675,7 @@ int check_ws(const poetx_layer* L, int64_t T, int op, const void* ws, size_t ws_
 // or the workspace in the memory variant). `recompute` only renames the
 // profiled steps: the memory variant's backward runs the first three again.
 bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r, const int32_t* perm_p,
-                  const void* g_r, const void* g_p, const void* wpt, const float* wscale_p, void* z, void* X1,
+                  const void* g_r, const void* g_p, const void* wp, const float* wscale_p, void* z, void* X1,
                   void* Y1, const FwdWs& w, bool recompute, hipStream_t stream) {
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   const int es = act_size(L);
@@ -679,12 +689,13 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
     ProfScope p(recompute ? "recompute_apply_r" : "apply_r_fwd", stream);
     ok = ok && block_apply(L, R, T, X1, w.buf, g_r, 1, nullptr, stream);
   }
+  // Y1 = X2 Wp with Wp read as B[k][n] (N-contiguous)
   GemmDesc d;
   d.dense = 1;
   d.A = w.buf;
   d.lda = L->m;
-  d.B = wpt;
-  d.ldb = L->m;
+  d.B = wp;
+  d.ldb = L->n;
   d.C = Y1;
   d.ldc = L->n;
   d.scale = i8 ? wscale_p : nullptr;
@@ -693,12 +704,12 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   d.K = static_cast<int>(L->m);
   if (w.wdeq) {
     ProfScope p(recompute ? "recompute_dequant_w" : "dequant_w_fwd", stream);
-    ok = ok && i8_to_bf16(static_cast<const int8_t*>(wpt), static_cast<uint16_t*>(w.wdeq), L->m * L->n, stream);
+    ok = ok && i8_to_bf16(static_cast<const int8_t*>(wp), static_cast<uint16_t*>(w.wdeq), L->m * L->n, stream);
     d.B = w.wdeq;
   }
   {
     ProfScope p(recompute ? "recompute_gemm_dense" : "gemm_dense_fwd", stream);
-    ok = ok && dense_product(L, d, i8 && !w.wdeq, w.split, stream);
+    ok = ok && dense_product(L, d, false, true, w.split, stream);
   }
   if (!z) return ok;
   {
@@ -765,7 +776,7 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   }
   {
     ProfScope p("gemm_dense_bwd", stream);
-    ok = ok && dense_product(L, d, i8 && !w.wdeq, w.split, stream);
+    ok = ok && dense_product(L, d, i8 && !w.wdeq, false, w.split, stream);
   }
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {
@@ -932,35 +943,48 @@ int poetx_cnp_build(const poetx_layer* L, const float* q_r, const float* q_p, vo
 }
 
 int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_scale, const int32_t* perm_r,
-                         const int32_t* perm_p, void* wp, void* wpt, float* wscale_p, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+                         const int32_t* perm_p, void* wp, float* wscale_p, hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
-  if (!ptrs_ok({w0, perm_r, perm_p, wp, wpt})) return POETX_EINVAL;
+  if (!ptrs_ok({w0, perm_r, perm_p, wp})) return POETX_EINVAL;
   const bool i8 = L->w_dtype == POETX_I8;
-  if (i8 && (!w_scale || !wscale_p)) return POETX_EINVAL;
-  const int es = w_size(L);
+  if (i8 && !ptrs_ok({w_scale, wscale_p})) return POETX_EINVAL;
   clear_pending_error();
   {
     ProfScope p("prepare_permute", stream);
-    if (!gather_cols(w0, L->n, perm_r, wp, L->n, nullptr, perm_p, L->n, L->m, es, stream))
+    if (!gather_cols(w0, L->n, perm_r, wp, L->n, nullptr, perm_p, L->n, L->m, w_size(L), stream))
       return POETX_EUNSUPPORTED;
     if (i8) gather_f32(w_scale, perm_p, wscale_p, L->n, stream);
   }
+  return launch_status();
+}
+
+int poetx_weight_export(const poetx_layer* L, const void* wp, const float* wscale_p, const int32_t* perm_r,
+                        const int32_t* perm_p, void* w0, float* w_scale, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!layer_ok(L)) return POETX_EINVAL;
+  if (!ptrs_ok({wp, perm_r, perm_p, w0})) return POETX_EINVAL;
+  const bool i8 = L->w_dtype == POETX_I8;
+  if (i8 && !ptrs_ok({wscale_p, w_scale})) return POETX_EINVAL;
+  if (const int e = check_ws(L, 0, POETX_OP_WEIGHT_EXPORT, ws, ws_bytes)) return e;
+  clear_pending_error();
+  // W0[perm_r[i]][c] = Wp[i][inv_p[c]], w_scale[c] = wscale_p[inv_p[c]]
+  int32_t* inv_p = static_cast<int32_t*>(ws);
   {
-    ProfScope p("prepare_transpose", stream);
-    if (!transpose(wp, wpt, L->m, L->n, es, stream)) return POETX_EUNSUPPORTED;
+    ProfScope p("export_permute", stream);
+    inverse_perm(perm_p, inv_p, L->n, stream);
+    if (!gather_cols(wp, L->n, nullptr, w0, L->n, perm_r, inv_p, L->n, L->m, w_size(L), stream))
+      return POETX_EUNSUPPORTED;
+    if (i8) gather_f32(wscale_p, inv_p, w_scale, L->n, stream);
   }
   return launch_status();
 }
 
 int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r, const int32_t* perm_p,
-                  const void* g_r, const void* g_p, const void* wpt, const float* wscale_p, void* z, void* saved,
+                  const void* g_r, const void* g_p, const void* wp, const float* wscale_p, void* z, void* saved,
                   void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
-  if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z, saved})) return POETX_EINVAL;
+  if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wp, z, saved})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_FORWARD, ws, ws_bytes)) return e;
   clear_pending_error();
@@ -968,17 +992,17 @@ int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   const FwdWs w = plan_fwd(L, T, c);
   void* X1 = saved;
   void* Y1 = static_cast<char*>(saved) + T * L->m * act_size(L);
-  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, X1, Y1, w, false, stream))
+  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wp, wscale_p, z, X1, Y1, w, false, stream))
     return POETX_EUNSUPPORTED;
   return launch_status();
 }
 
 int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x, const int32_t* perm_r,
-                      const int32_t* perm_p, const void* g_r, const void* g_p, const void* wpt,
+                      const int32_t* perm_p, const void* g_r, const void* g_p, const void* wp,
                       const float* wscale_p, void* z, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
-  if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wpt, z})) return POETX_EINVAL;
+  if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wp, z})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_FORWARD_MEM, ws, ws_bytes)) return e;
   clear_pending_error();
@@ -986,7 +1010,7 @@ int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x, const int3
   char* X1 = c.take<char>(saved_region(L, T));
   char* Y1 = X1 + T * L->m * act_size(L);
   const FwdWs w = plan_fwd(L, T, c);
-  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, X1, Y1, w, false, stream))
+  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wp, wscale_p, z, X1, Y1, w, false, stream))
     return POETX_EUNSUPPORTED;
   return launch_status();
 }
@@ -1019,8 +1043,8 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
 
 int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const void* dz, const int32_t* perm_r,
                        const int32_t* perm_p, const float* q_r, const float* q_p, const void* g_r,
-                       const void* g_p, const void* wp, const void* wpt, const float* wscale_p, float* dq_r,
-                       float* dq_p, void* dx, void* ws, size_t ws_bytes, hipStream_t stream) {
+                       const void* g_p, const void* wp, const float* wscale_p, float* dq_r, float* dq_p, void* dx,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (!ptrs_ok({dq_r, dq_p})) return POETX_EINVAL;
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
@@ -1029,7 +1053,7 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
     fill_zero2_f32(dq_r, packed_len(R), dq_p, packed_len(P), stream);
     return launch_status();
   }
-  if (!ptrs_ok({x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt, dx})) return POETX_EINVAL;
+  if (!ptrs_ok({x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, dx})) return POETX_EINVAL;
   if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_BACKWARD_MEM, ws, ws_bytes)) return e;
   Carve c(ws);
@@ -1041,7 +1065,7 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
   const FwdWs fw = plan_fwd(L, T, f);
   const BwdWs w = plan_bwd(L, T, b);
   void* cnp_ws = static_cast<char*>(ws) + w.cnp_off;
-  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, nullptr, X1, Y1, fw, true, stream))
+  if (!forward_core(L, T, x, perm_r, perm_p, g_r, g_p, wp, wscale_p, nullptr, X1, Y1, fw, true, stream))
     return POETX_EUNSUPPORTED;
   if (!backward_core(L, T, X1, Y1, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wscale_p, dq_r, dq_p, dx, w,
                      cnp_ws, stream))
@@ -1049,30 +1073,48 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
   return launch_status();
 }
 
-int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, const int32_t* perm_p,
-                const void* g_r, const void* g_p, void* w0, float* w_scale, float* q_r, float* q_p, void* ws,
-                size_t ws_bytes, hipStream_t stream) {
+int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* perm_r, const int32_t* perm_p,
+                const int32_t* perm_r_next, const int32_t* perm_p_next, hipEvent_t next_ready, const void* g_r,
+                const void* g_p, float* q_r, float* q_p, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
-  if (!ptrs_ok({wp, perm_r, perm_p, g_r, g_p, w0, q_r, q_p})) return POETX_EINVAL;
+  if (!ptrs_ok({wp, perm_r, perm_p, perm_r_next, perm_p_next, g_r, g_p, q_r, q_p})) return POETX_EINVAL;
   const bool i8 = L->w_dtype == POETX_I8;
-  if (i8 && (!w_scale || !aligned16(w_scale))) return POETX_EINVAL;
+  if (i8 && !ptrs_ok({wscale_p})) return POETX_EINVAL;
   if (const int e = check_ws(L, 0, POETX_OP_MERGE, ws, ws_bytes)) return e;
   clear_pending_error();
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   Carve c(ws);
   MergeWs w = plan_merge(L, c);
+  // R W0 P = Psi^T Diag(G) Wp Diag(H) Phi with Wp = Psi W0 Phi^T. In the next
+  // frame (Psi', Phi') the merged weight is Psi' Psi^T M Phi Phi'^T with
+  // M = Diag(G) Wp Diag(H): row i of it is row inv_r[perm_r_next[i]] of M,
+  // column c is column inv_p[perm_p_next[c]].
+  int wait_status = POETX_OK;
+  auto reframe_maps = [&]() -> bool {
+    if (next_ready) {
+      const hipError_t e = hipStreamWaitEvent(stream, next_ready, 0);
+      if (e != hipSuccess) {
+        g_last_hip = e;
+        wait_status = POETX_EHIP;
+        return false;
+      }
+    }
+    inverse_perm(perm_r, w.inv_r, L->m, stream);
+    inverse_perm(perm_p, w.inv_p, L->n, stream);
+    compose_perm(w.inv_r, perm_r_next, w.rmap, L->m, w.inv_p, perm_p_next, w.cmap, L->n, stream);
+    return true;
+  };
+  bool ok;
   if (i8) {
-    // Dequantize Wp (its column c carries the scale of original column
-    // perm_p[c]), merge in float with float copies of the (G - I) planes,
-    // scatter to the original frame, store per column again.
+    // Dequantize Wp with its column scales, merge in float with float copies
+    // of the (G - I) planes, gather into the next frame, store per column
+    // again.
     poetx_layer Lf = *L;
     Lf.act_dtype = POETX_F32;
     Lf.w_dtype = POETX_F32;
-    bool ok;
     {
       ProfScope p("merge_dequant", stream);
-      gather_f32(w_scale, perm_p, w.scale_p, L->n, stream);
-      ok = dequant_i8_cols(static_cast<const int8_t*>(wp), w.scale_p, nullptr, static_cast<float*>(w.C1), L->m,
+      ok = dequant_i8_cols(static_cast<const int8_t*>(wp), wscale_p, nullptr, static_cast<float*>(w.C1), L->m,
                            L->n, stream);
       bf16_to_f32(static_cast<const uint16_t*>(g_r), w.gr32, 2 * block_elems(R), stream);
       bf16_to_f32(static_cast<const uint16_t*>(g_p), w.gp32, 2 * block_elems(P), stream);
@@ -1091,25 +1133,23 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
       ok = ok && block_apply(&Lf, P, L->m, w.C2, w.C1, w.gp32, 1, nullptr, stream);
     }
     {
-      ProfScope p("merge_scatter", stream);
-      inverse_perm(perm_p, w.inv_p, L->n, stream);
-      ok = ok && gather_cols(w.C1, L->n, nullptr, w.C2, L->n, perm_r, w.inv_p, L->n, L->m, 4, stream);
+      ProfScope p("merge_reframe", stream);
+      ok = ok && reframe_maps();
+      ok = ok && gather_cols(w.C1, L->n, w.rmap, w.C2, L->n, nullptr, w.cmap, L->n, L->m, 4, stream);
     }
     {
       ProfScope p("merge_requant", stream);
-      ok = ok && requant_i8_cols(static_cast<const float*>(w.C2), w.amax, static_cast<int8_t*>(w0), w_scale, L->m,
+      ok = ok && requant_i8_cols(static_cast<const float*>(w.C2), w.amax, static_cast<int8_t*>(wp), wscale_p, L->m,
                                  L->n, stream);
       fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
     }
+    if (wait_status) return wait_status;
     if (!ok) return POETX_EUNSUPPORTED;
     return launch_status();
   }
-  // R W0 P = Psi^T Diag(G) Wp Diag(H) Phi with Wp = Psi W0 Phi^T: the left
-  // block product on the rows of Wp, then Diag(H) on the right, then the
-  // scatter back to the original frame.
-  bool ok;
   void* M;  // Diag(G) Wp Diag(H), m x n
   if (is_bf16(L) && R.b == 256) {
+    // the left block product on the rows of Wp, then Diag(H) on the right
     {
       ProfScope p("merge_left", stream);
       ok = block_apply_left_bf16(static_cast<const uint16_t*>(wp), static_cast<uint16_t*>(w.C2), L->n,
@@ -1138,13 +1178,13 @@ int poetx_merge(const poetx_layer* L, const void* wp, const int32_t* perm_r, con
     }
     M = w.C2;
   }
-  // W0[perm_r[i]][perm_p[c]] = C[i][c]
   {
-    ProfScope p("merge_scatter", stream);
-    inverse_perm(perm_p, w.inv_p, L->n, stream);
-    ok = ok && gather_cols(M, L->n, nullptr, w0, L->n, perm_r, w.inv_p, L->n, L->m, w_size(L), stream);
+    ProfScope p("merge_reframe", stream);
+    ok = ok && reframe_maps();
+    ok = ok && gather_cols(M, L->n, w.rmap, wp, L->n, nullptr, w.cmap, L->n, L->m, w_size(L), stream);
     fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
   }
+  if (wait_status) return wait_status;
   if (!ok) return POETX_EUNSUPPORTED;
   return launch_status();
 }

@@ -1,11 +1,12 @@
 """Device-resident POET-X layer state driven through the C ABI.
 
-Holds the torch device buffers one layer needs (base weight, its permuted
-frame, packed parameters, permutations, CNP block buffers, saved activations
-and a workspace sized by poetx_workspace_bytes) and calls the ABI entry points
-in order, including the merge schedule a training loop runs (merge, new
-permutation draws, weight rebuild). It allocates, marshals and orders work on
-streams; all arithmetic runs in libpoetx.so.
+Holds the torch device buffers one layer needs (the permuted-frame base
+weight, the only copy of it the layer keeps; packed parameters; permutations;
+CNP block buffers; saved activations and a workspace sized by
+poetx_workspace_bytes) and calls the ABI entry points in order, including the
+merge schedule a training loop runs (new permutation draws beside the merge,
+which writes the merged weight straight into their frame). It allocates,
+marshals and orders work on streams; all arithmetic runs in libpoetx.so.
 """
 
 import numpy as np
@@ -48,10 +49,8 @@ class DeviceLayer:
             raise ValueError("invalid layer shape or dtypes for libpoetx")
         dev = device
         u8 = torch.uint8
-        self.w0 = torch.empty((m, n), dtype=_TORCH[weight], device=dev)
+        # Psi W0 Phi^T, and for an int8 weight the scales of its columns
         self.wp = torch.empty((m, n), dtype=_TORCH[weight], device=dev)
-        self.wpt = torch.empty((n, m), dtype=_TORCH[weight], device=dev)
-        self.w_scale = torch.ones(n, dtype=torch.float32, device=dev) if weight == "i8" else None
         self.wscale_p = torch.ones(n, dtype=torch.float32, device=dev) if weight == "i8" else None
         self.perm_r = torch.arange(m, dtype=torch.int32, device=dev)
         self.perm_p = torch.arange(n, dtype=torch.int32, device=dev)
@@ -62,9 +61,10 @@ class DeviceLayer:
         self.T_max = 0
         self.saved = None
         self.ws = torch.empty(0, dtype=u8, device=dev)
-        # merge cycle: second stream, spare permutations and the draws' own workspace
+        # merge cycle: second stream, spare permutations, the draws' own
+        # workspace and the event the merge waits for before reading them
         self._side = None
-        self._next_r = self._next_p = self._draw_ws = None
+        self._next_r = self._next_p = self._draw_ws = self._drawn = None
         self.reserve(T_max)
 
     # -- buffers --------------------------------------------------------------
@@ -75,19 +75,35 @@ class DeviceLayer:
         self.T_max = max(T, self.T_max)
         self.saved = torch.empty(max(px.poetx_saved_bytes(self.L, self.T_max), 16), dtype=torch.uint8,
                                  device=self.device)
-        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(8))
+        need = max(px.poetx_workspace_bytes(self.L, self.T_max, op) for op in range(9))
         if need > self.ws.numel():
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
 
-    def load(self, layer):
-        """Upload a layer dict from ``synth.make_layer``."""
-        self.w0.copy_(to_device(layer["W0_raw"], self.weight, self.device))
-        if self.weight == "i8":
-            self.w_scale.copy_(to_device(layer["w_scale"], "f32", self.device))
+    def load(self, layer, stream=None):
+        """Upload a layer dict from ``synth.make_layer``: permutations, packed
+        parameters, and W0 (original frame), which becomes the permuted-frame
+        weight; the original-frame copy is not kept."""
         self.perm_r.copy_(to_device(layer["perm_r"], "i32", self.device))
         self.perm_p.copy_(to_device(layer["perm_p"], "i32", self.device))
         self.q_r.copy_(to_device(layer["q_r"], "f32", self.device))
         self.q_p.copy_(to_device(layer["q_p"], "f32", self.device))
+        w0 = to_device(layer["W0_raw"], self.weight, self.device)
+        scale = to_device(layer["w_scale"], "f32", self.device) if self.weight == "i8" else None
+        self.set_weight(w0, scale, stream)
+
+    def set_weight(self, w0, w_scale=None, stream=None):
+        """Permuted-frame weight from W0 [m][n] in the original frame (and its
+        column scales for an int8 weight), for the current permutations."""
+        px.poetx_weight_prepare(self.L, w0, w_scale, self.perm_r, self.perm_p, self.wp, self.wscale_p, stream)
+
+    def export_w0(self, stream=None):
+        """W0 in the original frame (and, for an int8 weight, its column
+        scales), e.g. for a checkpoint. Returns (w0, w_scale or None)."""
+        w0 = torch.empty((self.m, self.n), dtype=_TORCH[self.weight], device=self.device)
+        scale = torch.empty(self.n, dtype=torch.float32, device=self.device) if self.weight == "i8" else None
+        px.poetx_weight_export(self.L, self.wp, self.wscale_p, self.perm_r, self.perm_p, w0, scale, self.ws, None,
+                               stream)
+        return w0, scale
 
     def act_tensor(self, rows, cols):
         return torch.empty((rows, cols), dtype=_TORCH[self.act], device=self.device)
@@ -107,16 +123,12 @@ class DeviceLayer:
     def cnp_build(self, stream=None):
         px.poetx_cnp_build(self.L, self.q_r, self.q_p, self.g_r, self.g_p, self.ws, None, stream)
 
-    def prepare(self, stream=None):
-        px.poetx_weight_prepare(self.L, self.w0, self.w_scale, self.perm_r, self.perm_p, self.wp, self.wpt,
-                                self.wscale_p, self.ws, None, stream)
-
     def forward(self, x, z=None, stream=None):
         T = x.shape[0]
         self.reserve(T)
         if z is None:
             z = self.act_tensor(T, self.n)
-        px.poetx_forward(self.L, T, x, self.perm_r, self.perm_p, self.g_r, self.g_p, self.wpt, self.wscale_p,
+        px.poetx_forward(self.L, T, x, self.perm_r, self.perm_p, self.g_r, self.g_p, self.wp, self.wscale_p,
                          z, self.saved, self.ws, None, stream)
         return z
 
@@ -138,7 +150,7 @@ class DeviceLayer:
         self.reserve(T)
         if z is None:
             z = self.act_tensor(T, self.n)
-        px.poetx_forward_mem(self.L, T, x, self.perm_r, self.perm_p, self.g_r, self.g_p, self.wpt,
+        px.poetx_forward_mem(self.L, T, x, self.perm_r, self.perm_p, self.g_r, self.g_p, self.wp,
                              self.wscale_p, z, self.ws, None, stream)
         return z
 
@@ -153,26 +165,28 @@ class DeviceLayer:
         if dx is None:
             dx = self.act_tensor(T, self.m)
         px.poetx_backward_mem(self.L, T, x, dz, self.perm_r, self.perm_p, self.q_r, self.q_p, self.g_r,
-                              self.g_p, self.wp, self.wpt, self.wscale_p, dq_r, dq_p, dx, self.ws, None, stream)
+                              self.g_p, self.wp, self.wscale_p, dq_r, dq_p, dx, self.ws, None, stream)
         return dq_r, dq_p, dx
 
-    def merge(self, stream=None):
-        px.poetx_merge(self.L, self.wp, self.perm_r, self.perm_p, self.g_r, self.g_p, self.w0,
-                       self.w_scale if self.weight == "i8" else None, self.q_r, self.q_p, self.ws, None, stream)
-
-    def resample(self, seed, tag, draw, stream=None):
-        """Draw both permutations again: draw ``draw`` of Psi under tag 2*tag
-        and of Phi under tag 2*tag + 1 (``tag`` names the layer)."""
-        px.poetx_sample_perm(self.m, seed, 2 * tag, draw, self.perm_r, self.ws, None, stream)
-        px.poetx_sample_perm(self.n, seed, 2 * tag + 1, draw, self.perm_p, self.ws, None, stream)
+    def merge(self, perm_r_next=None, perm_p_next=None, next_ready=None, stream=None):
+        """W0 <- R W0 P with q <- 0. With new permutations (device int32
+        tensors, drawn before the call or, with ``next_ready``, on another
+        stream up to that recorded event) the merged weight lands in their
+        frame and they become the layer's permutations; without, the frame
+        stays."""
+        nr = self.perm_r if perm_r_next is None else perm_r_next
+        np_ = self.perm_p if perm_p_next is None else perm_p_next
+        px.poetx_merge(self.L, self.wp, self.wscale_p, self.perm_r, self.perm_p, nr, np_, next_ready, self.g_r,
+                       self.g_p, self.q_r, self.q_p, self.ws, None, stream)
+        self.perm_r, self.perm_p = nr, np_
 
     def merge_cycle(self, seed, tag, draw, stream=None):
-        """W0 <- R W0 P with q <- 0, draw ``draw`` of both permutations, and
-        the permuted-frame weight rebuilt for them. The draws do not depend on
-        the merge, so they run on a second stream (default priority) into
-        spare permutation buffers, with a small workspace of their own, while
-        the merge runs; the stream joins them before the rebuild, and the
-        buffers swap."""
+        """Draw ``draw`` of both permutations (Psi under tag 2*tag, Phi under
+        2*tag + 1; ``tag`` names the layer), then W0 <- R W0 P with q <- 0
+        written into their frame. The draws do not depend on the merge, so
+        they run on a second stream (default priority) into spare buffers
+        while the merge's block products run; the merge waits for them only
+        before its final gather, and the old permutations become the spares."""
         main = stream if stream is not None else torch.cuda.current_stream(self.device)
         if self._side is None:
             self._side = torch.cuda.Stream(device=self.device)
@@ -180,22 +194,21 @@ class DeviceLayer:
             self._next_p = torch.empty_like(self.perm_p)
             need = px.poetx_workspace_bytes(self.L, 0, px.POETX_OP_SAMPLE_PERM)
             self._draw_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+            self._drawn = torch.cuda.Event()
         # the spare buffers' earlier readers are on the main stream
         self._side.wait_stream(main)
         px.poetx_sample_perm(self.m, seed, 2 * tag, draw, self._next_r, self._draw_ws, None, self._side)
         px.poetx_sample_perm(self.n, seed, 2 * tag + 1, draw, self._next_p, self._draw_ws, None, self._side)
-        self.merge(main)
-        main.wait_stream(self._side)
-        self.perm_r, self._next_r = self._next_r, self.perm_r
-        self.perm_p, self._next_p = self._next_p, self.perm_p
-        self.prepare(main)
+        self._drawn.record(self._side)
+        old_r, old_p = self.perm_r, self.perm_p
+        self.merge(self._next_r, self._next_p, self._drawn, main)
+        self._next_r, self._next_p = old_r, old_p
 
     def merge_if_needed(self, step, interval, seed, tag, stream=None):
         """Called after optimizer step ``step`` (counted from 0). After every
-        ``interval``-th update: CNP blocks of the current q, W0 <- R W0 P with
-        q <- 0, draw k = (step + 1) / interval of both permutations, and the
-        permuted-frame weight and CNP blocks rebuilt for them. Returns whether
-        it merged."""
+        ``interval``-th update: CNP blocks of the current q, draw k = (step +
+        1) / interval of both permutations, W0 <- R W0 P with q <- 0 in their
+        frame, and the CNP blocks of q = 0. Returns whether it merged."""
         if (step + 1) % interval:
             return False
         self.cnp_build(stream)

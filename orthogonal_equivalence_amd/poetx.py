@@ -27,12 +27,13 @@ POETX_OK, POETX_EINVAL, POETX_EUNSUPPORTED, POETX_EHIP, POETX_EWORKSPACE = 0, 1,
 POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
 POETX_SIDE_R, POETX_SIDE_P = 0, 1
 (POETX_OP_CNP_BUILD, POETX_OP_WEIGHT_PREPARE, POETX_OP_FORWARD, POETX_OP_BACKWARD,
- POETX_OP_MERGE, POETX_OP_FORWARD_MEM, POETX_OP_BACKWARD_MEM, POETX_OP_SAMPLE_PERM) = range(8)
+ POETX_OP_MERGE, POETX_OP_FORWARD_MEM, POETX_OP_BACKWARD_MEM, POETX_OP_SAMPLE_PERM,
+ POETX_OP_WEIGHT_EXPORT) = range(9)
 
 EXPORTED = [
     "poetx_abi_version", "poetx_strerror", "poetx_last_hip_error", "poetx_packed_len", "poetx_gbuf_bytes",
     "poetx_saved_bytes", "poetx_wbuf_bytes", "poetx_workspace_bytes", "poetx_cnp_build",
-    "poetx_weight_prepare", "poetx_forward", "poetx_backward", "poetx_forward_mem", "poetx_backward_mem",
+    "poetx_weight_prepare", "poetx_weight_export", "poetx_forward", "poetx_backward", "poetx_forward_mem", "poetx_backward_mem",
     "poetx_merge", "poetx_sample_perm", "poetx_sample_perm_static",
     "poetx_profile_enable", "poetx_profile_count", "poetx_profile_get",
 ]
@@ -73,14 +74,15 @@ _sig = {
     "poetx_wbuf_bytes": (_SZ, [_L]),
     "poetx_workspace_bytes": (_SZ, [_L, _I64, ctypes.c_int]),
     "poetx_cnp_build": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _SZ, _P]),
-    "poetx_weight_prepare": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "poetx_weight_prepare": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P]),
+    "poetx_weight_export": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_forward": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_backward": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _SZ, _P]),
     "poetx_forward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_backward_mem": (ctypes.c_int, [_L, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                          _P, _P, _P, _SZ, _P]),
-    "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                          _P, _P, _SZ, _P]),
+    "poetx_merge": (ctypes.c_int, [_L, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "poetx_sample_perm": (ctypes.c_int, [_I64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P, _P, _SZ,
                                          _P]),
     "poetx_sample_perm_static": (ctypes.c_int, [_I64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, _P,
@@ -163,16 +165,20 @@ def poetx_cnp_build(L, q_r, q_p, g_r, g_p, ws=None, ws_bytes=None, stream=None):
           _size(ws, ws_bytes), _stream(stream))
 
 
-def poetx_weight_prepare(L, w0, w_scale, perm_r, perm_p, wp, wpt, wscale_p, ws=None, ws_bytes=None,
-                         stream=None):
+def poetx_weight_prepare(L, w0, w_scale, perm_r, perm_p, wp, wscale_p, stream=None):
     _call("poetx_weight_prepare", ctypes.byref(L), _ptr(w0), _ptr(w_scale), _ptr(perm_r), _ptr(perm_p),
-          _ptr(wp), _ptr(wpt), _ptr(wscale_p), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+          _ptr(wp), _ptr(wscale_p), _stream(stream))
 
 
-def poetx_forward(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, saved, ws=None, ws_bytes=None,
+def poetx_weight_export(L, wp, wscale_p, perm_r, perm_p, w0, w_scale, ws=None, ws_bytes=None, stream=None):
+    _call("poetx_weight_export", ctypes.byref(L), _ptr(wp), _ptr(wscale_p), _ptr(perm_r), _ptr(perm_p),
+          _ptr(w0), _ptr(w_scale), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+
+
+def poetx_forward(L, T, x, perm_r, perm_p, g_r, g_p, wp, wscale_p, z, saved, ws=None, ws_bytes=None,
                   stream=None):
     _call("poetx_forward", ctypes.byref(L), T, _ptr(x), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
-          _ptr(wpt), _ptr(wscale_p), _ptr(z), _ptr(saved), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+          _ptr(wp), _ptr(wscale_p), _ptr(z), _ptr(saved), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
 def poetx_backward(L, T, saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wscale_p, dq_r, dq_p, dx,
@@ -182,22 +188,32 @@ def poetx_backward(L, T, saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wsca
           _ptr(dx), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
-def poetx_forward_mem(L, T, x, perm_r, perm_p, g_r, g_p, wpt, wscale_p, z, ws=None, ws_bytes=None,
+def poetx_forward_mem(L, T, x, perm_r, perm_p, g_r, g_p, wp, wscale_p, z, ws=None, ws_bytes=None,
                       stream=None):
     _call("poetx_forward_mem", ctypes.byref(L), T, _ptr(x), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
-          _ptr(wpt), _ptr(wscale_p), _ptr(z), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+          _ptr(wp), _ptr(wscale_p), _ptr(z), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
-def poetx_backward_mem(L, T, x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wpt, wscale_p, dq_r, dq_p, dx,
+def poetx_backward_mem(L, T, x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, wscale_p, dq_r, dq_p, dx,
                        ws=None, ws_bytes=None, stream=None):
     _call("poetx_backward_mem", ctypes.byref(L), T, _ptr(x), _ptr(dz), _ptr(perm_r), _ptr(perm_p),
-          _ptr(q_r), _ptr(q_p), _ptr(g_r), _ptr(g_p), _ptr(wp), _ptr(wpt), _ptr(wscale_p), _ptr(dq_r),
+          _ptr(q_r), _ptr(q_p), _ptr(g_r), _ptr(g_p), _ptr(wp), _ptr(wscale_p), _ptr(dq_r),
           _ptr(dq_p), _ptr(dx), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
-def poetx_merge(L, wp, perm_r, perm_p, g_r, g_p, w0, w_scale, q_r, q_p, ws=None, ws_bytes=None, stream=None):
-    _call("poetx_merge", ctypes.byref(L), _ptr(wp), _ptr(perm_r), _ptr(perm_p), _ptr(g_r), _ptr(g_p),
-          _ptr(w0), _ptr(w_scale), _ptr(q_r), _ptr(q_p), _ptr(ws), _size(ws, ws_bytes), _stream(stream))
+def _event(e):
+    if e is None or isinstance(e, int):
+        return e
+    return e.cuda_event
+
+
+def poetx_merge(L, wp, wscale_p, perm_r, perm_p, perm_r_next, perm_p_next, next_ready, g_r, g_p, q_r, q_p,
+                ws=None, ws_bytes=None, stream=None):
+    """next_ready: None, a raw hipEvent_t handle, or a torch.cuda.Event
+    (recorded before the call)."""
+    _call("poetx_merge", ctypes.byref(L), _ptr(wp), _ptr(wscale_p), _ptr(perm_r), _ptr(perm_p),
+          _ptr(perm_r_next), _ptr(perm_p_next), _event(next_ready), _ptr(g_r), _ptr(g_p), _ptr(q_r), _ptr(q_p),
+          _ptr(ws), _size(ws, ws_bytes), _stream(stream))
 
 
 def poetx_sample_perm(dim, seed, tag, draw, perm, ws=None, ws_bytes=None, stream=None):

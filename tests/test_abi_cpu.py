@@ -28,7 +28,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = ctypes.CDLL(px.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -44,7 +44,7 @@ def test_profile_log_host_side():
 
 
 def test_version_and_messages():
-    assert px.poetx_abi_version() == 1
+    assert px.poetx_abi_version() == 2
     for s in range(5):
         assert px.poetx_strerror(s)
     assert px.poetx_strerror(99) == "unknown status"
@@ -107,7 +107,7 @@ def test_size_limits_at_their_edges():
     for call in (lambda T: px.poetx_forward(L, T, *([FAKE] * 9), FAKE, 1 << 62, stream=0),
                  lambda T: px.poetx_backward(L, T, *([FAKE] * 13), FAKE, 1 << 62, stream=0),
                  lambda T: px.poetx_forward_mem(L, T, *([FAKE] * 8), FAKE, 1 << 62, stream=0),
-                 lambda T: px.poetx_backward_mem(L, T, *([FAKE] * 14), FAKE, 1 << 62, stream=0)):
+                 lambda T: px.poetx_backward_mem(L, T, *([FAKE] * 13), FAKE, 1 << 62, stream=0)):
         with pytest.raises(px.PoetxError) as e:
             call((1 << 30) + 1)
         assert e.value.status == px.POETX_EINVAL
@@ -151,27 +151,47 @@ def test_argument_errors_before_any_launch():
         px.poetx_forward_mem(L, 32, *([FAKE] * 8), FAKE, ws_fm - 1, stream=0)
     assert e.value.status == px.POETX_EWORKSPACE
     with pytest.raises(px.PoetxError) as e:
-        px.poetx_backward_mem(L, 32, *([FAKE] * 14), FAKE, ws_bm - 1, stream=0)
+        px.poetx_backward_mem(L, 32, *([FAKE] * 13), FAKE, ws_bm - 1, stream=0)
     assert e.value.status == px.POETX_EWORKSPACE
     with pytest.raises(px.PoetxError) as e:
-        px.poetx_backward_mem(L, 32, None, *([FAKE] * 13), FAKE, ws_bm, stream=0)
+        px.poetx_backward_mem(L, 32, None, *([FAKE] * 12), FAKE, ws_bm, stream=0)
     assert e.value.status == px.POETX_EINVAL
     px.poetx_forward_mem(L, 0, *([None] * 8), None, 0, stream=0)
     # cnp build: q without g
     with pytest.raises(px.PoetxError) as e:
         px.poetx_cnp_build(L, FAKE, None, None, None, FAKE, 1 << 30, stream=0)
     assert e.value.status == px.POETX_EINVAL
-    # merge of an int8 weight needs its scales (in and out)
+    # merge: every pointer but the event is required; an int8 weight needs
+    # its scales (in and out)
+    ws_mb = px.poetx_workspace_bytes(L, 0, px.POETX_OP_MERGE)
+    margs = [FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE]
+    for i in (0, 2, 3, 4, 5, 7, 8, 9, 10):
+        a = list(margs)
+        a[i] = None
+        with pytest.raises(px.PoetxError) as e:
+            px.poetx_merge(L, *a, FAKE, ws_mb, stream=0)
+        assert e.value.status == px.POETX_EINVAL, i
+    with pytest.raises(px.PoetxError) as e:
+        px.poetx_merge(L, *margs, FAKE, ws_mb - 1, stream=0)
+    assert e.value.status == px.POETX_EWORKSPACE
     Lq = px.make_layer(64, 64, 16, 16, "bf16", "i8")
     ws_m = px.poetx_workspace_bytes(Lq, 0, px.POETX_OP_MERGE)
     assert ws_m >= 2 * 64 * 64 * 4
     with pytest.raises(px.PoetxError) as e:
-        px.poetx_merge(Lq, *([FAKE] * 6), None, FAKE, FAKE, FAKE, ws_m, stream=0)
+        px.poetx_merge(Lq, *margs, FAKE, ws_m, stream=0)
     assert e.value.status == px.POETX_EINVAL
     # int8 weights need their scales
     with pytest.raises(px.PoetxError) as e:
-        px.poetx_weight_prepare(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+        px.poetx_weight_prepare(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == px.POETX_EINVAL
+    with pytest.raises(px.PoetxError) as e:
+        px.poetx_weight_export(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == px.POETX_EINVAL
+    # export needs n int32 of workspace
+    assert px.poetx_workspace_bytes(L, 0, px.POETX_OP_WEIGHT_EXPORT) == 64 * 4
+    with pytest.raises(px.PoetxError) as e:
+        px.poetx_weight_export(L, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 64 * 4 - 1, stream=0)
+    assert e.value.status == px.POETX_EWORKSPACE
 
 
 def test_sample_perm_argument_errors():

@@ -35,7 +35,6 @@ def _setup(cfg):
     A = synth.make_activations(cfg, 0)
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
     dl.load(L)
-    dl.prepare()
     torch.cuda.synchronize()
     return dl, to_device(A["X_raw"], cfg.act), to_device(A["dZ_raw"], cfg.act)
 

@@ -1,5 +1,6 @@
 """The layer step captured in a HIP graph (through torch.cuda.CUDAGraph) and
-replayed: CNP build, forward, backward, merge and weight prepare.
+replayed: CNP build, forward, backward, draws of the next permutations and the
+merge into their frame.
 
 Every replay starts from the same layer state as an eager reference step and
 must reproduce its outputs bit for bit. Eager steps and synchronisations run
@@ -12,6 +13,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
+from orthogonal_equivalence_amd import poetx as px  # noqa: E402
 from orthogonal_equivalence_amd import synth  # noqa: E402
 from orthogonal_equivalence_amd.device import DeviceLayer, to_device  # noqa: E402
 
@@ -35,24 +37,31 @@ def test_graph_replays_match_the_eager_step():
     dx = dl.act_tensor(cfg.T, cfg.m)
     dq_r = torch.empty_like(dl.q_r)
     dq_p = torch.empty_like(dl.q_p)
-    dl.prepare()
-    w0_0, qr_0, qp_0 = dl.w0.clone(), dl.q_r.clone(), dl.q_p.clone()
+    wp_0, qr_0, qp_0 = dl.wp.clone(), dl.q_r.clone(), dl.q_p.clone()
+    cur_r, cur_p = dl.perm_r, dl.perm_p
+    pr_0, pp_0 = cur_r.clone(), cur_p.clone()
+    next_r, next_p = torch.empty_like(cur_r), torch.empty_like(cur_p)
+    draw_ws = torch.empty(8 * max(cfg.m, cfg.n), dtype=torch.uint8, device="cuda")
 
     def reset():
-        dl.w0.copy_(w0_0)
+        dl.wp.copy_(wp_0)
         dl.q_r.copy_(qr_0)
         dl.q_p.copy_(qp_0)
-        dl.prepare()
+        cur_r.copy_(pr_0)
+        cur_p.copy_(pp_0)
+        dl.perm_r, dl.perm_p = cur_r, cur_p
 
     def step(stream=None):
         dl.cnp_build(stream)
         dl.forward(x, z, stream)
         dl.backward(dz, dq_r, dq_p, dx, stream)
-        dl.merge(stream)
-        dl.prepare(stream)
+        px.poetx_sample_perm(cfg.m, 7, 0, 1, next_r, draw_ws, None, stream)
+        px.poetx_sample_perm(cfg.n, 7, 1, 1, next_p, draw_ws, None, stream)
+        dl.merge(next_r, next_p, None, stream)
+        dl.cnp_build(stream)
 
     def outputs():
-        return [t.clone() for t in (z, dx, dq_r, dq_p, dl.w0, dl.wp, dl.wpt, dl.q_r, dl.q_p)]
+        return [t.clone() for t in (z, dx, dq_r, dq_p, dl.wp, next_r, next_p, dl.q_r, dl.q_p, dl.g_r, dl.g_p)]
 
     reset()
     step()
@@ -79,7 +88,7 @@ def test_graph_replays_match_the_eager_step():
         g.replay()
         torch.cuda.synchronize()
         got = outputs()
-        names = ("z", "dx", "dq_r", "dq_p", "w0", "wp", "wpt", "q_r", "q_p")
+        names = ("z", "dx", "dq_r", "dq_p", "wp", "perm_r", "perm_p", "q_r", "q_p", "g_r", "g_p")
         bad = [nm for nm, a, b in zip(names, got, ref) if not torch.equal(a.view(torch.uint8), b.view(torch.uint8))]
         print(f"replay {rep}: {'bit-identical' if not bad else bad}", flush=True)
         assert not bad, (rep, bad)

@@ -75,14 +75,13 @@ def test_large_rotation_parity(cfg, strength):
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
     dl.load(L)
     dl.cnp_build()
-    dl.prepare()
     z = dl.forward(to_device(A["X_raw"], cfg.act))
     dq_r, dq_p, dx = dl.backward(to_device(A["dZ_raw"], cfg.act))
     got = dict(z=to_host_f64(z), dq_r=to_host_f64(dq_r), dq_p=to_host_f64(dq_p), dx=to_host_f64(dx),
                g_r=to_host_f64(dl.g_planes(px.POETX_SIDE_R)), g_p=to_host_f64(dl.g_planes(px.POETX_SIDE_P)))
     if merge:
         dl.merge()
-        got["w0"] = to_host_f64(dl.w0)
+        got["w0"] = to_host_f64(dl.export_w0()[0])
     torch.cuda.synchronize()
 
     W0 = O.dequantize(L["W0_raw"], L["w_scale"]) if cfg.weight == "i8" else L["W0"].astype(np.float64)

@@ -87,7 +87,6 @@ def test_large_batches_sampled(cfg):
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, T)
     dl.load(L)
     dl.cnp_build()
-    dl.prepare()
     x = to_device(A["X_raw"], cfg.act)
     z = dl.forward(x)
     rows_d = torch.from_numpy(rows).cuda()
@@ -127,14 +126,14 @@ def test_tall_int8_weight_with_identity_rotations():
     dl.q_r.zero_()
     dl.q_p.zero_()
     dl.cnp_build()
-    dl.prepare()
     z = to_host_f64(dl.forward(to_device(A["X_raw"], cfg.act)))
     _, _, dx = dl.backward(to_device(A["dZ_raw"], cfg.act))
     dx = to_host_f64(dx)
     dl.merge()
+    w0, w_scale = dl.export_w0()
     torch.cuda.synchronize()
-    codes = dl.w0.cpu().numpy().view(np.int8).reshape(cfg.m, cfg.n)
-    scale = dl.w_scale.cpu().numpy().astype(np.float32)
+    codes = w0.cpu().numpy().view(np.int8).reshape(cfg.m, cfg.n)
+    scale = w_scale.cpu().numpy().astype(np.float32)
 
     W0 = _w0_values(cfg, L)
     X = A["X"].astype(np.float64)

@@ -61,7 +61,6 @@ def test_memory_variant_equals_saving_variant(cfg):
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
     dl.load(L)
     dl.cnp_build()
-    dl.prepare()
     x = to_device(A["X_raw"], cfg.act)
     dz = to_device(A["dZ_raw"], cfg.act)
     z = dl.forward(x)
@@ -83,7 +82,6 @@ def test_memory_variant_against_the_oracle():
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
     dl.load(L)
     dl.cnp_build()
-    dl.prepare()
     x = to_device(A["X_raw"], cfg.act)
     dz = to_device(A["dZ_raw"], cfg.act)
     z = to_host_f64(dl.forward_mem(x))

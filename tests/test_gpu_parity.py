@@ -54,7 +54,6 @@ def _run(cfg, seed=0, merge=False):
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
     dl.load(L)
     dl.cnp_build()
-    dl.prepare()
     x = to_device(A["X_raw"], cfg.act)
     dz = to_device(A["dZ_raw"], cfg.act)
     z = dl.forward(x)
@@ -64,8 +63,14 @@ def _run(cfg, seed=0, merge=False):
                x1=to_host_f64(x1), y1=to_host_f64(y1),
                g_r=to_host_f64(dl.g_planes(px.POETX_SIDE_R)), g_p=to_host_f64(dl.g_planes(px.POETX_SIDE_P)))
     if merge:
-        dl.merge()
-        out["w0_merged"] = to_host_f64(dl.w0)
+        # merged into the frame of freshly drawn permutations, as a training
+        # loop does; W0 in the original frame is exported for the comparison
+        rng = np.random.default_rng([seed, cfg.cfg_id, 99])
+        nr, np_ = rng.permutation(cfg.m).astype(np.int32), rng.permutation(cfg.n).astype(np.int32)
+        dl.merge(to_device(nr, "i32"), to_device(np_, "i32"))
+        out["w0_merged"] = to_host_f64(dl.export_w0()[0])
+        out["wp_merged"] = to_host_f64(dl.wp)
+        out["perm_next"] = (nr, np_)
         out["q_after"] = to_host_f64(torch.cat([dl.q_r, dl.q_p]))
     torch.cuda.synchronize()
     return L, A, out, dl
@@ -161,6 +166,8 @@ def test_layer_parity(cfg):
     if "w0_merged" in out:
         errs["merge"] = rel(out["w0_merged"], O.merge(*args))
         assert np.all(out["q_after"] == 0.0)
+        # the resident weight is the merged one in the next frame, exactly
+        assert np.array_equal(out["wp_merged"], O.permuted_weight(out["w0_merged"], *out["perm_next"]))
     print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
@@ -174,7 +181,6 @@ def test_merge_preserves_the_layer_function():
     # after the merge q = 0 and the forward through the merged weight must
     # reproduce the forward before it
     dl.cnp_build()
-    dl.prepare()
     z2 = to_host_f64(dl.forward(to_device(A["X_raw"], cfg.act)))
     torch.cuda.synchronize()
     assert rel(z2, out["z"]) <= 1e-5
@@ -186,14 +192,10 @@ def test_merge_preserves_the_layer_function():
 ], ids=lambda c: c.name)
 def test_merge_then_new_permutations_keep_the_function(cfg):
     # after a merge q = 0, so the layer no longer depends on its permutations:
-    # fresh ones (as the caller draws at a merge) and a rebuilt weight must
-    # give the forward from before the merge
+    # the weight merged into the frame of fresh ones (as drawn at a merge)
+    # must give the forward from before the merge
     L, A, out, dl = _run(cfg, merge=True)
-    rng = np.random.default_rng(11)
-    dl.perm_r.copy_(to_device(rng.permutation(cfg.m).astype(np.int32), "i32"))
-    dl.perm_p.copy_(to_device(rng.permutation(cfg.n).astype(np.int32), "i32"))
     dl.cnp_build()
-    dl.prepare()
     z2 = to_host_f64(dl.forward(to_device(A["X_raw"], cfg.act)))
     torch.cuda.synchronize()
     err = rel(z2, out["z"])
@@ -209,7 +211,8 @@ def test_merge_then_new_permutations_keep_the_function(cfg):
 ], ids=lambda c: c.name)
 def test_merge_with_zero_q_leaves_w0_unchanged(cfg):
     # q = 0 makes every G and H the identity, so R W0 P = W0 exactly; both
-    # roundings to bfloat16 then return the stored values bit for bit
+    # roundings to bfloat16 then return the stored values bit for bit, in the
+    # same frame and, after a merge into new permutations, in theirs
     print(f"\n[gpu] {cfg.name} m={cfg.m} n={cfg.n} b={cfg.b_r}/{cfg.b_p}", flush=True)
     L = synth.make_layer(cfg, 0)
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
@@ -217,11 +220,16 @@ def test_merge_with_zero_q_leaves_w0_unchanged(cfg):
     dl.q_r.zero_()
     dl.q_p.zero_()
     dl.cnp_build()
-    dl.prepare()
-    before = dl.w0.clone()
+    before = dl.wp.clone()
     dl.merge()
     torch.cuda.synchronize()
-    assert torch.equal(dl.w0.view(torch.int16), before.view(torch.int16))
+    assert torch.equal(dl.wp.view(torch.int16), before.view(torch.int16))
+    rng = np.random.default_rng(12)
+    nr, np_ = rng.permutation(cfg.m).astype(np.int32), rng.permutation(cfg.n).astype(np.int32)
+    dl.merge(to_device(nr, "i32"), to_device(np_, "i32"))
+    torch.cuda.synchronize()
+    bits = L["W0_raw"].view(np.int16)[nr][:, np_]
+    assert np.array_equal(dl.wp.view(torch.int16).cpu().numpy(), bits)
 
 
 # ---------------------------------------------------------------------------
@@ -307,7 +315,6 @@ def test_permutations_bit_exact(act, b, T):
         host = np.stack([D, D.transpose(0, 2, 1)]).astype(np.float32)
         dev = to_device(synth.bf16_bits(host) if act == "bf16" else host, act)
         dl.g_planes(side).copy_(dev.view(dl.g_planes(side).shape))
-    dl.prepare()
     raw = (lambda a: synth.bf16_bits(a)) if act == "bf16" else (lambda a: a)
     z = to_host_f64(dl.forward(to_device(raw(X), act)))
     _, _, dx = dl.backward(to_device(raw(dZ), act))
@@ -320,7 +327,8 @@ def test_permutations_bit_exact(act, b, T):
     assert np.array_equal(dx, dZ.astype(np.float64) @ Weff.T)
     # the permuted-frame weight is Psi W0 Phi^T exactly
     assert np.array_equal(to_host_f64(dl.wp), O.permuted_weight(np.eye(m), perm_r, perm_p))
-    assert np.array_equal(to_host_f64(dl.wpt), O.permuted_weight(np.eye(m), perm_r, perm_p).T)
+    # and the export returns W0 itself
+    assert np.array_equal(to_host_f64(dl.export_w0()[0]), np.eye(m))
 
 
 # ---------------------------------------------------------------------------
@@ -366,7 +374,6 @@ def test_token_shard_linearity():
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, "f32", "f32", cfg.T)
     dl.load(L)
     dl.cnp_build()
-    dl.prepare()
     res = []
     for sl in (slice(0, 300), slice(0, 120), slice(120, 300)):
         dl.forward(to_device(A["X_raw"][sl], "f32"))

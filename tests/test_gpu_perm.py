@@ -98,7 +98,6 @@ def test_merge_schedule_matches_the_oracle(cfg):
         dl.q_r.copy_(torch.from_numpy(q_r))
         dl.q_p.copy_(torch.from_numpy(q_p))
         dl.cnp_build()
-        dl.prepare()
         z_before = to_host_f64(dl.forward(x))
         merged = dl.merge_if_needed(step, interval, seed, tag)
         assert merged == O.merge_due(step, interval), step
@@ -113,7 +112,7 @@ def test_merge_schedule_matches_the_oracle(cfg):
         assert np.array_equal(dl.perm_r.cpu().numpy().astype(np.int64), perm_r), step
         assert np.array_equal(dl.perm_p.cpu().numpy().astype(np.int64), perm_p), step
         assert np.array_equal(dl.q_r.cpu().numpy(), q_r) and np.array_equal(dl.q_p.cpu().numpy(), q_p), step
-        w_err = _rel(to_host_f64(dl.w0), W)
+        w_err = _rel(to_host_f64(dl.export_w0()[0]), W)
         z_ref = O.forward(A["X"], W, q_r, q_p, perm_r, perm_p, cfg.b_r, cfg.b_p)["Z"]
         errs = (w_err, _rel(z_after, z_ref), _rel(z_after, z_before))
         print(f"step {step} merged={merged} W0 {errs[0]:.2e} z {errs[1]:.2e} z vs before {errs[2]:.2e}",

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 
 import oracle as O  # noqa: E402
 from orthogonal_equivalence_amd import synth  # noqa: E402
-from orthogonal_equivalence_amd.device import DeviceLayer  # noqa: E402
+from orthogonal_equivalence_amd.device import DeviceLayer, to_device  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,17 +32,24 @@ def _cfg(name, T, m, n, b_r, b_p, cfg_id):
 
 
 def _merge_on_gpu(cfg, L, zero_q=False):
+    # merged into the frame of new permutations (as at a training loop's
+    # merge), then exported to the original frame for the comparison
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, 16)
     dl.load(L)
     if zero_q:
         dl.q_r.zero_()
         dl.q_p.zero_()
     dl.cnp_build()
-    dl.prepare()
-    dl.merge()
+    rng = np.random.default_rng([cfg.cfg_id, 98])
+    nr, np_ = rng.permutation(cfg.m).astype(np.int32), rng.permutation(cfg.n).astype(np.int32)
+    dl.merge(to_device(nr, "i32"), to_device(np_, "i32"))
+    w0, w_scale = dl.export_w0()
     torch.cuda.synchronize()
-    codes = dl.w0.cpu().numpy().view(np.int8).reshape(cfg.m, cfg.n)
-    scale = dl.w_scale.cpu().numpy().astype(np.float32)
+    codes = w0.cpu().numpy().view(np.int8).reshape(cfg.m, cfg.n)
+    scale = w_scale.cpu().numpy().astype(np.float32)
+    # the resident codes and scales are those in the new frame, exactly
+    assert np.array_equal(dl.wp.cpu().numpy(), codes[nr][:, np_])
+    assert np.array_equal(dl.wscale_p.cpu().numpy(), scale[np_])
     q_after = torch.cat([dl.q_r, dl.q_p]).cpu().numpy()
     return codes, scale, q_after
 
