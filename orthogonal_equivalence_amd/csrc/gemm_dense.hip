@@ -125,16 +125,21 @@ static_assert(BK * kNcRowBytes == kTileBytes, "N-contiguous B tile size");
 
 __device__ __forceinline__ int swz_nc(int r) { return (r & 3) << 2; }
 
-__device__ __forceinline__ void load_one_nc(const bf16_t* __restrict__ g, int64_t ld, int col0, int collim, int k0,
-                                            char* lds, int wave, int lane, int i) {
+// Element offset of lane `lane`'s chunk for instruction i, relative to row
+// k0 of the tile (the row term k0 * ld is uniform and added per K step).
+__device__ __forceinline__ int64_t nc_offset(int64_t ld, int col0, int collim, int wave, int lane, int i) {
   const int sub = lane / kNcChunks, slot = lane % kNcChunks;
-  const int rbase = (wave * kInstPerTile + i) * kNcRowsPerInst;
-  const int r = rbase + sub;
+  const int r = (wave * kInstPerTile + i) * kNcRowsPerInst + sub;
   const int c = slot ^ swz_nc(r);
   int col = col0 + c * 8;
   col = col < collim ? col : collim - 8;
-  const bf16_t* src = g + static_cast<int64_t>(k0 + r) * ld + col;
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t)(lds + rbase * kNcRowBytes), 16, 0, 0);
+  return static_cast<int64_t>(r) * ld + col;
+}
+
+__device__ __forceinline__ void load_one_nc(const bf16_t* __restrict__ g_k0, int64_t off, char* lds, int wave, int i) {
+  const int rbase = (wave * kInstPerTile + i) * kNcRowsPerInst;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g_k0 + off), (lds_void_t)(lds + rbase * kNcRowBytes), 16,
+                                   0, 0);
 }
 
 template <int N>
@@ -216,7 +221,10 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   // of a fragment) and +16 (next K group) keep the row's swizzle, so they are
   // 2048 and 8192 bytes further.
   uint32_t bnc_addr[TN];
+  int64_t bnc_goff[kInstPerTile];
   if constexpr (BNC) {
+#pragma unroll
+    for (int i = 0; i < kInstPerTile; ++i) bnc_goff[i] = nc_offset(d.ldb, n0, d.N, wave, lane, i);
     const int grp = lane >> 4, li = lane & 15;
     const int r = 8 * (grp >> 1) + (li >> 2);
 #pragma unroll
@@ -233,9 +241,9 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
     if (p < nk) {
       load_tile(A, d.lda, m0, d.M, (kb + p) * BK, smem + p * kStageBytes, wave, lane);
       if constexpr (BNC) {
+        const bf16_t* Bk = B + static_cast<int64_t>((kb + p) * BK) * d.ldb;
 #pragma unroll
-        for (int i = 0; i < kInstPerTile; ++i)
-          load_one_nc(B, d.ldb, n0, d.N, (kb + p) * BK, smem + p * kStageBytes + kTileBytes, wave, lane, i);
+        for (int i = 0; i < kInstPerTile; ++i) load_one_nc(Bk, bnc_goff[i], smem + p * kStageBytes + kTileBytes, wave, i);
       } else {
         load_tile(B, d.ldb, n0, d.N, (kb + p) * BK, smem + p * kStageBytes + kTileBytes, wave, lane);
       }
@@ -256,6 +264,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
     char* nxt = smem + (pf % NSTAGE) * kStageBytes;
     const int kpf = (kb + min(pf, nk - 1)) * BK;
     const char* st = smem + (it % NSTAGE) * kStageBytes;
+    const bf16_t* Bpf = BNC ? B + static_cast<int64_t>(kpf) * d.ldb : B;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       // this K group's share of the next stage's loads (branch-free: the last
@@ -264,7 +273,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
       for (int u = 0; u < 2 * kInstPerTile / (BK / 16); ++u) {
         const int i = kk * (2 * kInstPerTile / (BK / 16)) + u;
         if (BNC && i >= kInstPerTile)
-          load_one_nc(B, d.ldb, n0, d.N, kpf, nxt + kTileBytes, wave, lane, i % kInstPerTile);
+          load_one_nc(Bpf, bnc_goff[i % kInstPerTile], nxt + kTileBytes, wave, i % kInstPerTile);
         else
           load_one(i < kInstPerTile ? A : B, i < kInstPerTile ? d.lda : d.ldb, i < kInstPerTile ? m0 : n0,
                    i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
@@ -275,10 +284,6 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
       for (int i = 0; i < TM; ++i)
         af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
       if constexpr (BNC) {
-        // from inline asm that waits for its own results: through the
-        // compiler builtin each such read gets a vmcnt(0) in front of it while
-        // the direct loads are in flight, which would drain the prefetch
-        static_assert(TN == 2, "two column tiles per wave");
         typedef unsigned long long u64;
         typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
         const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + kk * 16 * kNcRowBytes;
