@@ -2,14 +2,18 @@
 """Throughput of the POET-X layer hot path on one GPU.
 
 One step = CNP build of R and P, forward, backward to dq_R / dq_P / dx, and
-(for the Llama-8B MLP up-projection workload) one merge cycle: W0 <- R W0 P,
-new draws of both permutations and the permuted-frame weight rebuild, all on
-synthetic seeded inputs already resident in HBM. Prints one JSON line on stdout; progress goes to stderr.
+(for the Llama-8B MLP up-projection workload) one merge cycle: new draws of
+both permutations and W0 <- R W0 P written into their frame, all on
+synthetic seeded inputs already resident in HBM. Prints one JSON line on
+stdout; progress goes to stderr.
 
 The step time comes from a timed pass of K steps with nothing else on the
 stream. A second timed pass of K steps runs with the library's HIP-event log
 on (an event pair on the launch stream around each of its kernel steps); the
 dominant kernel's roofline fraction and the per-kernel table come from it.
+Further passes, timed the same way: the step without its merge cycle (the
+forward + backward throughput and, with the difference, the merge cycle's
+wall-clock cost), the memory variant, and the step of every other workload.
 The CPU baseline is the float64 oracle timed on the same workload (whole, or
 a token sample when the whole would take too long).
 """
@@ -203,6 +207,69 @@ def kernel_roofline(cfg, per):
     return out
 
 
+# The other single-GPU workloads of the pages' Llama runs, timed as extra
+# lines of the same report (the tiny float32 layer is launch-bound and left out).
+OTHER_WORKLOADS = ("llama3b_proj", "llama13b_q_proj", "llama13b_down_proj", "xq_llama8b_mlp_up")
+
+
+def time_workload(cfg, steps, warmup):
+    """ms per step (CNP build + forward + backward) of one workload on fresh
+    device buffers, with W warmup steps and K timed ones between two
+    synchronisations, then the dense products' average launch times from a
+    logged pass."""
+    import torch
+    from orthogonal_equivalence_amd import synth
+    from orthogonal_equivalence_amd import poetx as px
+    from orthogonal_equivalence_amd.device import DeviceLayer, to_device
+
+    L = synth.make_layer(cfg, 0)
+    A = synth.make_activations(cfg, 0)
+    dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
+    dl.load(L)
+    x = to_device(A["X_raw"], cfg.act)
+    dz = to_device(A["dZ_raw"], cfg.act)
+    del A, L
+    z = dl.act_tensor(cfg.T, cfg.n)
+    dx = dl.act_tensor(cfg.T, cfg.m)
+    dq_r, dq_p = torch.empty_like(dl.q_r), torch.empty_like(dl.q_p)
+
+    def step():
+        dl.cnp_build()
+        dl.forward(x, z)
+        dl.backward(dz, dq_r, dq_p, dx)
+
+    for _ in range(warmup):
+        step()
+    st = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st)
+    for _ in range(steps):
+        step()
+    t1.record(st)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    px.poetx_profile_enable(1)
+    for _ in range(3):
+        step()
+    px.poetx_profile_enable(0)
+    g = {}
+    for i in range(px.poetx_profile_count()):
+        name, t = px.poetx_profile_get(i)
+        if name.startswith("gemm_dense"):
+            g.setdefault(name, []).append(t)
+    out = {"tokens": cfg.T, "m": cfg.m, "n": cfg.n, "b": cfg.b_r, "weight": cfg.weight,
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1)}
+    flops = 2.0 * cfg.T * cfg.m * cfg.n
+    for name, ts in sorted(g.items()):
+        avg = sum(ts) / len(ts)
+        out[name + "_ms"] = round(avg, 4)
+        out[name + "_frac_mfma"] = round(flops / (avg * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)
+    del dl
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(mib):
     """Plain device-to-device copies of a known size (the calibration for the
     HBM byte counters: a profiler reads FETCH_SIZE / WRITE_SIZE off these)."""
@@ -231,6 +298,8 @@ def main():
                     help="skip the per-step warm and cold spread passes (profiling runs)")
     ap.add_argument("--merge", action="store_true",
                     help="include one merge and the weight rebuild in every step (the 8B MLP-up workload always does)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the timed steps of the workloads other than --workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run three plain copies of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -387,14 +456,37 @@ def main():
                 "kernel": "dense W0 product (gemm_dense_fwd and gemm_dense_bwd launches)",
                 "flops_per_launch": flops_gemm, "avg_launch_ms": round(g_ms, 4)}
 
-    fwd_bwd_names = [k for k in per if k.startswith(("cnp_build", "gather", "apply", "gemm", "scatter",
-                                                     "grad", "cnp_bwd"))]
-    ms_fwd_bwd = sum(per[k][0] for k in fwd_bwd_names) / args.steps
-    # the merge cycle on the launch stream; the permutation draws run beside
-    # the merge on a second stream, so their (overlapping) time is reported
-    # on its own
-    ms_merge = sum(per[k][0] for k in per if k.startswith("merge")) / args.steps
+    # pass 5: the step without its merge cycle, timed like pass 1 (q stays
+    # nonzero without a merge, so no copy is needed); the merge cycle's
+    # wall-clock cost is the difference of the two passes
+    def step_fwd_bwd():
+        dl.cnp_build()
+        dl.forward(x, z)
+        dl.backward(dz, dq_r, dq_p, dx)
+
+    if cfg.merge:
+        ms_fwd_bwd = timed(args.steps, step_fwd_bwd) / args.steps
+        ms_merge = ms_step - ms_fwd_bwd
+        optimizer_stand_in()
+        log(f"[bench] without the merge cycle: {ms_fwd_bwd:.3f} ms/step (merge cycle {ms_merge:.3f} ms)")
+    else:
+        ms_fwd_bwd, ms_merge = ms_step, None
+    # the merge cycle's kernels on the launch stream; the permutation draws
+    # run beside them on a second stream, so their (overlapping) time is
+    # reported on its own
+    ms_merge_kernels = sum(per[k][0] for k in per if k.startswith("merge")) / args.steps
     ms_draws = sum(per[k][0] for k in per if k.startswith("sample_perm")) / args.steps
+
+    # pass 6: every other workload's step (CNP build, forward, backward; no
+    # merge), timed like pass 1, plus its dense products from a logged pass
+    others = None
+    if not args.no_other_workloads:
+        others = {}
+        for name in OTHER_WORKLOADS:
+            if name == cfg.name:
+                continue
+            others[name] = time_workload(synth.CONFIGS[name], args.steps, args.warmup)
+            log(f"[bench] {name}: {json.dumps(others[name])}")
 
     yard = None
     if not args.no_yardstick and bf16:
@@ -436,9 +528,12 @@ def main():
         "ms_per_step_with_kernel_log": round(ms_logged / args.steps, 4),
         "fwd_bwd_ms": round(ms_fwd_bwd, 4),
         "fwd_bwd_tokens_per_s": round(cfg.T / (ms_fwd_bwd * 1e-3), 1),
-        "merge_cycle_ms": round(ms_merge, 4),
+        "merge_cycle_ms": None if ms_merge is None else round(ms_merge, 4),
+        "merge_cycle_kernels_ms": round(ms_merge_kernels, 4),
         "perm_draws_ms_beside_merge": round(ms_draws, 4),
-        "tokens_per_s_merge_every_200": round(cfg.T / ((ms_fwd_bwd + ms_merge / 200) * 1e-3), 1),
+        "tokens_per_s_merge_every_200": (None if ms_merge is None else
+                                         round(cfg.T / ((ms_fwd_bwd + ms_merge / 200) * 1e-3), 1)),
+        "other_workloads": others,
         "step_spread": spread,
         "variant_mem": variant_mem,
         "kernels_ms": kernels,
