@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpoetx.so")
-SOURCES = ["gemm_dense.hip", "block_apply.hip", "block_grad.hip", "block_prod.hip", "gemm_bf16.hip", "gemm_f32.hip", "aux.hip", "perm.hip", "poetx_abi.hip"]
+SOURCES = ["gemm_dense.hip", "block_apply.hip", "block_grad.hip", "block_prod.hip", "cnp_fused.hip", "gemm_bf16.hip", "gemm_f32.hip", "aux.hip", "perm.hip", "poetx_abi.hip"]
 ARCH = os.environ.get("POETX_ARCH", "gfx950")
 
 # -packed-fp32-ops off: hipcc -O3 otherwise forms packed float32 ops on its own

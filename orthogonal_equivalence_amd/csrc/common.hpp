@@ -16,12 +16,14 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even float32 -> bfloat16 (NaN stays NaN).
+// Round-to-nearest-even float32 -> bfloat16 (NaN stays NaN, quieted).
+// Written as a select, not a branch, so that unrolled epilogues stay
+// straight-line code.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x40u;
+  return static_cast<bf16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 // Pack two floats into a bf16 pair (lo in bits 0..15).

@@ -121,6 +121,13 @@ struct BlockProdDesc {
 };
 bool block_prod_bf16(const BlockProdDesc& d, hipStream_t stream);
 
+// The Cayley-Neumann build of 256 x 256 bfloat16 blocks from Q (cnp_fused.hip):
+// Qh holds Q of blocks [0, n0 + n1) as bfloat16 [b][b] each (unpack_skew2's
+// bfloat16 output); blocks [0, n0) go to the CNP buffer g0 ([2][n0][b][b]:
+// G - I, then (G - I)^T), blocks [n0, n0 + n1) to g1. Four workgroups per
+// block, Q kept in LDS, no scratch. Returns false unless b == 256.
+bool cnp_build_fused(const uint16_t* Qh, int n0, int n1, int b, void* g0, void* g1, hipStream_t stream);
+
 // Left block product (block_apply.hip) on a row-major rows x ncols bfloat16
 // matrix (row stride ld): out[j*256 + i][c] = in[j*256 + i][c] + sum_k
 // plane[j][i][k] in[j*256 + k][c] for the ceil(rows/256) row blocks; plane

@@ -164,8 +164,16 @@ struct CnpWs {
   uint16_t *Qh, *Q2h, *Sh;
 };
 
+// bfloat16 blocks of 256 take the two-launch build: unpack to bfloat16 Q,
+// then every product of the chain with Q kept in LDS (cnp_fused.hip).
+bool cnp_fused_applies(const poetx_layer* L, int b) { return is_bf16(L) && b == 256; }
+
 CnpWs plan_cnp(const poetx_layer* L, int64_t bb, Carve& c) {
   CnpWs w{};
+  if (cnp_fused_applies(L, L->b_r) && cnp_fused_applies(L, L->b_p)) {
+    w.Qh = c.take<uint16_t>(bb);
+    return w;
+  }
   w.Qf = c.take<float>(bb);
   w.Q2f = c.take<float>(bb);
   w.Tf = c.take<float>(bb);
@@ -522,6 +530,11 @@ bool cnp_group(const poetx_layer* L, const Group& g, const float* q0, const floa
                hipStream_t st) {
   Carve c(ws);
   CnpWs w = plan_cnp(L, g.elems(), c);
+  if (cnp_fused_applies(L, g.b)) {
+    uint16_t* Qh = w.Qh;
+    unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, nullptr, Qh, st);
+    return cnp_build_fused(Qh, g.n0, g.n1, g.b, g0, g1, st);
+  }
   const bool bf = is_bf16(L);
   unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
   if (bf && g.b % 128 == 0) {
