@@ -51,12 +51,14 @@ bool gemm_f32(const GemmDesc& d, int a_mode, int b_mode, hipStream_t stream);
 
 // Dense bfloat16 product for the W0 products (gemm_dense.hip): A [M][K]
 // K-contiguous, B [N][K] K-contiguous (b_ncontig false) or [K][N]
-// N-contiguous (b_ncontig true), bfloat16; C bfloat16, optional per-column
-// scale; uses A, lda, B, ldb, C, ldc, scale, M, N, K only. Returns false
-// unless K % 64 == 0 and N % 8 == 0. split_ws: gemm_dense_split_bytes(M, N,
-// K) bytes (256-byte aligned) for splitting the output tiles of a partial
-// last round along K; with NULL, or 0 bytes needed, every tile runs whole.
+// N-contiguous (b_ncontig true), bfloat16 or, with b_int8, int8 codes
+// dequantised to bfloat16 inside the product (N and ldb multiples of 16);
+// C bfloat16, optional per-column scale; uses A, lda, B, ldb, C, ldc, scale,
+// M, N, K only. Returns false unless K % 64 == 0 and N % 8 == 0.
+// split_ws: gemm_dense_split_bytes(M, N, K) bytes (256-byte aligned) for
+// splitting the output tiles of a partial last round along K; with NULL, or
+// 0 bytes needed, every tile runs whole.
 size_t gemm_dense_split_bytes(int M, int N, int K);
-bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t stream, bool b_ncontig);
+bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t stream, bool b_ncontig, bool b_int8);
 
 }  // namespace poetx

@@ -26,6 +26,15 @@
 //    j gets rows k0 .. k0+3 of column n0 + j. The four rows a read touches
 //    then fall in four different 64-byte quarters of the 256-byte bank
 //    window, and the 32 columns of a fragment are 64 contiguous bytes.
+//  * An int8 B (the quantised base weight) is dequantised inside the
+//    product: its tiles go global -> LDS as int8 (half the bytes of bfloat16)
+//    into a staging area of two 16 KB buffers, with the direct loads, two K
+//    steps ahead (after that step's A loads, so that the wait at the top of a
+//    step leaves them in flight). At the end of the step before its own, each
+//    wave converts the chunks it loaded itself (no barrier needed) exactly to
+//    bfloat16 (|code| <= 127 has at most 8 significant bits) into the same
+//    LDS layouts as a bfloat16 B, K-contiguous or N-contiguous. The column
+//    scales are applied in the epilogue as for any scaled product.
 //  * Output tiles are ordered so that each XCD works on one contiguous band
 //    of tiles (shared A/B panels stay in that XCD's L2).
 //  * When the tiles do not fill a whole number of rounds over the 256 CUs,
@@ -167,10 +176,35 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
   tn = (pid % group) / gsz;
 }
 
+// Sixteen int8 codes as sixteen bfloat16 values (exact): each code widened
+// to float, whose low 16 bits are zero for |code| <= 127.
+__device__ __forceinline__ void i8x16_to_bf16(const uint4 raw, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float f0 = static_cast<float>(static_cast<int8_t>(w[q] & 0xffu));
+    const float f1 = static_cast<float>(static_cast<int8_t>((w[q] >> 8) & 0xffu));
+    const float f2 = static_cast<float>(static_cast<int8_t>((w[q] >> 16) & 0xffu));
+    const float f3 = static_cast<float>(static_cast<int8_t>(w[q] >> 24));
+    o[2 * q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    o[2 * q + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// int8 B tile: 16 KB of codes per stage, two 1 KB direct loads per wave.
+constexpr int kI8StageBytes = BN * BK;
+constexpr int kI8Chunks = kI8StageBytes / 1024 / (NT / 64);  // 2
+static_assert(NSTAGE * 2 * BM * BK * 2 + 2 * kI8StageBytes <= 160 * 1024, "LDS with int8 staging");
+
 // BNC: B is N-contiguous (B[k * ldb + n]) instead of K-contiguous.
-template <bool BNC>
+// BI8: B holds int8 codes (ldb in elements = bytes).
+template <bool BNC, bool BI8>
 __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n, DenseSplit sp) {
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes + (BI8 ? 2 * kI8StageBytes : 0)];
+  char* const i8st = smem + NSTAGE * kStageBytes;  // int8 staging (BI8 only)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,6 +256,79 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   // 2048 and 8192 bytes further.
   uint32_t bnc_addr[TN];
   int64_t bnc_goff[kInstPerTile];
+  // int8 B: per chunk, its element offset in B relative to K step k0 (add
+  // k0 for K-contiguous rows, k0 * ldb for N-contiguous ones) and the LDS
+  // offsets (within a B tile) of the two bfloat16 chunks it becomes
+  int64_t i8_goff[kI8Chunks];
+  int i8_lds[kI8Chunks][2];
+  if constexpr (BI8) {
+#pragma unroll
+    for (int u = 0; u < kI8Chunks; ++u) {
+      // chunk q of the tile: lane `lane` of this wave's direct load u
+      const int q = (wave * kI8Chunks + u) * 64 + lane;
+      if constexpr (BNC) {
+        const int row = q >> 4, part = q & 15;  // K row, 16 columns
+        int col = n0 + part * 16;
+        col = col < d.N ? col : d.N - 16;
+        i8_goff[u] = static_cast<int64_t>(row) * d.ldb + col;
+        i8_lds[u][0] = row * kNcRowBytes + (((2 * part) ^ swz_nc(row)) << 4);
+        i8_lds[u][1] = row * kNcRowBytes + (((2 * part + 1) ^ swz_nc(row)) << 4);
+      } else {
+        const int row = q >> 2, part = q & 3;  // N row, 16 K values
+        int gr = n0 + row;
+        gr = gr < d.N ? gr : d.N - 1;
+        i8_goff[u] = static_cast<int64_t>(gr) * d.ldb + part * 16;
+        i8_lds[u][0] = row * kRowBytes + (((2 * part) ^ swz(row)) << 4);
+        i8_lds[u][1] = row * kRowBytes + (((2 * part + 1) ^ swz(row)) << 4);
+      }
+    }
+  }
+  const int8_t* Bq = static_cast<const int8_t*>(d.B);
+  // direct loads of this wave's share of stage-K-step k0's codes into
+  // staging buffer sb
+  auto i8_load = [&](int k0, int sb) {
+    const int8_t* base = BNC ? Bq + static_cast<int64_t>(k0) * d.ldb : Bq + k0;
+#pragma unroll
+    for (int u = 0; u < kI8Chunks; ++u)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + i8_goff[u]),
+                                       (lds_void_t)(i8st + sb * kI8StageBytes + (wave * kI8Chunks + u) * 1024), 16,
+                                       0, 0);
+  };
+  // this wave's chunks of staging buffer sb, as bfloat16 into B tile btile
+  // (the staging reads are inline asm that waits for its own results: read
+  // through ordinary loads they get a vmcnt(0) in front of them, which would
+  // drain the loads in flight; the caller has waited for this buffer's loads)
+  auto i8_convert = [&](int sb, char* btile) {
+    static_assert(kI8Chunks == 2, "two staged chunks per lane");
+    u32x4_t rawv[2];
+    const uint32_t ad = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(i8st)) + sb * kI8StageBytes +
+                        wave * kI8Chunks * 1024 + lane * 16;
+    asm volatile("ds_read_b128 %0, %2\n ds_read_b128 %1, %2 offset:1024\n s_waitcnt lgkmcnt(0)"
+                 : "=&v"(rawv[0]), "=&v"(rawv[1])
+                 : "v"(ad)
+                 : "memory");
+    const uint4 raw[2] = {make_uint4(rawv[0][0], rawv[0][1], rawv[0][2], rawv[0][3]),
+                          make_uint4(rawv[1][0], rawv[1][1], rawv[1][2], rawv[1][3])};
+    // the writes, likewise from inline asm: as ordinary stores they get a
+    // vmcnt(0) in front of them (the direct loads in flight target other
+    // LDS: the next stage's A tile and the other staging buffer)
+    u32x4_t cv[2][2];
+#pragma unroll
+    for (int u = 0; u < kI8Chunks; ++u) {
+      uint4 lo, hi;
+      i8x16_to_bf16(raw[u], lo, hi);
+      cv[u][0] = u32x4_t{lo.x, lo.y, lo.z, lo.w};
+      cv[u][1] = u32x4_t{hi.x, hi.y, hi.z, hi.w};
+    }
+    const uint32_t bt = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(btile));
+    asm volatile(
+        "ds_write_b128 %0, %4\n ds_write_b128 %1, %5\n ds_write_b128 %2, %6\n ds_write_b128 %3, %7\n"
+        " s_waitcnt lgkmcnt(0)"
+        :
+        : "v"(bt + i8_lds[0][0]), "v"(bt + i8_lds[0][1]), "v"(bt + i8_lds[1][0]), "v"(bt + i8_lds[1][1]),
+          "v"(cv[0][0]), "v"(cv[0][1]), "v"(cv[1][0]), "v"(cv[1][1])
+        : "memory");
+  };
   if constexpr (BNC) {
 #pragma unroll
     for (int i = 0; i < kInstPerTile; ++i) bnc_goff[i] = nc_offset(d.ldb, n0, d.N, wave, lane, i);
@@ -240,7 +347,11 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   for (int p = 0; p < NSTAGE - 1; ++p) {
     if (p < nk) {
       load_tile(A, d.lda, m0, d.M, (kb + p) * BK, smem + p * kStageBytes, wave, lane);
-      if constexpr (BNC) {
+      if constexpr (BI8) {
+        i8_load((kb + p) * BK, 0);
+        wait_vmcnt<0>();
+        i8_convert(0, smem + p * kStageBytes + kTileBytes);
+      } else if constexpr (BNC) {
         const bf16_t* Bk = B + static_cast<int64_t>((kb + p) * BK) * d.ldb;
 #pragma unroll
         for (int i = 0; i < kInstPerTile; ++i) load_one_nc(Bk, bnc_goff[i], smem + p * kStageBytes + kTileBytes, wave, i);
@@ -250,21 +361,35 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
     }
   }
 
+  // int8 B: the codes of the stage after the one being computed, in staging
+  // buffer 1 (step `it` converts buffer (it + 1) % 2 and loads into it % 2)
+  if constexpr (BI8) i8_load((kb + min(1, nk - 1)) * BK, 1);
+
   for (int it = 0; it < nk; ++it) {
     // stage `it` is the oldest of the (up to NSTAGE - 1) stages in flight;
     // loads complete in order, so waiting until the younger ones remain
-    // suffices. Near the end fewer younger stages exist.
+    // suffices. Near the end fewer younger stages exist. With an int8 B the
+    // youngest loads are the next stage's codes, which stay in flight.
     constexpr int kPerStage = 2 * kInstPerTile;
     const int younger = min(NSTAGE - 2, nk - 1 - it);
-    if (younger >= 2) wait_vmcnt<2 * kPerStage>();
-    else if (younger == 1) wait_vmcnt<kPerStage>();
-    else wait_vmcnt<0>();
-    __syncthreads();
+    if constexpr (BI8) {
+      // a bare barrier: __syncthreads() would also wait for the codes in flight
+      wait_vmcnt<kI8Chunks>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      if (younger >= 2) wait_vmcnt<2 * kPerStage>();
+      else if (younger == 1) wait_vmcnt<kPerStage>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+    }
     const int pf = it + NSTAGE - 1;
     char* nxt = smem + (pf % NSTAGE) * kStageBytes;
     const int kpf = (kb + min(pf, nk - 1)) * BK;
     const char* st = smem + (it % NSTAGE) * kStageBytes;
     const bf16_t* Bpf = BNC ? B + static_cast<int64_t>(kpf) * d.ldb : B;
+
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       // this K group's share of the next stage's loads (branch-free: the last
@@ -272,6 +397,13 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
 #pragma unroll
       for (int u = 0; u < 2 * kInstPerTile / (BK / 16); ++u) {
         const int i = kk * (2 * kInstPerTile / (BK / 16)) + u;
+        if constexpr (BI8) {
+          if (i >= kInstPerTile) {
+            // B comes through registers: once the A loads are out
+            if (i == kInstPerTile) i8_load((kb + min(it + 2, nk - 1)) * BK, it & 1);
+            continue;
+          }
+        }
         if (BNC && i >= kInstPerTile)
           load_one_nc(Bpf, bnc_goff[i % kInstPerTile], nxt + kTileBytes, wave, i % kInstPerTile);
         else
@@ -308,6 +440,17 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      if constexpr (BI8) {
+        // the next stage's codes, loaded one step ago, into its B tile; younger
+        // loads are this step's A loads and the codes two stages ahead
+        // (in-order completion). N-contiguous: between the last two K groups,
+        // while this group's MFMAs run; K-contiguous: after the last group
+        // (each measured faster for its layout).
+        if (kk == (BNC ? BK / 16 - 2 : BK / 16 - 1)) {
+          wait_vmcnt<kInstPerTile + kI8Chunks>();
+          i8_convert((it + 1) & 1, nxt + kTileBytes);
+        }
+      }
     }
   }
 
@@ -427,18 +570,23 @@ size_t gemm_dense_split_bytes(int M, int N, int K) {
   return align256(static_cast<size_t>(p.tiles - p.full) * p.k * BM * BN * sizeof(float));
 }
 
-bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s, bool b_ncontig) {
+bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s, bool b_ncontig, bool b_int8) {
   if (d.M <= 0 || d.N <= 0) return true;
   if (d.K % 64 != 0 || d.K <= 0 || d.N % 8 != 0) return false;
+  if (b_int8 && (d.N % 16 != 0 || d.ldb % 16 != 0)) return false;
   const int tm = (d.M + BM - 1) / BM, tn = (d.N + BN - 1) / BN;
   SplitPlan p = split_plan(d.M, d.N, d.K);
   if (!split_ws) p = SplitPlan{p.tiles, p.tiles, 1};
   const DenseSplit sp{static_cast<float*>(split_ws), p.full, p.k};
   const int tail = p.tiles - p.full;
-  if (b_ncontig)
-    hipLaunchKernelGGL(k_gemm_dense<true>, dim3(p.full + tail * p.k), dim3(NT), 0, s, d, tm, tn, sp);
-  else
-    hipLaunchKernelGGL(k_gemm_dense<false>, dim3(p.full + tail * p.k), dim3(NT), 0, s, d, tm, tn, sp);
+  const dim3 grid(p.full + tail * p.k);
+  if (b_int8) {
+    if (b_ncontig) hipLaunchKernelGGL((k_gemm_dense<true, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+    else hipLaunchKernelGGL((k_gemm_dense<false, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+  } else {
+    if (b_ncontig) hipLaunchKernelGGL((k_gemm_dense<true, false>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+    else hipLaunchKernelGGL((k_gemm_dense<false, false>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+  }
   if (tail > 0)
     hipLaunchKernelGGL(k_dense_split_sum, dim3(tail * (BM * BN / 8 / 256)), dim3(256), 0, s, d, tm, tn, sp);
   return true;

@@ -212,7 +212,7 @@ struct FwdWs {
   void* buf;
   int32_t* inv_p;
   void* split;  // the dense product's split of a partial last round (or null)
-  void* wdeq;   // int8 weight: bfloat16 copy of Wp^T's codes (or null)
+  void* wdeq;   // int8 weight the dense kernel cannot take: bfloat16 copy of its codes (or null)
 };
 
 size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K);
@@ -224,7 +224,7 @@ FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.inv_p = c.take<int32_t>(L->n);
   const size_t sb = dense_split_bytes(L, T, L->n, L->m);
   w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
-  w.wdeq = L->w_dtype == POETX_I8 ? c.take<uint16_t>(L->m * L->n) : nullptr;
+  w.wdeq = i8_staging(L) ? c.take<uint16_t>(L->m * L->n) : nullptr;
   return w;
 }
 
@@ -236,7 +236,6 @@ struct BwdWs {
   float *Us, *Uk;     // symmetric / skew parts of dG (side R) and dH (side P)
   uint16_t *Ush, *Ukh;
   void* split;        // the dense product's split of a partial last round (or null)
-  void* wdeq;         // int8 weight: bfloat16 copy of Wp's codes (or null)
   size_t cnp_off;     // the CNP adjoint scratch starts here
 };
 
@@ -263,7 +262,6 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   w.Ukh = c.take<uint16_t>(all);
   const size_t sb = dense_split_bytes(L, T, L->m, L->n);
   w.split = sb ? c.take<char>(static_cast<int64_t>(sb)) : nullptr;
-  w.wdeq = i8_staging(L) ? c.take<uint16_t>(L->m * L->n) : nullptr;
   w.cnp_off = c.off;
   Carve m(nullptr);
   plan_cnp_bwd(L, cnp_batch_elems(L), m);
@@ -404,14 +402,14 @@ bool dense_kernel_applies(const poetx_layer* L, int N, int K) {
 }
 
 // The quantised variant stores the base weight as int8 and dequantises it at
-// run time (section "POET-XQ"): the codes are copied to bfloat16 (exact)
-// into the workspace right before each dense product, whose epilogue (or the
-// preceding apply, in the backward) applies the column scales. The stored
-// weight stays int8; the copy is transient scratch. The forward, which reads
-// Wp N-contiguous, always makes it; the backward does when the dense kernel
-// applies, and otherwise the general engine reads the codes itself.
+// run time (section "POET-XQ"): the dense kernel reads the int8 codes and
+// turns them into bfloat16 on their way into LDS (exact); its epilogue (or
+// the preceding apply, in the backward) applies the column scales. Where the
+// dense kernel's shape rules fail, the backward's general engine reads the
+// codes itself, and the forward (which reads Wp N-contiguous) copies them to
+// bfloat16 in the workspace first.
 bool i8_staging(const poetx_layer* L) {
-  return L->w_dtype == POETX_I8 && dense_kernel_applies(L, static_cast<int>(L->m), static_cast<int>(L->n));
+  return L->w_dtype == POETX_I8 && !dense_kernel_applies(L, static_cast<int>(L->n), static_cast<int>(L->m));
 }
 
 // Workspace of the dense kernel's split of a partial last round of tiles.
@@ -424,7 +422,7 @@ size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K) 
 // are K-contiguous (the backward). i8: B holds int8 codes (K-contiguous only).
 bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, bool b_ncontig, void* split_ws,
                    hipStream_t st) {
-  if (!i8 && dense_kernel_applies(L, d.N, d.K)) return gemm_dense_bf16(d, split_ws, st, b_ncontig);
+  if (dense_kernel_applies(L, d.N, d.K)) return gemm_dense_bf16(d, split_ws, st, b_ncontig, i8);
   if (b_ncontig) return !i8 && gemm(L, d, A_KCONTIG, B_NCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
   return gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
 }
@@ -722,7 +720,7 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   }
   {
     ProfScope p(recompute ? "recompute_gemm_dense" : "gemm_dense_fwd", stream);
-    ok = ok && dense_product(L, d, false, true, w.split, stream);
+    ok = ok && dense_product(L, d, i8 && !w.wdeq, true, w.split, stream);
   }
   if (!z) return ok;
   {
@@ -782,14 +780,9 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   d.M = static_cast<int>(T);
   d.N = static_cast<int>(L->m);
   d.K = static_cast<int>(L->n);
-  if (w.wdeq) {
-    ProfScope p("dequant_w_bwd", stream);
-    ok = ok && i8_to_bf16(static_cast<const int8_t*>(d.B), static_cast<uint16_t*>(w.wdeq), L->m * L->n, stream);
-    d.B = w.wdeq;
-  }
   {
     ProfScope p("gemm_dense_bwd", stream);
-    ok = ok && dense_product(L, d, i8 && !w.wdeq, false, w.split, stream);
+    ok = ok && dense_product(L, d, i8, false, w.split, stream);
   }
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {
