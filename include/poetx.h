@@ -266,8 +266,10 @@ POETX_API int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p,
  *   perm [dim] int32, overwritten.
  *   ws: at least 8 * dim bytes of scratch (poetx_workspace_bytes(L, 0,
  *       POETX_OP_SAMPLE_PERM) covers both sides of a layer L).
- * 1 <= dim <= 2^20 (POETX_EUNSUPPORTED above). Each index is ranked by
- * counting smaller keys, so the work grows as dim^2. */
+ * 1 <= dim <= 2^20 (POETX_EUNSUPPORTED above). Up to dim = 15360 the draw
+ * runs in one workgroup and leaves ws untouched (its keys stay in on-chip
+ * memory, the work grows as dim); wider draws rank each index by counting
+ * smaller keys over the whole GPU, and their work grows as dim^2. */
 POETX_API int poetx_sample_perm(int64_t dim, uint64_t seed, uint64_t tag, uint64_t draw,
                       int32_t* perm, void* ws, size_t ws_bytes, hipStream_t stream);
 

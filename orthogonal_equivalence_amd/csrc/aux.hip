@@ -114,7 +114,8 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads, 2)
 k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
                    T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
-                   const int32_t* __restrict__ cidx, int ncols, int64_t nrows) {
+                   const int32_t* __restrict__ cidx, int ncols, int64_t nrows,
+                   const int32_t* __restrict__ rmap_pre, const int32_t* __restrict__ cidx_pre) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -127,8 +128,19 @@ k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __res
   for (int g = 0; g < kPipeGroups; ++g) {
     const int grp = tid + g * kThreads;
     if (grp < ngroups) {
-      const int4 i0 = reinterpret_cast<const int4*>(cidx)[2 * grp];
-      const int4 i1 = reinterpret_cast<const int4*>(cidx)[2 * grp + 1];
+      int4 i0, i1;
+      if (cidx_pre) {
+        // composed map: column i takes cidx[cidx_pre[i]]
+        const int4 p0 = reinterpret_cast<const int4*>(cidx_pre)[2 * grp];
+        const int4 p1 = reinterpret_cast<const int4*>(cidx_pre)[2 * grp + 1];
+        i0 = make_int4(cidx[clamp_index(p0.x, ncols)], cidx[clamp_index(p0.y, ncols)],
+                       cidx[clamp_index(p0.z, ncols)], cidx[clamp_index(p0.w, ncols)]);
+        i1 = make_int4(cidx[clamp_index(p1.x, ncols)], cidx[clamp_index(p1.y, ncols)],
+                       cidx[clamp_index(p1.z, ncols)], cidx[clamp_index(p1.w, ncols)]);
+      } else {
+        i0 = reinterpret_cast<const int4*>(cidx)[2 * grp];
+        i1 = reinterpret_cast<const int4*>(cidx)[2 * grp + 1];
+      }
       ix[g][0] = clamp_index(i0.x, ncols) | (clamp_index(i0.y, ncols) << 16);
       ix[g][1] = clamp_index(i0.z, ncols) | (clamp_index(i0.w, ncols) << 16);
       ix[g][2] = clamp_index(i1.x, ncols) | (clamp_index(i1.y, ncols) << 16);
@@ -141,7 +153,7 @@ k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __res
   for (int g = 0; g < kPipeGroups; ++g) my_st += (wave * 64 + g * kThreads < ngroups) ? (sizeof(T) == 4 ? 2 : 1) : 0;
 
   auto issue = [&](int64_t r, char* buf) {
-    const int64_t src = rmap_in ? clamp_index(rmap_in[r], nrows) : r;
+    const int64_t src = rmap_in ? clamp_index(rmap_in[rmap_pre ? clamp_index(rmap_pre[r], nrows) : r], nrows) : r;
     const char* sp = reinterpret_cast<const char*>(in + src * ld_in);
     for (int i = wave; i < ninst; i += kThreads / 64) {
       const int ch = i * 64 + lane;
@@ -216,6 +228,14 @@ k_gather_cols_direct(const T* __restrict__ in, int64_t ld_in, const int32_t* __r
 
 __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __restrict__ inv, int64_t n) {
   POETX_GRID_STRIDE(i, n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
+}
+
+__global__ void k_inverse_perm2(const int32_t* __restrict__ perm0, int32_t* __restrict__ inv0, int64_t n0,
+                                const int32_t* __restrict__ perm1, int32_t* __restrict__ inv1, int64_t n1) {
+  POETX_GRID_STRIDE(i, n0 + n1) {
+    if (i < n0) inv0[clamp_index(perm0[i], n0)] = static_cast<int32_t>(i);
+    else inv1[clamp_index(perm1[i - n0], n1)] = static_cast<int32_t>(i - n0);
+  }
 }
 
 __global__ void k_compose_perm(const int32_t* __restrict__ inv0, const int32_t* __restrict__ next0,
@@ -756,16 +776,23 @@ inline unsigned grid1(int64_t n) { return static_cast<unsigned>(std::min<int64_t
 inline unsigned grid_yz(int64_t n) { return static_cast<unsigned>(std::min<int64_t>(n, kMaxGridYZ)); }
 
 template <typename T>
-void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
-                   const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, hipStream_t s) {
+bool pipe_applies(int64_t ncols) {
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
-  if (row_bytes % 16 == 0 && ncols <= kPipeGroups * 8 * kThreads && 2 * row_bytes <= 128 * 1024) {
+  return row_bytes % 16 == 0 && ncols <= kPipeGroups * 8 * kThreads && 2 * row_bytes <= 128 * 1024;
+}
+
+template <typename T>
+void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
+                   const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, hipStream_t s,
+                   const int32_t* rmap_pre = nullptr, const int32_t* cidx_pre = nullptr) {
+  const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
+  if (pipe_applies<T>(ncols)) {
     const int64_t lds = 2 * row_bytes;
     const int per_cu = static_cast<int>(std::min<int64_t>(2, (160 * 1024) / lds));
     const unsigned nwg = static_cast<unsigned>(std::min<int64_t>(nrows, 256 * per_cu));
     hipLaunchKernelGGL(k_gather_rows_pipe<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(lds), s,
                        static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
-                       static_cast<int>(ncols), nrows);
+                       static_cast<int>(ncols), nrows, rmap_pre, cidx_pre);
   } else if (row_bytes <= kRowLdsMax) {
     int rows = static_cast<int>(kRowLdsBudget / row_bytes);
     rows = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
@@ -799,6 +826,31 @@ bool gather_cols(const void* in, int64_t ld_in, const int32_t* rmap_in, void* ou
 
 void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_inverse_perm, dim3(grid1(n)), dim3(kThreads), 0, s, perm, inv, n);
+}
+
+void inverse_perm2(const int32_t* perm0, int32_t* inv0, int64_t n0, const int32_t* perm1, int32_t* inv1, int64_t n1,
+                   hipStream_t s) {
+  if (n0 + n1 > 0)
+    hipLaunchKernelGGL(k_inverse_perm2, dim3(grid1(n0 + n1)), dim3(kThreads), 0, s, perm0, inv0, n0, perm1, inv1, n1);
+}
+
+bool reframe_rows_cols(const void* in, const int32_t* inv_r, const int32_t* next_r, void* out,
+                       const int32_t* inv_c, const int32_t* next_c, int32_t* rmap, int32_t* cmap, int64_t ncols,
+                       int64_t nrows, int esize, hipStream_t s) {
+  if (nrows <= 0 || ncols <= 0) return true;
+  if (ncols % 8 != 0) return false;
+  const bool pipe = esize == 2 ? pipe_applies<uint16_t>(ncols)
+                               : (esize == 4 ? pipe_applies<uint32_t>(ncols) : pipe_applies<uint8_t>(ncols));
+  if (pipe) {
+    switch (esize) {
+      case 1: launch_gather<uint8_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c); return true;
+      case 2: launch_gather<uint16_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c); return true;
+      case 4: launch_gather<uint32_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c); return true;
+      default: return false;
+    }
+  }
+  compose_perm(inv_r, next_r, rmap, nrows, inv_c, next_c, cmap, ncols, s);
+  return gather_cols(in, ncols, rmap, out, ncols, nullptr, cmap, ncols, nrows, esize, s);
 }
 
 void compose_perm(const int32_t* inv0, const int32_t* next0, int32_t* out0, int64_t n0, const int32_t* inv1,

@@ -23,6 +23,21 @@ void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t stre
 void compose_perm(const int32_t* inv0, const int32_t* next0, int32_t* out0, int64_t n0, const int32_t* inv1,
                   const int32_t* next1, int32_t* out1, int64_t n1, hipStream_t stream);
 
+// inverse_perm for two permutations in one launch.
+void inverse_perm2(const int32_t* perm0, int32_t* inv0, int64_t n0, const int32_t* perm1, int32_t* inv1, int64_t n1,
+                   hipStream_t stream);
+
+// out[r][c] = in[inv_r[next_r[r]]][inv_c[next_c[c]]] for a row-major
+// nrows x ncols matrix (ncols % 8 == 0, element bytes esize): a matrix whose
+// rows and columns are in the frame of one pair of permutations, rewritten in
+// the frame of another (inv_*: inverses of the old permutations, next_*: the
+// new ones). The composition happens inside the gather where rows fit its
+// LDS pipeline; otherwise rmap / cmap (nrows / ncols int32 of scratch)
+// receive the composed maps first.
+bool reframe_rows_cols(const void* in, const int32_t* inv_r, const int32_t* next_r, void* out,
+                       const int32_t* inv_c, const int32_t* next_c, int32_t* rmap, int32_t* cmap, int64_t ncols,
+                       int64_t nrows, int esize, hipStream_t stream);
+
 // out[i] = in[idx[i]] (float), idx clamped to [0, n).
 void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipStream_t stream);
 
@@ -151,6 +166,9 @@ bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int
 // ascending (key, index). keys: n words of scratch. 1 <= n <= kMaxPermDim
 // (returns false otherwise).
 constexpr int64_t kMaxPermDim = int64_t(1) << 20;
+// draws of at most this many indices run in one workgroup's LDS (no use of
+// `keys`); 10 bytes per index plus 4 KB of bucket counters fit 160 KB
+constexpr int64_t kLdsPermMax = 15360;
 bool sample_perm(int64_t n, uint64_t seed, uint64_t tag, uint64_t draw, int32_t* perm, uint64_t* keys,
                  hipStream_t stream);
 

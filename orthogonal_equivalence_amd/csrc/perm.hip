@@ -10,11 +10,20 @@
 // (key, index).
 //
 // With dim <= 2^20 the pair packs into one word, key * 2^20 + i, and these
-// words are distinct. k_perm_keys writes them once; k_perm_rank ranks index i
-// by counting the smaller words, and perm[rank_i] = i writes every entry
-// exactly once. The words are streamed with wave-uniform (scalar) loads and
-// compared with the lane's own word, one 64-bit compare per pair; the count
-// grows as dim^2, which stays small at layer widths.
+// words are distinct; index i's rank is the number of smaller words, and
+// perm[rank_i] = i writes every entry exactly once.
+//
+// Layer widths (dim <= kLdsPermMax) take one workgroup that keeps every word
+// in LDS: a histogram of the words' top 10 bits, its exclusive scan, a
+// scatter of the indices into their buckets, and each index ranked as its
+// bucket's start plus the number of smaller words in its bucket (about
+// dim / 1024 of them). The keys are uniform, so the work grows as dim; one
+// CU does it, leaving the others to whatever else runs. Slot order inside a
+// bucket depends on the order of the LDS atomics, but a rank does not.
+//
+// Wider draws: k_perm_keys writes the words once; k_perm_rank ranks index i
+// by counting the smaller words with wave-uniform (scalar) loads of the
+// words, one 64-bit compare per pair (dim^2 in all).
 
 #include "kernels.hpp"
 
@@ -98,11 +107,91 @@ __global__ __launch_bounds__(64 * kRankWaves) void k_perm_rank(const uint64_t* _
   }
 }
 
+constexpr int kLdsBuckets = 1024;  // top 10 bits of a word
+constexpr int kLdsThreads = 1024;
+
+// Block-wide exclusive scan of kLdsBuckets counters in LDS (one per thread).
+__device__ __forceinline__ void scan_exclusive(uint32_t* cnt, uint32_t* wave_sum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint32_t v = cnt[t];
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wave_sum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t s = lane < kLdsThreads / 64 ? wave_sum[lane] : 0u;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
+    }
+    if (lane < kLdsThreads / 64) wave_sum[lane] = s;  // inclusive over waves
+  }
+  __syncthreads();
+  cnt[t] = x - v + (w ? wave_sum[w - 1] : 0u);
+  __syncthreads();
+}
+
+// The whole draw in one workgroup (dim <= kLdsPermMax): the words, the
+// indices in bucket order, the bucket counters and the scan's wave sums all
+// sit in LDS (157 KB at the largest dim).
+__global__ __launch_bounds__(kLdsThreads) void k_perm_lds(int n, uint64_t seed, uint64_t tag, uint64_t draw,
+                                                          int32_t* __restrict__ perm) {
+  __shared__ uint64_t words[kLdsPermMax];
+  __shared__ uint16_t idx[kLdsPermMax];
+  __shared__ uint32_t cnt[kLdsBuckets];
+  __shared__ uint32_t wave_sum[kLdsThreads / 64];
+  const int t = threadIdx.x;
+  constexpr int kShift = 64 - 10;
+  cnt[t] = 0;
+  __syncthreads();
+  // words and the histogram of their top 10 bits
+  constexpr uint64_t kKeyMask = ~((uint64_t(1) << kKeyShift) - 1);
+  for (int blk = t; 4 * blk < n; blk += kLdsThreads) {
+    uint64_t c[4] = {static_cast<uint64_t>(blk), draw, 0, 0};
+    philox4x64_10(c, seed, tag);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * blk + k;
+      if (i < n) {
+        const uint64_t w = (c[k] & kKeyMask) | static_cast<uint64_t>(i);
+        words[i] = w;
+        atomicAdd(&cnt[w >> kShift], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  scan_exclusive(cnt, wave_sum);  // cnt[b] = first slot of bucket b
+  // indices into their buckets; afterwards cnt[b] = end of bucket b
+  for (int i = t; i < n; i += kLdsThreads) {
+    const uint32_t slot = atomicAdd(&cnt[words[i] >> kShift], 1u);
+    idx[slot] = static_cast<uint16_t>(i);
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += kLdsThreads) {
+    const uint64_t w = words[i];
+    const uint32_t b = static_cast<uint32_t>(w >> kShift);
+    const uint32_t lo = b ? cnt[b - 1] : 0u, hi = cnt[b];
+    uint32_t r = lo;
+    for (uint32_t s = lo; s < hi; ++s) r += words[idx[s]] < w;
+    perm[r] = i;
+  }
+}
+
 }  // namespace
 
 bool sample_perm(int64_t n, uint64_t seed, uint64_t tag, uint64_t draw, int32_t* perm, uint64_t* keys,
                  hipStream_t stream) {
   if (n < 1 || n > kMaxPermDim) return false;
+  if (n <= kLdsPermMax) {
+    hipLaunchKernelGGL(k_perm_lds, dim3(1), dim3(kLdsThreads), 0, stream, static_cast<int>(n), seed,
+                       tag, draw, perm);
+    return true;
+  }
   const int nb = static_cast<int>((n + 3) / 4);
   k_perm_keys<<<(nb + 255) / 256, 256, 0, stream>>>(static_cast<int>(n), seed, tag, draw, keys);
   k_perm_rank<<<static_cast<int>((n + 63) / 64), 64 * kRankWaves, 0, stream>>>(keys, static_cast<int>(n), perm);

@@ -1105,9 +1105,7 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
         return false;
       }
     }
-    inverse_perm(perm_r, w.inv_r, L->m, stream);
-    inverse_perm(perm_p, w.inv_p, L->n, stream);
-    compose_perm(w.inv_r, perm_r_next, w.rmap, L->m, w.inv_p, perm_p_next, w.cmap, L->n, stream);
+    inverse_perm2(perm_r, w.inv_r, L->m, perm_p, w.inv_p, L->n, stream);
     return true;
   };
   bool ok;
@@ -1141,7 +1139,8 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     {
       ProfScope p("merge_reframe", stream);
       ok = ok && reframe_maps();
-      ok = ok && gather_cols(w.C1, L->n, w.rmap, w.C2, L->n, nullptr, w.cmap, L->n, L->m, 4, stream);
+      ok = ok && reframe_rows_cols(w.C1, w.inv_r, perm_r_next, w.C2, w.inv_p, perm_p_next, w.rmap, w.cmap, L->n,
+                                   L->m, 4, stream);
     }
     {
       ProfScope p("merge_requant", stream);
@@ -1187,7 +1186,8 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
   {
     ProfScope p("merge_reframe", stream);
     ok = ok && reframe_maps();
-    ok = ok && gather_cols(M, L->n, w.rmap, wp, L->n, nullptr, w.cmap, L->n, L->m, w_size(L), stream);
+    ok = ok && reframe_rows_cols(M, w.inv_r, perm_r_next, wp, w.inv_p, perm_p_next, w.rmap, w.cmap, L->n, L->m,
+                                 w_size(L), stream);
     fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
   }
   if (wait_status) return wait_status;

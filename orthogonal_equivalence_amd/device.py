@@ -65,6 +65,7 @@ class DeviceLayer:
         # workspace and the event the merge waits for before reading them
         self._side = None
         self._next_r = self._next_p = self._draw_ws = self._drawn = None
+        self._pending = None
         self.reserve(T_max)
 
     # -- buffers --------------------------------------------------------------
@@ -180,13 +181,13 @@ class DeviceLayer:
                        self.g_p, self.q_r, self.q_p, self.ws, None, stream)
         self.perm_r, self.perm_p = nr, np_
 
-    def merge_cycle(self, seed, tag, draw, stream=None):
-        """Draw ``draw`` of both permutations (Psi under tag 2*tag, Phi under
-        2*tag + 1; ``tag`` names the layer), then W0 <- R W0 P with q <- 0
-        written into their frame. The draws do not depend on the merge, so
-        they run on a second stream (default priority) into spare buffers
-        while the merge's block products run; the merge waits for them only
-        before its final gather, and the old permutations become the spares."""
+    def begin_draw(self, seed, tag, draw, stream=None):
+        """Start draw ``draw`` of both permutations (Psi under tag 2*tag, Phi
+        under 2*tag + 1; ``tag`` names the layer) on a second stream (default
+        priority) into spare buffers, and record an event when they are done.
+        A draw depends on nothing, so a training loop can start it well before
+        the merge that uses it (merge_cycle with the same arguments then only
+        waits for the event); merge_cycle starts it itself otherwise."""
         main = stream if stream is not None else torch.cuda.current_stream(self.device)
         if self._side is None:
             self._side = torch.cuda.Stream(device=self.device)
@@ -195,11 +196,22 @@ class DeviceLayer:
             need = px.poetx_workspace_bytes(self.L, 0, px.POETX_OP_SAMPLE_PERM)
             self._draw_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
             self._drawn = torch.cuda.Event()
-        # the spare buffers' earlier readers are on the main stream
+        # the spare buffers' earlier readers (the last merge) are on the main stream
         self._side.wait_stream(main)
         px.poetx_sample_perm(self.m, seed, 2 * tag, draw, self._next_r, self._draw_ws, None, self._side)
         px.poetx_sample_perm(self.n, seed, 2 * tag + 1, draw, self._next_p, self._draw_ws, None, self._side)
         self._drawn.record(self._side)
+        self._pending = (seed, tag, draw)
+
+    def merge_cycle(self, seed, tag, draw, stream=None):
+        """Draw ``draw`` of both permutations (see begin_draw), then
+        W0 <- R W0 P with q <- 0 written into their frame. The merge's block
+        products do not wait for the draws; its final gather does (an event
+        wait on the stream). The old permutations become the spares."""
+        main = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if getattr(self, "_pending", None) != (seed, tag, draw):
+            self.begin_draw(seed, tag, draw, main)
+        self._pending = None
         old_r, old_p = self.perm_r, self.perm_p
         self.merge(self._next_r, self._next_p, self._drawn, main)
         self._next_r, self._next_p = old_r, old_p

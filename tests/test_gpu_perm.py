@@ -28,16 +28,19 @@ def _gpu():
 
 
 DRAWS = [
+    # one workgroup, words in LDS
     (1, 0, 0, 0),
     (3, 5, 1, 0),
-    (64, 7, 2, 1),            # one ranking workgroup exactly
-    (65, 7, 3, 1),            # a second, nearly empty workgroup
-    (511, 11, 4, 2),          # 16 waves x 32-word batches = 512 words per round
-    (512, 11, 4, 3),
-    (513, 11, 5, 4),
-    (2049, 11, 5, 5),         # ragged tails in every wave's range
+    (1023, 7, 2, 1),          # fewer indices than buckets
+    (1025, 7, 3, 1),          # threads take a second index
     (4096, 2024, 0, 1),       # Llama-8B hidden width
+    (4099, 2024, 0, 2),       # last Philox block partly used
     (14336, 2024, 1, 1),      # Llama-8B MLP width
+    (15360, 2024, 1, 2),      # the largest LDS draw
+    # keys in the workspace, ranked by many workgroups
+    (15361, 2024, 1, 3),      # the smallest such draw
+    (15424, 11, 4, 2),        # 241 ranking workgroups exactly
+    (16385, 11, 5, 5),        # ragged tails in every wave's range
     (28672, 1, 2**63 + 5, 2**40),
     (100003, 2**64 - 1, 9, 2**64 - 1),
     (1 << 20, 3, 6, 7),       # the largest accepted dim
