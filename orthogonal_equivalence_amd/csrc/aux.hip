@@ -91,31 +91,42 @@ k_gather_cols_lds(const T* __restrict__ in, int64_t ld_in, const int32_t* __rest
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 16] (larger n waits for all)
-__device__ __forceinline__ void wait_vm16(int n) {
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63] (the counter's range on
+// gfx950; larger n waits for all)
+__device__ __forceinline__ void wait_vm63(int n) {
   switch (n) {
 #define POETX_VM(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-    POETX_VM(1) POETX_VM(2) POETX_VM(3) POETX_VM(4) POETX_VM(5) POETX_VM(6) POETX_VM(7) POETX_VM(8)
-    POETX_VM(9) POETX_VM(10) POETX_VM(11) POETX_VM(12) POETX_VM(13) POETX_VM(14) POETX_VM(15) POETX_VM(16)
+#define POETX_VM8(k) POETX_VM(k) POETX_VM(k + 1) POETX_VM(k + 2) POETX_VM(k + 3) POETX_VM(k + 4) POETX_VM(k + 5) \
+  POETX_VM(k + 6) POETX_VM(k + 7)
+    POETX_VM8(1) POETX_VM8(9) POETX_VM8(17) POETX_VM8(25) POETX_VM8(33) POETX_VM8(41) POETX_VM8(49)
+    POETX_VM(57) POETX_VM(58) POETX_VM(59) POETX_VM(60) POETX_VM(61) POETX_VM(62) POETX_VM(63)
+#undef POETX_VM8
 #undef POETX_VM
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
 
 // Column gather, streaming version for rows of at most kPipeGroups * 8 * 256
-// elements and a multiple of 16 bytes. Each workgroup keeps its threads'
-// source indices in registers (16-bit, loaded once) and walks rows
-// blockIdx.x, blockIdx.x + gridDim.x, ...: a row is copied into one of two LDS
-// buffers with global_load_lds_dwordx4 while the previous row is gathered
-// from the other buffer and written with 16-byte stores.
+// elements and a multiple of 16 bytes. Each workgroup walks rows
+// blockIdx.x, blockIdx.x + gridDim.x, ... through a ring of `nbuf` LDS row
+// buffers: rows are copied in with global_load_lds_dwordx4 nbuf - 1 rows
+// ahead, and each row is gathered out of LDS and written with 16-byte stores.
+// The threads' source indices sit in registers (16-bit), loaded once while
+// the first row is already on its way.
+//
+// Loads and stores share the vector-memory counter, which retires in issue
+// order, so the wait for row k counts what this wave issued after that row's
+// loads: the loads of the rows still ahead of it and the stores of the rows
+// before it. The host keeps that count within the counter's 63.
 constexpr int kPipeGroups = 8;  // column groups of 8 per thread
+constexpr int kPipeMaxBuf = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 2)
 k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
                    T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
                    const int32_t* __restrict__ cidx, int ncols, int64_t nrows,
-                   const int32_t* __restrict__ rmap_pre, const int32_t* __restrict__ cidx_pre) {
+                   const int32_t* __restrict__ rmap_pre, const int32_t* __restrict__ cidx_pre, int nbuf) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,38 +134,16 @@ k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __res
   const int nchunk = row_bytes >> 4;
   const int ninst = (nchunk + 63) >> 6;  // 1 KB load instructions per row
   const int ngroups = ncols >> 3;
-  uint32_t ix[kPipeGroups][4];
-#pragma unroll
-  for (int g = 0; g < kPipeGroups; ++g) {
-    const int grp = tid + g * kThreads;
-    if (grp < ngroups) {
-      int4 i0, i1;
-      if (cidx_pre) {
-        // composed map: column i takes cidx[cidx_pre[i]]
-        const int4 p0 = reinterpret_cast<const int4*>(cidx_pre)[2 * grp];
-        const int4 p1 = reinterpret_cast<const int4*>(cidx_pre)[2 * grp + 1];
-        i0 = make_int4(cidx[clamp_index(p0.x, ncols)], cidx[clamp_index(p0.y, ncols)],
-                       cidx[clamp_index(p0.z, ncols)], cidx[clamp_index(p0.w, ncols)]);
-        i1 = make_int4(cidx[clamp_index(p1.x, ncols)], cidx[clamp_index(p1.y, ncols)],
-                       cidx[clamp_index(p1.z, ncols)], cidx[clamp_index(p1.w, ncols)]);
-      } else {
-        i0 = reinterpret_cast<const int4*>(cidx)[2 * grp];
-        i1 = reinterpret_cast<const int4*>(cidx)[2 * grp + 1];
-      }
-      ix[g][0] = clamp_index(i0.x, ncols) | (clamp_index(i0.y, ncols) << 16);
-      ix[g][1] = clamp_index(i0.z, ncols) | (clamp_index(i0.w, ncols) << 16);
-      ix[g][2] = clamp_index(i1.x, ncols) | (clamp_index(i1.y, ncols) << 16);
-      ix[g][3] = clamp_index(i1.z, ncols) | (clamp_index(i1.w, ncols) << 16);
-    }
-  }
-  // store instructions this wave issues per row (its lane 0 has the lowest group)
-  int my_st = 0;
-#pragma unroll
-  for (int g = 0; g < kPipeGroups; ++g) my_st += (wave * 64 + g * kThreads < ngroups) ? (sizeof(T) == 4 ? 2 : 1) : 0;
+  // rows of this workgroup: blockIdx.x + k * gridDim.x for k < nrow
+  const int64_t r0 = blockIdx.x;
+  if (r0 >= nrows) return;
+  const int nrow = static_cast<int>((nrows - 1 - r0) / gridDim.x + 1);
 
-  auto issue = [&](int64_t r, char* buf) {
+  auto issue = [&](int k) {
+    const int64_t r = r0 + static_cast<int64_t>(k) * gridDim.x;
     const int64_t src = rmap_in ? clamp_index(rmap_in[rmap_pre ? clamp_index(rmap_pre[r], nrows) : r], nrows) : r;
     const char* sp = reinterpret_cast<const char*>(in + src * ld_in);
+    char* buf = lds_raw + (k % nbuf) * row_bytes;
     for (int i = wave; i < ninst; i += kThreads / 64) {
       const int ch = i * 64 + lane;
       if (ch < nchunk)
@@ -162,22 +151,57 @@ k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __res
                                          (lds_void_t)(buf + i * 1024), 16, 0, 0);
     }
   };
+  issue(0);
 
-  int64_t r = blockIdx.x;
-  if (r >= nrows) return;
-  issue(r, lds_raw);
-  int buf = 0;
-  bool first = true;
-  for (; r < nrows; r += gridDim.x) {
-    // this row's loads are followed only by this wave's stores of the previous row
-    wait_vm16(first ? 0 : my_st);
-    first = false;
+  // every group's index loads go out before the first wait (groups past the
+  // row's end load the last group again and are never used); with a composed
+  // map, column i takes cidx[cidx_pre[i]]
+  int4 iv[kPipeGroups][2];
+  const int4* const first = reinterpret_cast<const int4*>(cidx_pre ? cidx_pre : cidx);
+#pragma unroll
+  for (int g = 0; g < kPipeGroups; ++g) {
+    const int grp = min(tid + g * kThreads, ngroups - 1);
+    iv[g][0] = first[2 * grp];
+    iv[g][1] = first[2 * grp + 1];
+  }
+  if (cidx_pre) {
+#pragma unroll
+    for (int g = 0; g < kPipeGroups; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        iv[g][h] = make_int4(cidx[clamp_index(iv[g][h].x, ncols)], cidx[clamp_index(iv[g][h].y, ncols)],
+                             cidx[clamp_index(iv[g][h].z, ncols)], cidx[clamp_index(iv[g][h].w, ncols)]);
+  }
+  uint32_t ix[kPipeGroups][4];
+#pragma unroll
+  for (int g = 0; g < kPipeGroups; ++g) {
+    ix[g][0] = clamp_index(iv[g][0].x, ncols) | (clamp_index(iv[g][0].y, ncols) << 16);
+    ix[g][1] = clamp_index(iv[g][0].z, ncols) | (clamp_index(iv[g][0].w, ncols) << 16);
+    ix[g][2] = clamp_index(iv[g][1].x, ncols) | (clamp_index(iv[g][1].y, ncols) << 16);
+    ix[g][3] = clamp_index(iv[g][1].z, ncols) | (clamp_index(iv[g][1].w, ncols) << 16);
+  }
+  // the rest of the ring's first fill, after the wait for the indices (which
+  // also covers row 0), so that it overlaps the first rows' gathers
+  for (int k = 1; k < nbuf - 1 && k < nrow; ++k) issue(k);
+  // load and store instructions this wave issues per row
+  int my_ld = 0, my_st = 0;
+  for (int i = wave; i < ninst; i += kThreads / 64) ++my_ld;
+#pragma unroll
+  for (int g = 0; g < kPipeGroups; ++g) my_st += (wave * 64 + g * kThreads < ngroups) ? (sizeof(T) == 4 ? 2 : 1) : 0;
+
+  for (int k = 0; k < nrow; ++k) {
+    // issued after row k's loads: the loads of rows k+1 .. k+nbuf-2 and the
+    // stores of rows k-nbuf+1 .. k-1 (those that exist)
+    const int ld_after = min(nbuf - 2, nrow - 1 - k);
+    const int st_after = min(nbuf - 1, k);
+    wait_vm63(ld_after * my_ld + st_after * my_st);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int64_t rn = r + gridDim.x;
-    if (rn < nrows) issue(rn, lds_raw + (buf ^ 1) * row_bytes);
-    const T* L = reinterpret_cast<const T*>(lds_raw + buf * row_bytes);
+    // the ring slot of row k - 1 is free: every wave has read it
+    if (k + nbuf - 1 < nrow) issue(k + nbuf - 1);
+    const T* L = reinterpret_cast<const T*>(lds_raw + (k % nbuf) * row_bytes);
+    const int64_t r = r0 + static_cast<int64_t>(k) * gridDim.x;
     const int64_t dst = rmap_out ? clamp_index(rmap_out[r], nrows) : r;
     T* op = out + dst * ld_out;
     // all LDS reads of the row first (independent registers), then the stores
@@ -202,7 +226,6 @@ k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __res
         store8(op + static_cast<int64_t>(grp) * 8, v);
       }
     }
-    buf ^= 1;
   }
 }
 
@@ -781,18 +804,48 @@ bool pipe_applies(int64_t ncols) {
   return row_bytes % 16 == 0 && ncols <= kPipeGroups * 8 * kThreads && 2 * row_bytes <= 128 * 1024;
 }
 
+#ifndef POETX_PIPE_LDS_KB
+#define POETX_PIPE_LDS_KB 96
+#endif
+
+// Workgroups per CU and ring depth of k_gather_rows_pipe: the most row bytes
+// in flight per CU (per_cu * (nbuf - 1) rows) within POETX_PIPE_LDS_KB of LDS
+// per CU, with the wait count of the kernel's deepest wave within the
+// counter's 63. At the 8B MLP widths this gives 28 KB rows one workgroup with
+// three buffers and 8 KB rows two workgroups with six; a full 160 KB ring
+// measured slower for the 8 KB rows and no faster for the 28 KB ones.
+template <typename T>
+void pipe_shape(int64_t ncols, int* per_cu, int* nbuf) {
+  const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
+  const int64_t ninst = (row_bytes / 16 + 63) / 64;
+  const int64_t ld = (ninst + kThreads / 64 - 1) / (kThreads / 64);
+  const int64_t st = ((ncols / 8 + kThreads - 1) / kThreads) * (sizeof(T) == 4 ? 2 : 1);
+  int64_t best = -1;
+  for (int pc = 1; pc <= 2; ++pc) {
+    int d = static_cast<int>(std::min<int64_t>(kPipeMaxBuf, POETX_PIPE_LDS_KB * 1024 / (pc * row_bytes)));
+    while (d > 2 && (d - 2) * ld + (d - 1) * st > 63) --d;
+    if (d < 2) continue;
+    const int64_t inflight = pc * (d - 1) * row_bytes;
+    if (inflight >= best) {
+      best = inflight;
+      *per_cu = pc;
+      *nbuf = d;
+    }
+  }
+}
+
 template <typename T>
 void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
                    const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, hipStream_t s,
                    const int32_t* rmap_pre = nullptr, const int32_t* cidx_pre = nullptr) {
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
   if (pipe_applies<T>(ncols)) {
-    const int64_t lds = 2 * row_bytes;
-    const int per_cu = static_cast<int>(std::min<int64_t>(2, (160 * 1024) / lds));
+    int per_cu = 1, nbuf = 2;
+    pipe_shape<T>(ncols, &per_cu, &nbuf);
     const unsigned nwg = static_cast<unsigned>(std::min<int64_t>(nrows, 256 * per_cu));
-    hipLaunchKernelGGL(k_gather_rows_pipe<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(lds), s,
+    hipLaunchKernelGGL(k_gather_rows_pipe<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(nbuf * row_bytes), s,
                        static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
-                       static_cast<int>(ncols), nrows, rmap_pre, cidx_pre);
+                       static_cast<int>(ncols), nrows, rmap_pre, cidx_pre, nbuf);
   } else if (row_bytes <= kRowLdsMax) {
     int rows = static_cast<int>(kRowLdsBudget / row_bytes);
     rows = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
