@@ -157,19 +157,26 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
 // plane[J][i][k] in[J k][c] for the b = 256 row blocks J, i.e. Diag(G) W with
 // plane = G - I row-major (the merge's left factor on the rows of W directly).
 // Each wave keeps rows 32w .. 32w+31 of its block's plane as MFMA A fragments
-// for a whole run of columns; 256-row x 32-column tiles go global -> LDS
-// (global_load_lds_dwordx4, two stages), and the B fragments (8 consecutive
-// rows of one column per lane) come from ds_read_b64_tr_b16 on the row-major
-// tile: within each group of 16 lanes, lane j receives element (j % 4) of the
-// 8 bytes addressed by lane 4e + j / 4 (e = 0..3), so with lane i addressing
-// row r0 + i / 4 at column c0 + 4 (i % 4), lane j gets rows r0 .. r0+3 of
-// column c0 + j. Tile rows are 64 bytes, so the 8 rows one read touches fall
-// in distinct bank groups two cycles apart without a swizzle.
+// for a whole run of columns; 256-row x 64-column tiles (128-byte row
+// segments, whole cache lines) go global -> LDS (global_load_lds_dwordx4, two
+// stages), and the B fragments (8 consecutive rows of one column per lane)
+// come from ds_read_b64_tr_b16 on the row-major tile: within each group of 16
+// lanes, lane j receives element (j % 4) of the 8 bytes addressed by lane
+// 4e + j / 4 (e = 0..3), so with lane i addressing row r0 + i / 4 at column
+// c0 + 4 (i % 4), lane j gets rows r0 .. r0+3 of column c0 + j. Chunk c of
+// tile row r sits in slot c ^ 4 ((r / 2) % 2): the 8 rows one read touches
+// (r0 .. r0+3 and r0+8 .. r0+11) then cover each bank twice, the minimum for
+// 512 bytes. The epilogue goes through a per-wave float slab of 16 rows x 32
+// columns (8-column groups swizzled by row), which keeps a workgroup at
+// 80 KB of LDS, two per CU.
+__device__ __forceinline__ int left_slot(int r, int c) { return c ^ (((r >> 1) & 1) << 2); }
+
 __global__ void __launch_bounds__(512, 4)
 k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t ld,
                    const bf16_t* __restrict__ plane, int64_t rows, int64_t ncols, int cols_per_wg, int wgs_per_block) {
-  constexpr int B = 256, TC = 32, ROWB = TC * 2, STAGE = B * ROWB, KS = B / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 8 * 32 * 33 * 4];
+  constexpr int B = 256, TC = 64, ROWB = TC * 2, STAGE = B * ROWB, KS = B / 16;
+  constexpr int SLAB = 16 * 32;  // floats per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 8 * SLAB * 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   // the workgroups of one block run on one XCD (one L2 holds its plane)
@@ -191,15 +198,17 @@ k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int6
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) afrag[kk] = *reinterpret_cast<const bf16x8_t*>(arow + kk * 16);
 
-  // loads: 16 instructions of 16 rows x 64 bytes per stage, two per wave;
-  // rows past a short block re-read its last row, columns past the end its
-  // last 8 columns (neither reaches a stored output)
+  // loads: 32 instructions of 8 rows x 128 bytes per stage, four per wave;
+  // lane l lands in slot l % 8 of row 8 q + l / 8 and fetches the chunk that
+  // belongs there. Rows past a short block re-read its last row, columns past
+  // the end its last 8 columns (neither reaches a stored output).
   auto issue = [&](int sub, int stage) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = wave * 2 + u;
-      const int r = q * 16 + (lane >> 2);
-      int64_t c = c_begin + static_cast<int64_t>(sub) * TC + (lane & 3) * 8;
+    for (int u = 0; u < 4; ++u) {
+      const int q = wave * 4 + u;
+      const int r = q * 8 + (lane >> 3);
+      const int ch = left_slot(r, lane & 7);
+      int64_t c = c_begin + static_cast<int64_t>(sub) * TC + ch * 8;
       c = c < ncols - 8 ? c : ncols - 8;
       const int rr = r < height ? r : height - 1;
       const bf16_t* src = in + (row0 + rr) * ld + c;
@@ -208,11 +217,19 @@ k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int6
     }
   };
 
-  // transposed-read address of this lane (k rows kb + 8 (G / 2) + i / 4,
-  // column 16 (G % 2) + 4 (i % 4)) for kb = 0; +256 bytes per 4 rows
+  // transposed-read address of this lane for K rows kb = 0 and column tile ct:
+  // row 8 (G / 2) + i / 4, column 32 ct + 16 (G % 2) + 4 (i % 4). Rows +4
+  // (second half of a fragment) and +16 (next K group) keep the row's slot
+  // pattern, so they are immediate offsets of 512 and 2048 bytes.
   const int grp = lane >> 4, li = lane & 15;
   const int rd_row = 8 * (grp >> 1) + (li >> 2), rd_col = 16 * (grp & 1) + 4 * (li & 3);
-  float* slab = reinterpret_cast<float*>(smem + 2 * STAGE) + wave * 32 * 33;
+  uint32_t rd_off[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int col = ct * 32 + rd_col;
+    rd_off[ct] = static_cast<uint32_t>(rd_row * ROWB + (left_slot(rd_row, col >> 3) << 4) + (col & 7) * 2);
+  }
+  float* slab = reinterpret_cast<float*>(smem + 2 * STAGE) + wave * SLAB;
   typedef unsigned long long u64;
   typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
@@ -222,55 +239,63 @@ k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int6
     __syncthreads();
     if (s + 1 < nsub) issue(s + 1, (s + 1) & 1);
     const char* st = smem + (s & 1) * STAGE;
-    // 32 transposed reads (16 k groups x 2 halves) in four self-waiting asm
-    // blocks of 4 k groups: k group kk adds 16 rows (1024 bytes), the second
-    // half of a fragment 4 rows (256 bytes)
-    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st + rd_row * ROWB + rd_col * 2));
-    f32x16_t acc;
+    const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int ct = 0; ct < 2; ++ct) {
+      f32x16_t acc;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      u64 t[8];
-      const uint32_t bh = base + h * 4 * 1024;
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %8 offset:256\n"
-          "ds_read_b64_tr_b16 %2, %8 offset:1024\n ds_read_b64_tr_b16 %3, %8 offset:1280\n"
-          "ds_read_b64_tr_b16 %4, %8 offset:2048\n ds_read_b64_tr_b16 %5, %8 offset:2304\n"
-          "ds_read_b64_tr_b16 %6, %8 offset:3072\n ds_read_b64_tr_b16 %7, %8 offset:3328\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]),
-            "=&v"(t[7])
-          : "v"(bh)
-          : "memory");
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      // 32 transposed reads (16 K groups x 2 halves) in eight self-waiting
+      // asm blocks of 2 K groups
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            afrag[4 * h + k4], __builtin_bit_cast(bf16x8_t, u64x2{t[2 * k4], t[2 * k4 + 1]}), acc, 0, 0, 0);
-    }
-    // accumulator -> slab (32 rows x 32 columns); per lane 8 consecutive
-    // columns of a row: + residual from the staged tile, one 16-byte store
+      for (int h = 0; h < 8; ++h) {
+        u64 t[4];
+        const uint32_t bh = sbase + rd_off[ct] + h * 2 * 2048;
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n ds_read_b64_tr_b16 %1, %4 offset:512\n"
+            "ds_read_b64_tr_b16 %2, %4 offset:2048\n ds_read_b64_tr_b16 %3, %4 offset:2560\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+            : "v"(bh)
+            : "memory");
 #pragma unroll
-    for (int r = 0; r < 16; ++r) slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 33 + lrow] = acc[r];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = lane + i * 64;
-      const int row = q >> 2, c4 = q & 3;  // row within the wave's 32, 8-column chunk
-      const int grow = wave * 32 + row;
-      const int64_t c = c_begin + static_cast<int64_t>(s) * TC + c4 * 8;
-      const uint4 xr = *reinterpret_cast<const uint4*>(st + grow * ROWB + c4 * 16);
-      const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = slab[row * 33 + c4 * 8 + 2 * e] + __uint_as_float(xw[e] << 16);
-        v[2 * e + 1] = slab[row * 33 + c4 * 8 + 2 * e + 1] + __uint_as_float(xw[e] & 0xffff0000u);
+        for (int k2 = 0; k2 < 2; ++k2)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              afrag[2 * h + k2], __builtin_bit_cast(bf16x8_t, u64x2{t[2 * k2], t[2 * k2 + 1]}), acc, 0, 0, 0);
       }
-      if (grow < height && c < c_end)
-        *reinterpret_cast<uint4*>(out + (row0 + grow) * ld + c) =
-            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7]));
+      // per half of the wave's 32 rows: accumulators -> slab (16 rows x 32
+      // columns), then per lane 8 consecutive columns of a row: + residual
+      // from the staged tile, one 16-byte store
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int r = 8 * hh; r < 8 * hh + 8; ++r) {
+          const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) - 16 * hh;
+          slab[row * 32 + ((((lrow >> 3) ^ ((row >> 1) & 3))) << 3) + (lrow & 7)] = acc[r];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int row = lane >> 2, c4 = lane & 3;  // row within the half, 8-column chunk
+        const int grow = wave * 32 + 16 * hh + row;
+        const int64_t c = c_begin + static_cast<int64_t>(s) * TC + ct * 32 + c4 * 8;
+        const uint4 xr = *reinterpret_cast<const uint4*>(st + grow * ROWB + (left_slot(grow, ct * 4 + c4) << 4));
+        const float* sp = slab + row * 32 + ((c4 ^ ((row >> 1) & 3)) << 3);
+        const float4 a0 = *reinterpret_cast<const float4*>(sp);
+        const float4 a1 = *reinterpret_cast<const float4*>(sp + 4);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = av[2 * e] + __uint_as_float(xw[e] << 16);
+          v[2 * e + 1] = av[2 * e + 1] + __uint_as_float(xw[e] & 0xffff0000u);
+        }
+        if (grow < height && c < c_end)
+          *reinterpret_cast<uint4*>(out + (row0 + grow) * ld + c) =
+              make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7]));
+        // every lane's slab reads are complete before the next tile's writes
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
     }
   }
 }
@@ -282,10 +307,10 @@ bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const 
   if (rows <= 0 || ncols <= 0) return true;
   if (b != 256 || ncols % 8 != 0 || ncols < 8) return false;
   const int nblk = static_cast<int>((rows + b - 1) / b);
-  // two 512-thread workgroups per CU (registers) -> 512 resident
+  // two 512-thread workgroups per CU (LDS) -> 512 resident
   int64_t wpb = std::max<int64_t>(1, 512 / nblk);
   int64_t cpw = (ncols + wpb - 1) / wpb;
-  cpw = (cpw + 31) / 32 * 32;
+  cpw = (cpw + 63) / 64 * 64;
   wpb = (ncols + cpw - 1) / cpw;
   hipLaunchKernelGGL(k_block_apply_left, dim3(static_cast<unsigned>(nblk * wpb)), dim3(512), 0, s,
                      reinterpret_cast<const bf16_t*>(in), reinterpret_cast<bf16_t*>(out), ld,

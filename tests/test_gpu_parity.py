@@ -142,6 +142,9 @@ SMALL = [
     # the smallest block size the library takes, b = 8
     _cfg("f32_b8", 40, 48, 64, 8, 8, "f32", "f32", 54),
     _cfg("bf16_b8", 40, 48, 64, 8, 8, "bf16", "bf16", 55),
+    # a weight width that ends inside a 64-column tile of the merge's left
+    # product (1000 = 15*64 + 40), with a short last P block (1000 = 3*256 + 232)
+    _cfg("bf16_left_ragged_cols", 200, 512, 1000, 256, 256, "bf16", "bf16", 56),
 ]
 
 
