@@ -395,21 +395,26 @@ bool gemm(const poetx_layer* L, const GemmDesc& d, int am, int bm, int ct, hipSt
 }
 
 // The dense W0 product: the specialised kernel when its shape constraints
-// hold, else the general engine. An int8 weight goes through it too, as a
-// bfloat16 copy of its codes made just before the product (see i8_staging).
+// hold, else the general engine.
 bool dense_kernel_applies(const poetx_layer* L, int N, int K) {
   return is_bf16(L) && K % 64 == 0 && N % 8 == 0;
+}
+
+// ... with B as int8 codes, converted inside the kernel: the code rows must
+// also be whole 16-byte chunks (see i8_staging for the other widths)
+bool dense_i8_applies(const poetx_layer* L, int N, int K, int64_t ldb) {
+  return dense_kernel_applies(L, N, K) && N % 16 == 0 && ldb % 16 == 0;
 }
 
 // The quantised variant stores the base weight as int8 and dequantises it at
 // run time (section "POET-XQ"): the dense kernel reads the int8 codes and
 // turns them into bfloat16 on their way into LDS (exact); its epilogue (or
 // the preceding apply, in the backward) applies the column scales. Where the
-// dense kernel's shape rules fail, the backward's general engine reads the
-// codes itself, and the forward (which reads Wp N-contiguous) copies them to
-// bfloat16 in the workspace first.
+// dense kernel's int8 shape rules fail, the backward's general engine reads
+// the codes itself, and the forward (which reads Wp N-contiguous) copies them
+// to bfloat16 in the workspace first.
 bool i8_staging(const poetx_layer* L) {
-  return L->w_dtype == POETX_I8 && !dense_kernel_applies(L, static_cast<int>(L->n), static_cast<int>(L->m));
+  return L->w_dtype == POETX_I8 && !dense_i8_applies(L, static_cast<int>(L->n), static_cast<int>(L->m), L->n);
 }
 
 // Workspace of the dense kernel's split of a partial last round of tiles.
@@ -422,7 +427,8 @@ size_t dense_split_bytes(const poetx_layer* L, int64_t M, int64_t N, int64_t K) 
 // are K-contiguous (the backward). i8: B holds int8 codes (K-contiguous only).
 bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, bool b_ncontig, void* split_ws,
                    hipStream_t st) {
-  if (dense_kernel_applies(L, d.N, d.K)) return gemm_dense_bf16(d, split_ws, st, b_ncontig, i8);
+  if (i8 ? dense_i8_applies(L, d.N, d.K, d.ldb) : dense_kernel_applies(L, d.N, d.K))
+    return gemm_dense_bf16(d, split_ws, st, b_ncontig, i8);
   if (b_ncontig) return !i8 && gemm(L, d, A_KCONTIG, B_NCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
   return gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
 }

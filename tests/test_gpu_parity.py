@@ -145,6 +145,11 @@ SMALL = [
     # a weight width that ends inside a 64-column tile of the merge's left
     # product (1000 = 15*64 + 40), with a short last P block (1000 = 3*256 + 232)
     _cfg("bf16_left_ragged_cols", 200, 512, 1000, 256, 256, "bf16", "bf16", 56),
+    # int8 weight whose widths are not multiples of 64 (the dense kernel's K
+    # step): the forward multiplies a bfloat16 copy of the codes in the general
+    # engine, the backward reads the codes in the general engine; short last
+    # blocks of 16 on both sides (528 = 4*128 + 16, 1040 = 8*128 + 16)
+    _cfg("xq_widths_not_64", 200, 528, 1040, 128, 128, "bf16", "i8", 57),
 ]
 
 
