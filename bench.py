@@ -177,7 +177,7 @@ def algorithmic_work(cfg):
         "apply_r_bwd": (2 * es * T * m, 2.0 * T * m * br),
         "grad_g": (2 * es * T * m + 4 * nr * br * br, 2.0 * T * m * br),
         "scatter_dx": (2 * es * T * m, 0.0),
-        "cnp_bwd": (4 * blk + 8 * (pr + pp), 8.0 * cube),
+        "cnp_bwd": (4 * blk + 8 * (pr + pp), 10.0 * cube),
         "merge_left": (2 * wes * m * n, 2.0 * m * n * br),
         "merge_transpose": (2 * wes * m * n, 0.0),
         "merge_right": (2 * wes * m * n, 2.0 * m * n * bp),

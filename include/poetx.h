@@ -166,9 +166,11 @@ POETX_API int poetx_weight_export(const poetx_layer* L, const void* wp, const fl
  *   wp: permuted-frame weight (poetx_weight_prepare, poetx_merge);
  *   wscale_p: its column scales (I8 only, else ignored).
  *   saved: poetx_saved_bytes(L, T) bytes, overwritten with X1 and Y1.
- * An int8 weight is dequantised at run time (section "POET-XQ"): its codes are
- * copied to bfloat16 (exact) in the workspace and the dense product applies
- * the column scales in its epilogue. T == 0 launches nothing. */
+ * An int8 weight is dequantised at run time (section "POET-XQ"): the dense
+ * product turns its codes into bfloat16 (exact) on their way into on-chip
+ * memory and applies the column scales in its epilogue; when m or n is not a
+ * multiple of 64 the codes are first copied to bfloat16 in the workspace.
+ * T == 0 launches nothing. */
 POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
                   const int32_t* perm_r, const int32_t* perm_p,
                   const void* g_r, const void* g_p,
@@ -186,8 +188,8 @@ POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
  * m < T, the P-side product dY1 = dY2 H^T is not formed: the dense product
  * takes dY2 and the weight Wp H (built in the workspace), which is the same
  * dX2 = dY2 H^T Wp^T with fewer bytes moved. For an int8 weight, dY1 takes the
- * column scales and the dense product reads a bfloat16 copy of Wp's codes made
- * in the workspace. */
+ * column scales and the dense product reads Wp's codes, converting them to
+ * bfloat16 (exact) itself. */
 POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const void* dz,
                    const int32_t* perm_r, const int32_t* perm_p,
                    const float* q_r, const float* q_p,

@@ -128,8 +128,8 @@ SMALL = [
     # every tile into four K parts, whose fp32 partial tiles a second kernel
     # adds in fixed part order
     _cfg("bf16_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 36),
-    # the same with an int8 weight: codes copied to bfloat16, column scales in
-    # the split sum's epilogue
+    # the same with an int8 weight: codes converted to bfloat16 inside the
+    # dense kernel, column scales in the split sum's epilogue
     _cfg("xq_split_k", 300, 2048, 2304, 256, 256, "bf16", "i8", 39),
     # one block per side: R's block size exceeds m (a single short block of
     # 64), P is exactly one block
