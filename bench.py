@@ -176,6 +176,7 @@ def algorithmic_work(cfg):
         "gemm_dense_bwd": (dense[1], dense[0]),
         "apply_r_bwd": (2 * es * T * m, 2.0 * T * m * br),
         "grad_g": (2 * es * T * m + 4 * nr * br * br, 2.0 * T * m * br),
+        "grad_gh": (2 * es * T * (m + n) + 4 * blk, 2.0 * T * (m * br + n * bp)),
         "scatter_dx": (2 * es * T * m, 0.0),
         "cnp_bwd": (4 * blk + 8 * (pr + pp), 10.0 * cube),
         "merge_left": (2 * wes * m * n, 2.0 * m * n * br),

@@ -253,11 +253,16 @@ __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __rest
   POETX_GRID_STRIDE(i, n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
 }
 
+// Inverses of two permutations, and (optionally, in the same launch) two
+// float arrays set to zero.
 __global__ void k_inverse_perm2(const int32_t* __restrict__ perm0, int32_t* __restrict__ inv0, int64_t n0,
-                                const int32_t* __restrict__ perm1, int32_t* __restrict__ inv1, int64_t n1) {
-  POETX_GRID_STRIDE(i, n0 + n1) {
+                                const int32_t* __restrict__ perm1, int32_t* __restrict__ inv1, int64_t n1,
+                                float* __restrict__ z0, int64_t nz0, float* __restrict__ z1, int64_t nz1) {
+  POETX_GRID_STRIDE(i, n0 + n1 + nz0 + nz1) {
     if (i < n0) inv0[clamp_index(perm0[i], n0)] = static_cast<int32_t>(i);
-    else inv1[clamp_index(perm1[i - n0], n1)] = static_cast<int32_t>(i - n0);
+    else if (i < n0 + n1) inv1[clamp_index(perm1[i - n0], n1)] = static_cast<int32_t>(i - n0);
+    else if (i < n0 + n1 + nz0) z0[i - n0 - n1] = 0.f;
+    else z1[i - n0 - n1 - nz0] = 0.f;
   }
 }
 
@@ -882,9 +887,11 @@ void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s) {
 }
 
 void inverse_perm2(const int32_t* perm0, int32_t* inv0, int64_t n0, const int32_t* perm1, int32_t* inv1, int64_t n1,
-                   hipStream_t s) {
-  if (n0 + n1 > 0)
-    hipLaunchKernelGGL(k_inverse_perm2, dim3(grid1(n0 + n1)), dim3(kThreads), 0, s, perm0, inv0, n0, perm1, inv1, n1);
+                   hipStream_t s, float* z0, int64_t nz0, float* z1, int64_t nz1) {
+  const int64_t total = n0 + n1 + nz0 + nz1;
+  if (total > 0)
+    hipLaunchKernelGGL(k_inverse_perm2, dim3(grid1(total)), dim3(kThreads), 0, s, perm0, inv0, n0, perm1, inv1, n1,
+                       z0, nz0, z1, nz1);
 }
 
 bool reframe_rows_cols(const void* in, const int32_t* inv_r, const int32_t* next_r, void* out,

@@ -44,15 +44,23 @@ constexpr int STAGE = 2 * TILE;     // act + dout
 // four rows over all 16 bank groups, two cycles per read.
 __device__ __forceinline__ int slot(int r, int c) { return c ^ ((r & 3) << 2); }
 
-struct GradArgs {
+// One side's operands: act and dout [T][dim] (row stride dim), partials
+// [nsplit][nblk][b][b].
+struct GradSide {
   const bf16_t* act;
   const bf16_t* dout;
-  float* part;          // [nsplit][nblk][b][b]
-  int64_t ld;           // row stride of act and dout (elements)
+  float* part;
   int64_t dim;          // row width (short last block)
+  int nblk;
+};
+
+// Up to two sides with the same block size and token split in one launch:
+// workgroups [0, wgs0) take side 0, the rest side 1.
+struct GradArgs {
+  GradSide side[2];
+  int wgs0;
   int64_t T;
   int b;                // block size (256 or 512)
-  int nblk;
   int slices;           // b / 256
   int tokens_per_wg;
   int nsplit;
@@ -67,16 +75,19 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // workgroup -> (block, slice pair, split)
+  // workgroup -> (side, block, slice pair, split)
   const int pairs = g.slices * g.slices;
   int w = blockIdx.x;
+  const bool second = w >= g.wgs0;
+  const GradSide sd = second ? g.side[1] : g.side[0];
+  if (second) w -= g.wgs0;
   const int split = w % g.nsplit;
   w /= g.nsplit;
   const int pair = w % pairs;
   const int blk = w / pairs;
   const int si = pair / g.slices, sc = pair % g.slices;
   const int64_t blk0 = static_cast<int64_t>(blk) * g.b;
-  const int width = static_cast<int>(min(static_cast<int64_t>(g.b), g.dim - blk0));
+  const int width = static_cast<int>(min(static_cast<int64_t>(g.b), sd.dim - blk0));
   const int a0 = si * S, d0 = sc * S;  // slice offsets inside the block
   const int64_t t_begin = static_cast<int64_t>(split) * g.tokens_per_wg;
   const int64_t t_end = min(g.T, t_begin + g.tokens_per_wg);
@@ -100,7 +111,7 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
       f = f < width - 8 ? f : width - 8;
       int64_t t = t_begin + static_cast<int64_t>(sub) * TK + row;
       t = t < t_end ? t : t_end - 1;
-      const bf16_t* src = (op ? g.dout : g.act) + t * g.ld + blk0 + f;
+      const bf16_t* src = (op ? sd.dout : sd.act) + t * sd.dim + blk0 + f;
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
                                        (lds_void_t)(st + op * TILE + inst * 1024), 16, 0, 0);
     }
@@ -228,7 +239,7 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
 
   // partial for this split: rows a0 + i, columns d0 + c of the b x b block;
   // entries outside a short block are stored as zeros
-  float* out = g.part + (static_cast<int64_t>(split) * g.nblk + blk) * g.b * g.b;
+  float* out = sd.part + (static_cast<int64_t>(split) * sd.nblk + blk) * g.b * g.b;
   const int lrow = lane & 31;
 #pragma unroll
   for (int i = 0; i < TMw; ++i)
@@ -244,14 +255,15 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
 
 }  // namespace
 
-// Splits of the token range: as many as fit one round of workgroups on the
+// Splits of the token range for blocks of b over `dim` features (plus dim1
+// more in the same launch): as many as fit one round of workgroups on the
 // 256 CUs (one 128 KB-LDS workgroup per CU), so that no partial second round
 // doubles the time; at least 8 sub-tiles of tokens per split.
-int block_grad_splits(int64_t T, int64_t dim, int b) {
+int block_grad_splits(int64_t T, int64_t dim, int b, int64_t dim1) {
   if (b != 256 && b != 512) return 0;
-  const int nblk = static_cast<int>((dim + b - 1) / b);
   const int slices = b / S;
-  const int64_t units = static_cast<int64_t>(nblk) * slices * slices;
+  const int64_t nblk = (dim + b - 1) / b + (dim1 + b - 1) / b;
+  const int64_t units = nblk * slices * slices;
   int64_t ns = std::max<int64_t>(1, 256 / units);
   ns = std::max<int64_t>(1, std::min<int64_t>(ns, (T + 8 * TK - 1) / (8 * TK)));
   int64_t tpw = (T + ns - 1) / ns;
@@ -259,27 +271,41 @@ int block_grad_splits(int64_t T, int64_t dim, int b) {
   return static_cast<int>(std::max<int64_t>(1, (T + tpw - 1) / tpw));
 }
 
-bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int64_t ld, int64_t T, int64_t dim,
-                     int b, int nsplit, hipStream_t s) {
+bool block_grad2_bf16(const uint16_t* act0, const uint16_t* dout0, float* part0, int64_t dim0,
+                      const uint16_t* act1, const uint16_t* dout1, float* part1, int64_t dim1, int64_t T, int b,
+                      int nsplit, hipStream_t s) {
   if (b != 256 && b != 512) return false;
   if (T <= 0 || nsplit <= 0) return true;
   GradArgs g;
-  g.act = act;
-  g.dout = dout;
-  g.part = part;
-  g.ld = ld;
-  g.dim = dim;
   g.T = T;
   g.b = b;
-  g.nblk = static_cast<int>((dim + b - 1) / b);
   g.slices = b / S;
   int64_t tpw = (T + nsplit - 1) / nsplit;
   tpw = (tpw + TK - 1) / TK * TK;
   g.tokens_per_wg = static_cast<int>(tpw);
   g.nsplit = nsplit;
-  const unsigned grid = static_cast<unsigned>(g.nblk * g.slices * g.slices * nsplit);
-  hipLaunchKernelGGL(k_block_grad, dim3(grid), dim3(NT), 0, s, g);
+  const uint16_t* act[2] = {act0, act1};
+  const uint16_t* dout[2] = {dout0, dout1};
+  float* part[2] = {part0, part1};
+  const int64_t dim[2] = {dim0, dim1};
+  int wgs[2];
+  for (int k = 0; k < 2; ++k) {
+    g.side[k].act = reinterpret_cast<const bf16_t*>(act[k]);
+    g.side[k].dout = reinterpret_cast<const bf16_t*>(dout[k]);
+    g.side[k].part = part[k];
+    g.side[k].dim = dim[k];
+    g.side[k].nblk = act[k] ? static_cast<int>((dim[k] + b - 1) / b) : 0;
+    wgs[k] = g.side[k].nblk * g.slices * g.slices * nsplit;
+  }
+  g.wgs0 = wgs[0];
+  if (wgs[0] + wgs[1] > 0) hipLaunchKernelGGL(k_block_grad, dim3(static_cast<unsigned>(wgs[0] + wgs[1])), dim3(NT), 0, s, g);
   return true;
+}
+
+bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int64_t ld, int64_t T, int64_t dim,
+                     int b, int nsplit, hipStream_t s) {
+  if (ld != dim) return false;
+  return block_grad2_bf16(act, dout, part, dim, nullptr, nullptr, nullptr, 0, T, b, nsplit, s);
 }
 
 }  // namespace poetx

@@ -23,9 +23,10 @@ void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t stre
 void compose_perm(const int32_t* inv0, const int32_t* next0, int32_t* out0, int64_t n0, const int32_t* inv1,
                   const int32_t* next1, int32_t* out1, int64_t n1, hipStream_t stream);
 
-// inverse_perm for two permutations in one launch.
+// inverse_perm for two permutations in one launch, which also sets the
+// float arrays z0 [nz0] and z1 [nz1] to zero (none by default).
 void inverse_perm2(const int32_t* perm0, int32_t* inv0, int64_t n0, const int32_t* perm1, int32_t* inv1, int64_t n1,
-                   hipStream_t stream);
+                   hipStream_t stream, float* z0 = nullptr, int64_t nz0 = 0, float* z1 = nullptr, int64_t nz1 = 0);
 
 // out[r][c] = in[inv_r[next_r[r]]][inv_c[next_c[c]]] for a row-major
 // nrows x ncols matrix (ncols % 8 == 0, element bytes esize): a matrix whose
@@ -155,10 +156,15 @@ bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const 
 // 256 or 512: part[s][j][i][c] = sum over the tokens of split s of
 // act[t][j*b + i] * dout[t][j*b + c], written for every (i, c) < b (zeros
 // outside a short last block). block_grad_splits gives the split count the
-// kernel uses for T tokens (0 if b is not 256 or 512).
-int block_grad_splits(int64_t T, int64_t dim, int b);
+// kernel uses for T tokens (0 if b is not 256 or 512), for dim features plus
+// dim1 more of a second side in the same launch. block_grad2_bf16 runs two
+// sides with the same b and split count in one launch (act1 null: one side).
+int block_grad_splits(int64_t T, int64_t dim, int b, int64_t dim1 = 0);
 bool block_grad_bf16(const uint16_t* act, const uint16_t* dout, float* part, int64_t ld, int64_t T, int64_t dim,
                      int b, int nsplit, hipStream_t stream);
+bool block_grad2_bf16(const uint16_t* act0, const uint16_t* dout0, float* part0, int64_t dim0,
+                      const uint16_t* act1, const uint16_t* dout1, float* part1, int64_t dim1, int64_t T, int b,
+                      int nsplit, hipStream_t stream);
 
 // Seeded uniformly random permutation of [0, n) (perm.hip): index i's key is
 // the top 44 bits of word i mod 4 of Philox4x64-10 at counter

@@ -109,10 +109,18 @@ struct Split {
   int kchunk;
 };
 
+// Both sides' token sums in one launch after the rest of the backward
+// (nothing needs dH before the CNP adjoint): one split count sized for the
+// blocks of both sides, which halves the float partials against two launches
+// each filling the GPU on its own.
+bool grads_merged(const poetx_layer* L) {
+  return is_bf16(L) && L->b_r == L->b_p && (L->b_r == 256 || L->b_r == 512);
+}
+
 Split token_split(const poetx_layer* L, const Side& s, int64_t T) {
   if (is_bf16(L) && (s.b == 256 || s.b == 512)) {
     Split r;
-    r.nsplit = std::max(1, block_grad_splits(T, s.dim, s.b));
+    r.nsplit = std::max(1, grads_merged(L) ? block_grad_splits(T, L->m, s.b, L->n) : block_grad_splits(T, s.dim, s.b));
     r.kchunk = 0;
     return r;
   }
@@ -230,6 +238,7 @@ FwdWs plan_fwd(const poetx_layer* L, int64_t T, Carve& c) {
 
 struct BwdWs {
   void *bufA, *bufB;
+  void* bufC;         // [T][m]: keeps dY2 alive for the merged token sums (or null)
   void* wh;           // Wp H (m x n), when the backward folds H into the weight
   int32_t* inv_r;
   float *part_r, *part_p;
@@ -251,6 +260,7 @@ BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   const int64_t Tn = std::max<int64_t>(T, 1);
   w.bufA = c.take<char>(T * rowmax * act_size(L));
   w.bufB = c.take<char>(T * rowmax * act_size(L));
+  w.bufC = grads_merged(L) ? c.take<char>(T * L->m * act_size(L)) : nullptr;
   w.wh = fold_h(L, T) ? c.take<char>(L->m * L->n * w_size(L)) : nullptr;
   w.inv_r = c.take<int32_t>(L->m);
   w.part_r = c.take<float>(static_cast<int64_t>(token_split(L, R, Tn).nsplit) * block_elems(R));
@@ -759,27 +769,33 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
     ok = gather_cols(dz, L->n, nullptr, w.bufA, L->n, nullptr, perm_p, L->n, T, es, stream);
   }
   const Split spP = token_split(L, P, T);
-  {
+  const bool merged = grads_merged(L);
+  void* const dY2 = w.bufA;
+  if (!merged) {
     ProfScope p("grad_h", stream);
-    ok = ok && block_token_grad(L, P, T, Y1, w.bufA, w.part_p, spP, stream);
+    ok = ok && block_token_grad(L, P, T, Y1, dY2, w.part_p, spP, stream);
   }
+  // buffers: dY2 in bufA; with the merged token sums it stays there until
+  // the end, and the [T][m] results use bufB and bufC
   GemmDesc d;
   d.dense = 1;
+  void* dX1;
   if (fold) {
     ProfScope p("fold_h_bwd", stream);
     ok = ok && block_apply(L, P, L->m, wp, w.wh, g_p, 1, nullptr, stream);
-    d.A = w.bufA;
+    d.A = dY2;
     d.B = w.wh;
     d.C = w.bufB;
+    dX1 = merged ? w.bufC : w.bufA;
   } else {
     ProfScope p("apply_p_bwd", stream);
-    ok = ok && block_apply(L, P, T, w.bufA, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
+    ok = ok && block_apply(L, P, T, dY2, w.bufB, g_p, 0, i8 ? wscale_p : nullptr, stream);
     d.A = w.bufB;
     d.B = wp;
-    d.C = w.bufA;
+    d.C = merged ? w.bufC : w.bufA;
+    dX1 = w.bufB;
   }
   void* const dX2 = d.C;
-  void* const dX1 = fold ? w.bufA : w.bufB;
   d.lda = L->n;
   d.ldb = L->n;
   d.ldc = L->m;
@@ -796,7 +812,7 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
     ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream);
   }
   const Split spR = token_split(L, R, T);
-  {
+  if (!merged) {
     ProfScope p("grad_g", stream);
     ok = ok && block_token_grad(L, R, T, X1, dX2, w.part_r, spR, stream);
   }
@@ -804,6 +820,12 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
     ProfScope p("scatter_dx", stream);
     inverse_perm(perm_r, w.inv_r, L->m, stream);
     ok = ok && gather_cols(dX1, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
+  }
+  if (merged) {
+    ProfScope p("grad_gh", stream);
+    ok = ok && block_grad2_bf16(static_cast<const uint16_t*>(X1), static_cast<const uint16_t*>(dX2), w.part_r, L->m,
+                                static_cast<const uint16_t*>(Y1), static_cast<const uint16_t*>(dY2), w.part_p, L->n,
+                                T, R.b, spR.nsplit, stream);
   }
   // dq_r, dq_p from the token sums dG, dH
   {
@@ -1111,7 +1133,8 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
         return false;
       }
     }
-    inverse_perm2(perm_r, w.inv_r, L->m, perm_p, w.inv_p, L->n, stream);
+    // q <- 0 in the same launch: the merge reads only the CNP planes
+    inverse_perm2(perm_r, w.inv_r, L->m, perm_p, w.inv_p, L->n, stream, q_r, packed_len(R), q_p, packed_len(P));
     return true;
   };
   bool ok;
@@ -1152,7 +1175,6 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
       ProfScope p("merge_requant", stream);
       ok = ok && requant_i8_cols(static_cast<const float*>(w.C2), w.amax, static_cast<int8_t*>(wp), wscale_p, L->m,
                                  L->n, stream);
-      fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
     }
     if (wait_status) return wait_status;
     if (!ok) return POETX_EUNSUPPORTED;
@@ -1194,7 +1216,6 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     ok = ok && reframe_maps();
     ok = ok && reframe_rows_cols(M, w.inv_r, perm_r_next, wp, w.inv_p, perm_p_next, w.rmap, w.cmap, L->n, L->m,
                                  w_size(L), stream);
-    fill_zero2_f32(q_r, packed_len(R), q_p, packed_len(P), stream);
   }
   if (wait_status) return wait_status;
   if (!ok) return POETX_EUNSUPPORTED;

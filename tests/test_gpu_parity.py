@@ -454,3 +454,16 @@ def test_profile_log_fold_path():
         px.poetx_profile_enable(0)
     names = [px.poetx_profile_get(i)[0] for i in range(px.poetx_profile_count())]
     assert "fold_h_bwd" in names and "apply_p_bwd" not in names, names
+
+
+def test_profile_log_merged_token_sums():
+    # equal bf16 block sizes of 256: one token-sum launch for both sides at
+    # the end of the backward
+    cfg = _cfg("profile_merged", 300, 512, 768, 256, 256, "bf16", "bf16", 59)
+    px.poetx_profile_enable(1)
+    try:
+        _run(cfg)
+    finally:
+        px.poetx_profile_enable(0)
+    names = [px.poetx_profile_get(i)[0] for i in range(px.poetx_profile_count())]
+    assert "grad_gh" in names and "grad_g" not in names and "grad_h" not in names, names
