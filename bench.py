@@ -289,7 +289,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="llama8b_mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
