@@ -43,7 +43,7 @@ template <int B>
 __global__ void __launch_bounds__(64 * ((B > 256 ? 256 : B) / 32), (B > 256 ? 2 : (B >= 256 ? 4 : 2)))
 k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t ld, const bf16_t* __restrict__ plane,
               const float* __restrict__ scale, int64_t T, int64_t dim, int tokens_per_wg, int wgs_per_block,
-              int npairs) {
+              int npairs, const int32_t* __restrict__ inv_src, int32_t* __restrict__ inv_dst, int inv_n) {
   constexpr int NH = B > 256 ? 2 : 1;  // workgroups sharing a block (column halves)
   constexpr int NW = B / NH / 32;      // waves, 32 output columns each
   constexpr int ROWB = B * 2;
@@ -54,6 +54,10 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   constexpr int SLAB = 32 * 33 * 4;  // per wave: 32 rows x 32 fp32 columns (+1 pad)
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + NW * SLAB];
 
+  // optional side job for the launch after this one: inv_dst[inv_src[i]] = i
+  // (the inverse of a permutation of [0, inv_n)), spread over every workgroup
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < inv_n; i += gridDim.x * blockDim.x)
+    inv_dst[min(max(inv_src[i], 0), inv_n - 1)] = i;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int blk, part, cofs = 0;  // cofs: first output column of this workgroup within the block
@@ -320,8 +324,9 @@ bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const 
 }
 
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
-                      int64_t T, int64_t dim, int b, hipStream_t s) {
-  if (T <= 0) return true;
+                      int64_t T, int64_t dim, int b, hipStream_t s, const int32_t* inv_src, int32_t* inv_dst,
+                      int64_t inv_n) {
+  if (T <= 0) return inv_n <= 0;  // (no launch to carry the inverse)
   if (b != 64 && b != 128 && b != 256 && b != 512) return false;
   const int nblk = static_cast<int>((dim + b - 1) / b);
   const int nh = b == 512 ? 2 : 1;  // workgroups per block and token run
@@ -341,20 +346,20 @@ bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint1
   switch (b) {
     case 64:
       hipLaunchKernelGGL(k_block_apply<64>, dim3(static_cast<unsigned>(npairs)), dim3(128), 0, s, in, out, ld, plane,
-                         scale, T, dim, itpw, iwpb, inp);
+                         scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
       break;
     case 128:
       hipLaunchKernelGGL(k_block_apply<128>, dim3(static_cast<unsigned>(npairs)), dim3(256), 0, s, in, out, ld, plane,
-                         scale, T, dim, itpw, iwpb, inp);
+                         scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
       break;
     case 256:
       hipLaunchKernelGGL(k_block_apply<256>, dim3(static_cast<unsigned>(npairs)), dim3(512), 0, s, in, out, ld, plane,
-                         scale, T, dim, itpw, iwpb, inp);
+                         scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
       break;
     default:
       // both halves of every pair, in runs of 16 workgroups (8 pairs each)
       hipLaunchKernelGGL(k_block_apply<512>, dim3(static_cast<unsigned>((npairs + 7) / 8 * 16)), dim3(512), 0, s, in,
-                         out, ld, plane, scale, T, dim, itpw, iwpb, inp);
+                         out, ld, plane, scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
       break;
   }
   return true;

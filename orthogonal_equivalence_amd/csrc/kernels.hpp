@@ -101,10 +101,13 @@ void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16
 // rows: out[t][j*b + c] = (in[t][j*b + c] + sum_k in[t][j*b + k] *
 // plane[j][c][k]) * scale[j*b + c] (scale optional), for the ceil(dim/b)
 // blocks of a row of width dim (row stride ld). plane holds b x b bfloat16
-// blocks, zero outside a short last block. Returns false unless b is 64,
-// 128, 256 or 512.
+// blocks, zero outside a short last block. The same launch optionally writes
+// the inverse of a permutation for the launch after it: inv_dst[inv_src[i]]
+// = i for i < inv_n (inv_n = 0: none). Returns false unless b is 64, 128,
+// 256 or 512, or when an inverse is asked for and T = 0 (no launch).
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
-                      int64_t T, int64_t dim, int b, hipStream_t stream);
+                      int64_t T, int64_t dim, int b, hipStream_t stream, const int32_t* inv_src = nullptr,
+                      int32_t* inv_dst = nullptr, int64_t inv_n = 0);
 
 // Batched b x b block products with fused epilogue (block_prod.hip), for
 // bfloat16 blocks with b a multiple of 128 (up to 1024). Per block z:

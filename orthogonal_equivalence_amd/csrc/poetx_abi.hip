@@ -450,11 +450,18 @@ const void* plane(const poetx_layer* L, const void* g, const Side& s, int p) {
 
 // out[:, blocks] = in + in (G - I)^{T or not} for every diagonal block
 // (plane 1 gives in G, plane 0 gives in G^T), optional per-column scale.
+// inv_src, inv_dst, inv_n (optional): also inv_dst = the inverse of the
+// permutation inv_src of [0, inv_n), for a later launch (in the same launch
+// where the apply kernel runs, else in a launch of its own).
 bool block_apply(const poetx_layer* L, const Side& s, int64_t T, const void* in, void* out, const void* gbuf,
-                 int p, const float* colscale, hipStream_t st) {
-  if (is_bf16(L) && (s.b == 64 || s.b == 128 || s.b == 256 || s.b == 512))
+                 int p, const float* colscale, hipStream_t st, const int32_t* inv_src = nullptr,
+                 int32_t* inv_dst = nullptr, int64_t inv_n = 0) {
+  if (is_bf16(L) && (s.b == 64 || s.b == 128 || s.b == 256 || s.b == 512) && T > 0)
     return block_apply_bf16(static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), s.dim,
-                            static_cast<const uint16_t*>(plane(L, gbuf, s, p)), colscale, T, s.dim, s.b, st);
+                            static_cast<const uint16_t*>(plane(L, gbuf, s, p)), colscale, T, s.dim, s.b, st, inv_src,
+                            inv_dst, inv_n);
+  if (inv_n > 0) inverse_perm(inv_src, inv_dst, inv_n, st);
+  if (T <= 0) return true;
   GemmDesc d;
   d.A = in;
   d.lda = s.dim;
@@ -741,11 +748,11 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   if (!z) return ok;
   {
     ProfScope p("apply_p_fwd", stream);
-    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream);
+    // the same launch inverts perm_p for the scatter
+    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream, perm_p, w.inv_p, L->n);
   }
   {
     ProfScope p("scatter_z", stream);
-    inverse_perm(perm_p, w.inv_p, L->n, stream);
     ok = ok && gather_cols(w.buf, L->n, nullptr, z, L->n, nullptr, w.inv_p, L->n, T, es, stream);
   }
   return ok;
@@ -809,7 +816,8 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   // R side: dX1 = dX2 G^T, dG = sum_t X1^T dX2, dX = dX1 Psi
   {
     ProfScope p("apply_r_bwd", stream);
-    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream);
+    // the same launch inverts perm_r for the scatter of dx
+    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream, perm_r, w.inv_r, L->m);
   }
   const Split spR = token_split(L, R, T);
   if (!merged) {
@@ -818,7 +826,6 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   }
   {
     ProfScope p("scatter_dx", stream);
-    inverse_perm(perm_r, w.inv_r, L->m, stream);
     ok = ok && gather_cols(dX1, L->m, nullptr, dx, L->m, nullptr, w.inv_r, L->m, T, es, stream);
   }
   if (merged) {
