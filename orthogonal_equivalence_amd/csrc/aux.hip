@@ -126,8 +126,11 @@ __global__ void __launch_bounds__(kThreads, 2)
 k_gather_rows_pipe(const T* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ rmap_in,
                    T* __restrict__ out, int64_t ld_out, const int32_t* __restrict__ rmap_out,
                    const int32_t* __restrict__ cidx, int ncols, int64_t nrows,
-                   const int32_t* __restrict__ rmap_pre, const int32_t* __restrict__ cidx_pre, int nbuf) {
+                   const int32_t* __restrict__ rmap_pre, const int32_t* __restrict__ cidx_pre, int nbuf,
+                   const SideJob job) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  // the side job's stores go out before every load the waits below count
+  run_side_job(job);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row_bytes = ncols * static_cast<int>(sizeof(T));
@@ -253,18 +256,7 @@ __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __rest
   POETX_GRID_STRIDE(i, n) inv[clamp_index(perm[i], n)] = static_cast<int32_t>(i);
 }
 
-// Inverses of two permutations, and (optionally, in the same launch) two
-// float arrays set to zero.
-__global__ void k_inverse_perm2(const int32_t* __restrict__ perm0, int32_t* __restrict__ inv0, int64_t n0,
-                                const int32_t* __restrict__ perm1, int32_t* __restrict__ inv1, int64_t n1,
-                                float* __restrict__ z0, int64_t nz0, float* __restrict__ z1, int64_t nz1) {
-  POETX_GRID_STRIDE(i, n0 + n1 + nz0 + nz1) {
-    if (i < n0) inv0[clamp_index(perm0[i], n0)] = static_cast<int32_t>(i);
-    else if (i < n0 + n1) inv1[clamp_index(perm1[i - n0], n1)] = static_cast<int32_t>(i - n0);
-    else if (i < n0 + n1 + nz0) z0[i - n0 - n1] = 0.f;
-    else z1[i - n0 - n1 - nz0] = 0.f;
-  }
-}
+__global__ void __launch_bounds__(kThreads) k_side_job(const SideJob job) { run_side_job(job); }
 
 __global__ void k_compose_perm(const int32_t* __restrict__ inv0, const int32_t* __restrict__ next0,
                                int32_t* __restrict__ out0, int64_t n0, const int32_t* __restrict__ inv1,
@@ -842,7 +834,8 @@ void pipe_shape(int64_t ncols, int* per_cu, int* nbuf) {
 template <typename T>
 void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* out, int64_t ld_out,
                    const int32_t* rmap_out, const int32_t* cidx, int64_t ncols, int64_t nrows, hipStream_t s,
-                   const int32_t* rmap_pre = nullptr, const int32_t* cidx_pre = nullptr) {
+                   const int32_t* rmap_pre = nullptr, const int32_t* cidx_pre = nullptr,
+                   const SideJob& job = SideJob()) {
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
   if (pipe_applies<T>(ncols)) {
     int per_cu = 1, nbuf = 2;
@@ -850,8 +843,11 @@ void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* 
     const unsigned nwg = static_cast<unsigned>(std::min<int64_t>(nrows, 256 * per_cu));
     hipLaunchKernelGGL(k_gather_rows_pipe<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(nbuf * row_bytes), s,
                        static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
-                       static_cast<int>(ncols), nrows, rmap_pre, cidx_pre, nbuf);
-  } else if (row_bytes <= kRowLdsMax) {
+                       static_cast<int>(ncols), nrows, rmap_pre, cidx_pre, nbuf, job);
+    return;
+  }
+  if (!job.empty()) side_job(job, s);
+  if (row_bytes <= kRowLdsMax) {
     int rows = static_cast<int>(kRowLdsBudget / row_bytes);
     rows = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
     const int chunk = (row_bytes % 16 == 0) ? 16 : 8;
@@ -886,29 +882,29 @@ void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_inverse_perm, dim3(grid1(n)), dim3(kThreads), 0, s, perm, inv, n);
 }
 
-void inverse_perm2(const int32_t* perm0, int32_t* inv0, int64_t n0, const int32_t* perm1, int32_t* inv1, int64_t n1,
-                   hipStream_t s, float* z0, int64_t nz0, float* z1, int64_t nz1) {
-  const int64_t total = n0 + n1 + nz0 + nz1;
-  if (total > 0)
-    hipLaunchKernelGGL(k_inverse_perm2, dim3(grid1(total)), dim3(kThreads), 0, s, perm0, inv0, n0, perm1, inv1, n1,
-                       z0, nz0, z1, nz1);
+void side_job(const SideJob& job, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(job.n0) + job.n1 + job.nz0 + job.nz1;
+  if (total > 0) hipLaunchKernelGGL(k_side_job, dim3(grid1(total)), dim3(kThreads), 0, s, job);
 }
 
 bool reframe_rows_cols(const void* in, const int32_t* inv_r, const int32_t* next_r, void* out,
                        const int32_t* inv_c, const int32_t* next_c, int32_t* rmap, int32_t* cmap, int64_t ncols,
-                       int64_t nrows, int esize, hipStream_t s) {
-  if (nrows <= 0 || ncols <= 0) return true;
-  if (ncols % 8 != 0) return false;
+                       int64_t nrows, int esize, hipStream_t s, const SideJob& job) {
+  if (ncols % 8 != 0 || (esize != 1 && esize != 2 && esize != 4)) return false;
+  if (nrows <= 0 || ncols <= 0) {
+    side_job(job, s);
+    return true;
+  }
   const bool pipe = esize == 2 ? pipe_applies<uint16_t>(ncols)
                                : (esize == 4 ? pipe_applies<uint32_t>(ncols) : pipe_applies<uint8_t>(ncols));
   if (pipe) {
     switch (esize) {
-      case 1: launch_gather<uint8_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c); return true;
-      case 2: launch_gather<uint16_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c); return true;
-      case 4: launch_gather<uint32_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c); return true;
-      default: return false;
+      case 1: launch_gather<uint8_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c, job); return true;
+      case 2: launch_gather<uint16_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c, job); return true;
+      default: launch_gather<uint32_t>(in, ncols, inv_r, out, ncols, nullptr, inv_c, ncols, nrows, s, next_r, next_c, job); return true;
     }
   }
+  side_job(job, s);
   compose_perm(inv_r, next_r, rmap, nrows, inv_c, next_c, cmap, ncols, s);
   return gather_cols(in, ncols, rmap, out, ncols, nullptr, cmap, ncols, nrows, esize, s);
 }

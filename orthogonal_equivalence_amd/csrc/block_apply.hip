@@ -43,7 +43,7 @@ template <int B>
 __global__ void __launch_bounds__(64 * ((B > 256 ? 256 : B) / 32), (B > 256 ? 2 : (B >= 256 ? 4 : 2)))
 k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t ld, const bf16_t* __restrict__ plane,
               const float* __restrict__ scale, int64_t T, int64_t dim, int tokens_per_wg, int wgs_per_block,
-              int npairs, const int32_t* __restrict__ inv_src, int32_t* __restrict__ inv_dst, int inv_n) {
+              int npairs, const SideJob job) {
   constexpr int NH = B > 256 ? 2 : 1;  // workgroups sharing a block (column halves)
   constexpr int NW = B / NH / 32;      // waves, 32 output columns each
   constexpr int ROWB = B * 2;
@@ -54,10 +54,7 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   constexpr int SLAB = 32 * 33 * 4;  // per wave: 32 rows x 32 fp32 columns (+1 pad)
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + NW * SLAB];
 
-  // optional side job for the launch after this one: inv_dst[inv_src[i]] = i
-  // (the inverse of a permutation of [0, inv_n)), spread over every workgroup
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < inv_n; i += gridDim.x * blockDim.x)
-    inv_dst[min(max(inv_src[i], 0), inv_n - 1)] = i;
+  run_side_job(job);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int blk, part, cofs = 0;  // cofs: first output column of this workgroup within the block
@@ -177,10 +174,12 @@ __device__ __forceinline__ int left_slot(int r, int c) { return c ^ (((r >> 1) &
 
 __global__ void __launch_bounds__(512, 4)
 k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t ld,
-                   const bf16_t* __restrict__ plane, int64_t rows, int64_t ncols, int cols_per_wg, int wgs_per_block) {
+                   const bf16_t* __restrict__ plane, int64_t rows, int64_t ncols, int cols_per_wg, int wgs_per_block,
+                   const SideJob job) {
   constexpr int B = 256, TC = 64, ROWB = TC * 2, STAGE = B * ROWB, KS = B / 16;
   constexpr int SLAB = 16 * 32;  // floats per wave
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 8 * SLAB * 4];
+  run_side_job(job);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   // the workgroups of one block run on one XCD (one L2 holds its plane)
@@ -307,8 +306,8 @@ k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int6
 }  // namespace
 
 bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, int64_t rows,
-                           int64_t ncols, int b, hipStream_t s) {
-  if (rows <= 0 || ncols <= 0) return true;
+                           int64_t ncols, int b, hipStream_t s, const SideJob& job) {
+  if (rows <= 0 || ncols <= 0) return job.empty();  // (no launch to carry the side job)
   if (b != 256 || ncols % 8 != 0 || ncols < 8) return false;
   const int nblk = static_cast<int>((rows + b - 1) / b);
   // two 512-thread workgroups per CU (LDS) -> 512 resident
@@ -319,14 +318,13 @@ bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const 
   hipLaunchKernelGGL(k_block_apply_left, dim3(static_cast<unsigned>(nblk * wpb)), dim3(512), 0, s,
                      reinterpret_cast<const bf16_t*>(in), reinterpret_cast<bf16_t*>(out), ld,
                      reinterpret_cast<const bf16_t*>(plane), rows, ncols, static_cast<int>(cpw),
-                     static_cast<int>(wpb));
+                     static_cast<int>(wpb), job);
   return true;
 }
 
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
-                      int64_t T, int64_t dim, int b, hipStream_t s, const int32_t* inv_src, int32_t* inv_dst,
-                      int64_t inv_n) {
-  if (T <= 0) return inv_n <= 0;  // (no launch to carry the inverse)
+                      int64_t T, int64_t dim, int b, hipStream_t s, const SideJob& job) {
+  if (T <= 0) return job.empty();  // (no launch to carry the side job)
   if (b != 64 && b != 128 && b != 256 && b != 512) return false;
   const int nblk = static_cast<int>((dim + b - 1) / b);
   const int nh = b == 512 ? 2 : 1;  // workgroups per block and token run
@@ -346,20 +344,20 @@ bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint1
   switch (b) {
     case 64:
       hipLaunchKernelGGL(k_block_apply<64>, dim3(static_cast<unsigned>(npairs)), dim3(128), 0, s, in, out, ld, plane,
-                         scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
+                         scale, T, dim, itpw, iwpb, inp, job);
       break;
     case 128:
       hipLaunchKernelGGL(k_block_apply<128>, dim3(static_cast<unsigned>(npairs)), dim3(256), 0, s, in, out, ld, plane,
-                         scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
+                         scale, T, dim, itpw, iwpb, inp, job);
       break;
     case 256:
       hipLaunchKernelGGL(k_block_apply<256>, dim3(static_cast<unsigned>(npairs)), dim3(512), 0, s, in, out, ld, plane,
-                         scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
+                         scale, T, dim, itpw, iwpb, inp, job);
       break;
     default:
       // both halves of every pair, in runs of 16 workgroups (8 pairs each)
       hipLaunchKernelGGL(k_block_apply<512>, dim3(static_cast<unsigned>((npairs + 7) / 8 * 16)), dim3(512), 0, s, in,
-                         out, ld, plane, scale, T, dim, itpw, iwpb, inp, inv_src, inv_dst, static_cast<int>(inv_n));
+                         out, ld, plane, scale, T, dim, itpw, iwpb, inp, job);
       break;
   }
   return true;

@@ -12,7 +12,8 @@
 // The Cayley-Neumann build (zhichai.net digest of arXiv:2603.05500, section
 // "3. Cayley-Neumann 参数化优化") is two such products, Q^2 = -Q Q^T with
 // S = 2Q + Q^2 in the epilogue, then G - I = 2Q + 2Q^2 + S Q^2 written as both
-// planes of the block buffer; the adjoint is three (see poetx_abi.hip).
+// planes of the block buffer; the adjoint is three (see poetx_abi.hip), the
+// last of which writes the packed gradient straight from its epilogue.
 //
 // gfx950 design: 128 x 128 output tile per workgroup (the tiles of one block
 // on one XCD), 4 waves of 64 x 64
@@ -83,6 +84,13 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
   const int64_t zout = static_cast<int64_t>(hi ? z - d.z_split : z) * d.b * d.b;
   void* const out1 = hi ? d.out1_hi : d.out1;
   void* const out1t = hi ? d.out1t_hi : d.out1t;
+  // packed strict upper triangle: nothing to do below the diagonal
+  float* const pk = hi ? d.pk_hi : d.pk;
+  if ((d.pk || d.pk_hi) && (pk == nullptr || i0 > n0)) return;
+  const int zl = hi ? z - d.z_split : z;
+  const int pk_r = static_cast<int>(min(static_cast<int64_t>(d.b), (hi ? d.pk_dim_hi : d.pk_dim) -
+                                                                       static_cast<int64_t>(zl) * d.b));
+  const int64_t pk_off = static_cast<int64_t>(zl) * d.b * (d.b - 1) / 2;
   const int ksteps = d.b / BK;
   const int nk = ksteps * (d.A2 ? 2 : 1);
 
@@ -184,6 +192,13 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v1[e] = alpha * a[e] + d.beta * ef[e] + d.gamma * eh[e];
       if (out1) store8(out1, zout + roff, d.out1_f32, v1);
+      if (pk && gi < pk_r) {
+        // row gi's run of the packed triangle: columns gi + 1 .. pk_r - 1
+        const int64_t rbase = pk_off + static_cast<int64_t>(gi) * pk_r - static_cast<int64_t>(gi) * (gi + 1) / 2 - gi - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gn + e > gi && gn + e < pk_r) pk[rbase + gn + e] = v1[e];
+      }
       if (d.out2) {
         float v2[8];
 #pragma unroll

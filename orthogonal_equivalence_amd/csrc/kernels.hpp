@@ -7,6 +7,48 @@
 
 namespace poetx {
 
+// Small independent work a launch can carry for the launches after it,
+// spread over all its threads: dst0 / dst1 = the inverses of the
+// permutations src0 / src1 of [0, n0) / [0, n1) (dst[src[i]] = i, entries
+// clamped to the range), and z0[0, nz0), z1[0, nz1) set to zero. Counts of 0
+// leave a part out.
+struct SideJob {
+  const int32_t* src0 = nullptr;
+  int32_t* dst0 = nullptr;
+  int n0 = 0;
+  const int32_t* src1 = nullptr;
+  int32_t* dst1 = nullptr;
+  int n1 = 0;
+  float* z0 = nullptr;
+  int64_t nz0 = 0;
+  float* z1 = nullptr;
+  int64_t nz1 = 0;
+  bool empty() const { return n0 <= 0 && n1 <= 0 && nz0 <= 0 && nz1 <= 0; }
+};
+
+// The side job's share of the calling thread (grid-stride over the launch).
+__device__ __forceinline__ void run_side_job(const SideJob& j) {
+  const int64_t total = static_cast<int64_t>(j.n0) + j.n1 + j.nz0 + j.nz1;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    if (i < j.n0) {
+      const int32_t v = j.src0[i];
+      j.dst0[v < 0 ? 0 : (v >= j.n0 ? j.n0 - 1 : v)] = static_cast<int32_t>(i);
+    } else if (i < j.n0 + j.n1) {
+      const int32_t k = static_cast<int32_t>(i - j.n0);
+      const int32_t v = j.src1[k];
+      j.dst1[v < 0 ? 0 : (v >= j.n1 ? j.n1 - 1 : v)] = k;
+    } else if (i < j.n0 + j.n1 + j.nz0) {
+      j.z0[i - j.n0 - j.n1] = 0.f;
+    } else {
+      j.z1[i - j.n0 - j.n1 - j.nz0] = 0.f;
+    }
+  }
+}
+
+// The side job in a launch of its own (for paths whose kernels do not carry it).
+void side_job(const SideJob& job, hipStream_t stream);
+
 // out[ro][i] = in[ri][cidx[i]] for i < ncols, rows r < nrows, with
 // ri = rmap_in ? rmap_in[r] : r and ro = rmap_out ? rmap_out[r] : r.
 // esize = element bytes (1, 2 or 4); ncols % 8 == 0. Indices are clamped to
@@ -23,21 +65,17 @@ void inverse_perm(const int32_t* perm, int32_t* inv, int64_t n, hipStream_t stre
 void compose_perm(const int32_t* inv0, const int32_t* next0, int32_t* out0, int64_t n0, const int32_t* inv1,
                   const int32_t* next1, int32_t* out1, int64_t n1, hipStream_t stream);
 
-// inverse_perm for two permutations in one launch, which also sets the
-// float arrays z0 [nz0] and z1 [nz1] to zero (none by default).
-void inverse_perm2(const int32_t* perm0, int32_t* inv0, int64_t n0, const int32_t* perm1, int32_t* inv1, int64_t n1,
-                   hipStream_t stream, float* z0 = nullptr, int64_t nz0 = 0, float* z1 = nullptr, int64_t nz1 = 0);
-
 // out[r][c] = in[inv_r[next_r[r]]][inv_c[next_c[c]]] for a row-major
 // nrows x ncols matrix (ncols % 8 == 0, element bytes esize): a matrix whose
 // rows and columns are in the frame of one pair of permutations, rewritten in
 // the frame of another (inv_*: inverses of the old permutations, next_*: the
 // new ones). The composition happens inside the gather where rows fit its
 // LDS pipeline; otherwise rmap / cmap (nrows / ncols int32 of scratch)
-// receive the composed maps first.
+// receive the composed maps first. job runs in the gather's launch, or in a
+// launch of its own before it; nothing runs when false is returned.
 bool reframe_rows_cols(const void* in, const int32_t* inv_r, const int32_t* next_r, void* out,
                        const int32_t* inv_c, const int32_t* next_c, int32_t* rmap, int32_t* cmap, int64_t ncols,
-                       int64_t nrows, int esize, hipStream_t stream);
+                       int64_t nrows, int esize, hipStream_t stream, const SideJob& job = SideJob());
 
 // out[i] = in[idx[i]] (float), idx clamped to [0, n).
 void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipStream_t stream);
@@ -101,13 +139,11 @@ void cnp_h1(const float* Uk, const float* P1, int b, int nblk, float* Hf, uint16
 // rows: out[t][j*b + c] = (in[t][j*b + c] + sum_k in[t][j*b + k] *
 // plane[j][c][k]) * scale[j*b + c] (scale optional), for the ceil(dim/b)
 // blocks of a row of width dim (row stride ld). plane holds b x b bfloat16
-// blocks, zero outside a short last block. The same launch optionally writes
-// the inverse of a permutation for the launch after it: inv_dst[inv_src[i]]
-// = i for i < inv_n (inv_n = 0: none). Returns false unless b is 64, 128,
-// 256 or 512, or when an inverse is asked for and T = 0 (no launch).
+// blocks, zero outside a short last block. The same launch also does job.
+// Returns false unless b is 64, 128, 256 or 512, or when job is not empty
+// and T = 0 (no launch).
 bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, const float* scale,
-                      int64_t T, int64_t dim, int b, hipStream_t stream, const int32_t* inv_src = nullptr,
-                      int32_t* inv_dst = nullptr, int64_t inv_n = 0);
+                      int64_t T, int64_t dim, int b, hipStream_t stream, const SideJob& job = SideJob());
 
 // Batched b x b block products with fused epilogue (block_prod.hip), for
 // bfloat16 blocks with b a multiple of 128 (up to 1024). Per block z:
@@ -118,7 +154,12 @@ bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint1
 // bfloat16, either addend optional). v1 goes to out1 (row-major) and/or
 // out1t (transposed), as float if out1_f32 else bfloat16; v2 to out2
 // (bfloat16, row-major). Outputs of blocks z >= z_split go to out1_hi /
-// out1t_hi at block z - z_split (two sides batched in one launch).
+// out1t_hi at block z - z_split (two sides batched in one launch). pk
+// (optional, float) receives the strict upper triangle of v1 packed row by
+// row: for block zl of its side (zl = z, or z - z_split into pk_hi), of size
+// r = min(b, dim - zl b) with dim = pk_dim (pk_dim_hi), entry (i, l), i < l
+// < r, goes to pk[zl b (b-1)/2 + i r - i (i+1)/2 + l - i - 1]; tiles wholly
+// below the diagonal are then skipped.
 struct BlockProdDesc {
   const uint16_t* A1 = nullptr;
   const uint16_t* B1 = nullptr;
@@ -137,6 +178,9 @@ struct BlockProdDesc {
   int z_split = 1 << 30;
   void* out1_hi = nullptr;
   void* out1t_hi = nullptr;
+  float* pk = nullptr;
+  float* pk_hi = nullptr;
+  int64_t pk_dim = 0, pk_dim_hi = 0;
 };
 bool block_prod_bf16(const BlockProdDesc& d, hipStream_t stream);
 
@@ -150,10 +194,11 @@ bool cnp_build_fused(const uint16_t* Qh, int n0, int n1, int b, void* g0, void* 
 // Left block product (block_apply.hip) on a row-major rows x ncols bfloat16
 // matrix (row stride ld): out[j*256 + i][c] = in[j*256 + i][c] + sum_k
 // plane[j][i][k] in[j*256 + k][c] for the ceil(rows/256) row blocks; plane
-// holds 256 x 256 bfloat16 blocks, zero outside a short last block. b = 256
-// and ncols a multiple of 8 only (returns false otherwise).
+// holds 256 x 256 bfloat16 blocks, zero outside a short last block. The same
+// launch also does job. b = 256 and ncols a multiple of 8 only (returns false
+// otherwise, and when job is not empty and there is nothing to launch).
 bool block_apply_left_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint16_t* plane, int64_t rows,
-                           int64_t ncols, int b, hipStream_t stream);
+                           int64_t ncols, int b, hipStream_t stream, const SideJob& job = SideJob());
 
 // Token sums of the block gradients (block_grad.hip) for bfloat16 blocks of
 // 256 or 512: part[s][j][i][c] = sum over the tokens of split s of

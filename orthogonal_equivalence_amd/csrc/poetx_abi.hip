@@ -448,19 +448,25 @@ const void* plane(const poetx_layer* L, const void* g, const Side& s, int p) {
   return static_cast<const char*>(g) + static_cast<int64_t>(p) * block_elems(s) * act_size(L);
 }
 
+// The side job that writes inv = the inverse of the permutation perm of [0, n).
+SideJob inverse_job(const int32_t* perm, int32_t* inv, int64_t n) {
+  SideJob j;
+  j.src0 = perm;
+  j.dst0 = inv;
+  j.n0 = static_cast<int>(n);
+  return j;
+}
+
 // out[:, blocks] = in + in (G - I)^{T or not} for every diagonal block
 // (plane 1 gives in G, plane 0 gives in G^T), optional per-column scale.
-// inv_src, inv_dst, inv_n (optional): also inv_dst = the inverse of the
-// permutation inv_src of [0, inv_n), for a later launch (in the same launch
-// where the apply kernel runs, else in a launch of its own).
+// job (optional): work for later launches, done in the same launch where the
+// apply kernel runs, else in a launch of its own.
 bool block_apply(const poetx_layer* L, const Side& s, int64_t T, const void* in, void* out, const void* gbuf,
-                 int p, const float* colscale, hipStream_t st, const int32_t* inv_src = nullptr,
-                 int32_t* inv_dst = nullptr, int64_t inv_n = 0) {
+                 int p, const float* colscale, hipStream_t st, const SideJob& job = SideJob()) {
   if (is_bf16(L) && (s.b == 64 || s.b == 128 || s.b == 256 || s.b == 512) && T > 0)
     return block_apply_bf16(static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), s.dim,
-                            static_cast<const uint16_t*>(plane(L, gbuf, s, p)), colscale, T, s.dim, s.b, st, inv_src,
-                            inv_dst, inv_n);
-  if (inv_n > 0) inverse_perm(inv_src, inv_dst, inv_n, st);
+                            static_cast<const uint16_t*>(plane(L, gbuf, s, p)), colscale, T, s.dim, s.b, st, job);
+  side_job(job, st);
   if (T <= 0) return true;
   GemmDesc d;
   d.A = in;
@@ -622,7 +628,9 @@ bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const 
     // symmetric, Uk skew, so every right factor is read by rows):
     //   H1/2 = 2 Uk - (Q Us + Us Q),          Q Us = NT(Q, Us), Us Q = -NT(Us, Q)
     //   F    = -4 Us - 2 (NT(Uk, Q) + NT(Q, H1/2)),   written transposed
-    //   E    = 2 Uk + NT(Q, F^T)
+    //   E    = 2 Uk + NT(Q, F^T), of which only E - E^T is needed:
+    //   E - E^T = 4 Uk + NT(Q, F^T) - NT(F^T, Q)  (Uk skew; (Q F)^T = F^T Q^T),
+    //   one product whose epilogue writes dq packed
     unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, nullptr, w.Qh, st);
     BlockProdDesc h;
     h.A1 = w.Qh;
@@ -652,16 +660,20 @@ bool cnp_bwd_group(const poetx_layer* L, const Group& g, const float* q0, const 
     BlockProdDesc e;
     e.A1 = w.Qh;
     e.B1 = w.Fh;
+    e.A2 = w.Fh;
+    e.B2 = w.Qh;
+    e.neg2 = 1;
     e.b = g.b;
     e.nblk = nb;
     e.alpha = 1.f;
-    e.beta = 2.f;
+    e.beta = 4.f;
     e.Ef = Uk;
-    e.out1 = w.E;
-    e.out1_f32 = 1;
-    if (!block_prod_bf16(e, st)) return false;
-    pack_asym2(w.E, g.b, g.dim0, g.n0, dq0, g.dim1, g.n1, dq1, st);
-    return true;
+    e.z_split = g.n0;
+    e.pk = dq0;
+    e.pk_dim = g.dim0;
+    e.pk_hi = dq1;
+    e.pk_dim_hi = g.dim1;
+    return block_prod_bf16(e, st);
   }
   unpack_skew2(q0, g.dim0, g.n0, q1, g.dim1, g.n1, g.b, w.Qf, bf ? w.Qh : nullptr, st);
   const void* Q = bf ? static_cast<const void*>(w.Qh) : w.Qf;
@@ -749,7 +761,7 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   {
     ProfScope p("apply_p_fwd", stream);
     // the same launch inverts perm_p for the scatter
-    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream, perm_p, w.inv_p, L->n);
+    ok = ok && block_apply(L, P, T, Y1, w.buf, g_p, 1, nullptr, stream, inverse_job(perm_p, w.inv_p, L->n));
   }
   {
     ProfScope p("scatter_z", stream);
@@ -817,7 +829,7 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   {
     ProfScope p("apply_r_bwd", stream);
     // the same launch inverts perm_r for the scatter of dx
-    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream, perm_r, w.inv_r, L->m);
+    ok = ok && block_apply(L, R, T, dX2, dX1, g_r, 0, nullptr, stream, inverse_job(perm_r, w.inv_r, L->m));
   }
   const Split spR = token_split(L, R, T);
   if (!merged) {
@@ -1131,7 +1143,7 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
   // M = Diag(G) Wp Diag(H): row i of it is row inv_r[perm_r_next[i]] of M,
   // column c is column inv_p[perm_p_next[c]].
   int wait_status = POETX_OK;
-  auto reframe_maps = [&]() -> bool {
+  auto wait_next = [&]() -> bool {
     if (next_ready) {
       const hipError_t e = hipStreamWaitEvent(stream, next_ready, 0);
       if (e != hipSuccess) {
@@ -1140,10 +1152,20 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
         return false;
       }
     }
-    // q <- 0 in the same launch: the merge reads only the CNP planes
-    inverse_perm2(perm_r, w.inv_r, L->m, perm_p, w.inv_p, L->n, stream, q_r, packed_len(R), q_p, packed_len(P));
     return true;
   };
+  // inv_r, inv_p: written by the right block product's launch (workspace
+  // only, so a failed wait leaves wp and q as they were)
+  SideJob inv_job = inverse_job(perm_r, w.inv_r, L->m);
+  inv_job.src1 = perm_p;
+  inv_job.dst1 = w.inv_p;
+  inv_job.n1 = static_cast<int>(L->n);
+  // q <- 0 in the reframe's launch (the merge reads only the CNP planes)
+  SideJob zero_q;
+  zero_q.z0 = q_r;
+  zero_q.nz0 = packed_len(R);
+  zero_q.z1 = q_p;
+  zero_q.nz1 = packed_len(P);
   bool ok;
   if (i8) {
     // Dequantize Wp with its column scales, merge in float with float copies
@@ -1170,13 +1192,13 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     }
     {
       ProfScope p("merge_right", stream);
-      ok = ok && block_apply(&Lf, P, L->m, w.C2, w.C1, w.gp32, 1, nullptr, stream);
+      ok = ok && block_apply(&Lf, P, L->m, w.C2, w.C1, w.gp32, 1, nullptr, stream, inv_job);
     }
     {
       ProfScope p("merge_reframe", stream);
-      ok = ok && reframe_maps();
+      ok = ok && wait_next();
       ok = ok && reframe_rows_cols(w.C1, w.inv_r, perm_r_next, w.C2, w.inv_p, perm_p_next, w.rmap, w.cmap, L->n,
-                                   L->m, 4, stream);
+                                   L->m, 4, stream, zero_q);
     }
     {
       ProfScope p("merge_requant", stream);
@@ -1197,7 +1219,7 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     }
     {
       ProfScope p("merge_right", stream);
-      ok = ok && block_apply(L, P, L->m, w.C2, w.C1, g_p, 1, nullptr, stream);
+      ok = ok && block_apply(L, P, L->m, w.C2, w.C1, g_p, 1, nullptr, stream, inv_job);
     }
     M = w.C1;
   } else {
@@ -1214,15 +1236,15 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     }
     {
       ProfScope p("merge_right", stream);
-      ok = ok && block_apply(L, P, L->m, w.C1, w.C2, g_p, 1, nullptr, stream);
+      ok = ok && block_apply(L, P, L->m, w.C1, w.C2, g_p, 1, nullptr, stream, inv_job);
     }
     M = w.C2;
   }
   {
     ProfScope p("merge_reframe", stream);
-    ok = ok && reframe_maps();
+    ok = ok && wait_next();
     ok = ok && reframe_rows_cols(M, w.inv_r, perm_r_next, wp, w.inv_p, perm_p_next, w.rmap, w.cmap, L->n, L->m,
-                                 w_size(L), stream);
+                                 w_size(L), stream, zero_q);
   }
   if (wait_status) return wait_status;
   if (!ok) return POETX_EUNSUPPORTED;
