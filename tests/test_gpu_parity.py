@@ -150,6 +150,13 @@ SMALL = [
     # engine, the backward reads the codes in the general engine; short last
     # blocks of 16 on both sides (528 = 4*128 + 16, 1040 = 8*128 + 16)
     _cfg("xq_widths_not_64", 200, 528, 1040, 128, 128, "bf16", "i8", 57),
+    # weight rows wider than the LDS-staged gathers take (float32 65 568 bytes,
+    # bfloat16 past 16384 columns): the z scatter, the dx scatter and the
+    # merge's reframe gather from global memory, and the work the apply and
+    # gather launches otherwise carry (inverse permutations, q <- 0) runs in
+    # launches of its own; last P blocks of 8 and 16
+    _cfg("f32_wide_rows", 8, 64, 16392, 64, 512, "f32", "f32", 60),
+    _cfg("bf16_wide_rows", 8, 64, 16400, 64, 256, "bf16", "bf16", 61),
 ]
 
 
