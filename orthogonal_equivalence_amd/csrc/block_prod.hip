@@ -162,6 +162,25 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kSlab + j * 32 + lrow] = acc[i][j][r];
+    if (pk) {
+      // packed upper triangle: lane -> column, one row per step, so that each
+      // store instruction covers a contiguous run of the row's packed entries
+      const int gn = n0 + wn * 64 + lane;
+      float ef[32];
+#pragma unroll
+      for (int row = 0; row < 32; ++row) {
+        const int gi = i0 + wm * 64 + i * 32 + row;
+        ef[row] = d.Ef ? d.Ef[zoff + static_cast<int64_t>(gi) * d.b + gn] : 0.f;
+      }
+#pragma unroll
+      for (int row = 0; row < 32; ++row) {
+        const int gi = i0 + wm * 64 + i * 32 + row;
+        const float v = alpha * slab[row * kSlab + lane] + d.beta * ef[row];
+        if (gi < gn && gn < pk_r)
+          pk[pk_off + static_cast<int64_t>(gi) * pk_r - static_cast<int64_t>(gi) * (gi + 1) / 2 + gn - gi - 1] = v;
+      }
+      continue;
+    }
     // row pass: lane -> (row, 8 columns); 32 rows x 8 chunks = 4 per lane
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -192,13 +211,6 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v1[e] = alpha * a[e] + d.beta * ef[e] + d.gamma * eh[e];
       if (out1) store8(out1, zout + roff, d.out1_f32, v1);
-      if (pk && gi < pk_r) {
-        // row gi's run of the packed triangle: columns gi + 1 .. pk_r - 1
-        const int64_t rbase = pk_off + static_cast<int64_t>(gi) * pk_r - static_cast<int64_t>(gi) * (gi + 1) / 2 - gi - 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gn + e > gi && gn + e < pk_r) pk[rbase + gn + e] = v1[e];
-      }
       if (d.out2) {
         float v2[8];
 #pragma unroll

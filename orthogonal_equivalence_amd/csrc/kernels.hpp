@@ -159,7 +159,8 @@ bool block_apply_bf16(const uint16_t* in, uint16_t* out, int64_t ld, const uint1
 // row: for block zl of its side (zl = z, or z - z_split into pk_hi), of size
 // r = min(b, dim - zl b) with dim = pk_dim (pk_dim_hi), entry (i, l), i < l
 // < r, goes to pk[zl b (b-1)/2 + i r - i (i+1)/2 + l - i - 1]; tiles wholly
-// below the diagonal are then skipped.
+// below the diagonal are then skipped. With pk the only output is the packed
+// one and v1 takes no Eh term (gamma is ignored).
 struct BlockProdDesc {
   const uint16_t* A1 = nullptr;
   const uint16_t* B1 = nullptr;
