@@ -468,15 +468,18 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * kSlabStride;
   constexpr int kChunksPerRow = WTN / 8;
   constexpr int kChunksPerLane = 32 * kChunksPerRow / 64;
+  // every wave is done with the stages before the slabs overwrite them; the
+  // slabs are per wave, so the passes need no further barrier (one wave's
+  // LDS accesses complete in order)
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kSlabStride + j * 32 + lrow] = acc[i][j][r];
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int c = 0; c < kChunksPerLane; ++c) {
       const int ch = lane + c * 64;
