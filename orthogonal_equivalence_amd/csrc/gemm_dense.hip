@@ -159,10 +159,13 @@ __device__ __forceinline__ void load_one_nc(const bf16_t* __restrict__ g_k0, int
 // last, so that every load has at least a group's MFMAs to land in; measured
 // against an even 2-2-2-2 spread at the 8B shapes: forward 0.820 -> 0.807 ms,
 // backward 0.751 -> 0.748 ms.
-// (Other stage shapes spread their loads evenly.)
+// Other stage shapes spread their loads evenly, and so does the int8
+// N-contiguous (forward) kernel, whose B comes as codes in two loads per wave
+// and step: there the even spread measured 0.87-0.90 ms against 0.94 ms.
+template <bool EVEN>
 __host__ __device__ constexpr int load_first(int kk) {
   constexpr int kGroups = BK / 16, kLoads = 2 * kInstPerTile;
-  if constexpr (kGroups == 4 && kLoads == 8) return kk <= 0 ? 0 : (kk == 1 ? 2 : (kk == 2 ? 5 : 8));
+  if constexpr (!EVEN && kGroups == 4 && kLoads == 8) return kk <= 0 ? 0 : (kk == 1 ? 2 : (kk == 2 ? 5 : 8));
   else return kk * kLoads / kGroups;
 }
 
@@ -410,7 +413,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
       // this K group's share of the next stage's loads (branch-free: the last
       // iteration re-loads the last K slice into the idle stage)
 #pragma unroll
-      for (int i = load_first(kk); i < load_first(kk + 1); ++i) {
+      for (int i = load_first<BI8 && BNC>(kk); i < load_first<BI8 && BNC>(kk + 1); ++i) {
         if constexpr (BI8) {
           if (i >= kInstPerTile) {
             // B comes through registers: once the A loads are out
