@@ -157,7 +157,11 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
     const char* A = smem + (s % NSTAGE) * STAGE;
     const char* B = A + TILE;
     const int valid = static_cast<int>(min(static_cast<int64_t>(TK), t_end - t_begin - static_cast<int64_t>(s) * TK));
-    // all fragments of the stage first, then the next loads, then the MFMAs.
+    // the loads three stages ahead first, into the buffer the step before
+    // read (every wave is past those reads at the barrier; issued here they
+    // measured 3 us faster than after the fragment reads), then all fragments
+    // of the stage, then the MFMAs.
+    if (s + NSTAGE - 1 < nsub) issue(s + NSTAGE - 1, smem + ((s + NSTAGE - 1) % NSTAGE) * STAGE);
     // The transposed reads are issued from inline asm that waits for them
     // itself (every output is complete when the asm statement ends): the
     // compiler otherwise places a vmcnt(0) before each such read while direct
@@ -227,7 +231,6 @@ __global__ void __launch_bounds__(NT) k_block_grad(const GradArgs g) {
           bfr[kk][j] = __builtin_bit_cast(bf16x8_t, u64x2{rb[4 * j + 2 * kk], rb[4 * j + 2 * kk + 1]});
       }
     }
-    if (s + NSTAGE - 1 < nsub) issue(s + NSTAGE - 1, smem + ((s + NSTAGE - 1) % NSTAGE) * STAGE);
 #pragma unroll
     for (int kk = 0; kk < TK / 16; ++kk)
 #pragma unroll
