@@ -805,22 +805,33 @@ bool pipe_applies(int64_t ncols) {
 #define POETX_PIPE_LDS_KB 96
 #endif
 
-// Workgroups per CU and ring depth of k_gather_rows_pipe: the most row bytes
-// in flight per CU (per_cu * (nbuf - 1) rows) within POETX_PIPE_LDS_KB of LDS
-// per CU, with the wait count of the kernel's deepest wave within the
-// counter's 63. At the 8B MLP widths this gives 28 KB rows one workgroup with
-// three buffers and 8 KB rows two workgroups with six; a full 160 KB ring
-// measured slower for the 8 KB rows and no faster for the 28 KB ones.
+// Workgroups per CU and ring depth of k_gather_rows_pipe. Rows of at most
+// 8 KB: four workgroups per CU, each with a ring of up to 32 KB (four 8 KB
+// rows); wider rows: the most row bytes in flight per CU (per_cu * (nbuf - 1)
+// rows) within POETX_PIPE_LDS_KB of LDS per CU, one or two workgroups. The
+// wait count of the kernel's deepest wave stays within the counter's 63. At
+// the 8B MLP widths: 28 KB rows one workgroup with three buffers; 8 KB rows
+// four with four buffers, which measured 0.039 -> 0.034 ms for the m-wide
+// token gather against two workgroups with six (more in flight per
+// workgroup, e.g. a full 160 KB ring, measured slower).
 template <typename T>
 void pipe_shape(int64_t ncols, int* per_cu, int* nbuf) {
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
   const int64_t ninst = (row_bytes / 16 + 63) / 64;
   const int64_t ld = (ninst + kThreads / 64 - 1) / (kThreads / 64);
   const int64_t st = ((ncols / 8 + kThreads - 1) / kThreads) * (sizeof(T) == 4 ? 2 : 1);
+  auto fit = [&](int d) {
+    while (d > 2 && (d - 2) * ld + (d - 1) * st > 63) --d;
+    return d;
+  };
+  if (row_bytes <= 8192) {
+    *per_cu = 4;
+    *nbuf = fit(static_cast<int>(std::min<int64_t>(kPipeMaxBuf, 32768 / row_bytes)));
+    return;
+  }
   int64_t best = -1;
   for (int pc = 1; pc <= 2; ++pc) {
-    int d = static_cast<int>(std::min<int64_t>(kPipeMaxBuf, POETX_PIPE_LDS_KB * 1024 / (pc * row_bytes)));
-    while (d > 2 && (d - 2) * ld + (d - 1) * st > 63) --d;
+    const int d = fit(static_cast<int>(std::min<int64_t>(kPipeMaxBuf, POETX_PIPE_LDS_KB * 1024 / (pc * row_bytes))));
     if (d < 2) continue;
     const int64_t inflight = pc * (d - 1) * row_bytes;
     if (inflight >= best) {
