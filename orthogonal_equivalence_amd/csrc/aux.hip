@@ -807,15 +807,17 @@ bool pipe_applies(int64_t ncols) {
 
 // Workgroups per CU and ring depth of k_gather_rows_pipe. Rows of at most
 // 8 KB: four workgroups per CU, each with a ring of up to 32 KB (four 8 KB
-// rows); wider rows: the most row bytes in flight per CU (per_cu * (nbuf - 1)
-// rows) within POETX_PIPE_LDS_KB of LDS per CU, one or two workgroups. The
-// wait count of the kernel's deepest wave stays within the counter's 63. At
-// the 8B MLP widths: 28 KB rows one workgroup with three buffers; 8 KB rows
-// four with four buffers, which measured 0.039 -> 0.034 ms for the m-wide
-// token gather against two workgroups with six (more in flight per
-// workgroup, e.g. a full 160 KB ring, measured slower).
+// rows). Wider rows: the most row bytes in flight per CU (per_cu * (nbuf - 1)
+// rows) within POETX_PIPE_LDS_KB of LDS per CU, one or two workgroups; but
+// with at most 16 rows per CU, two workgroups of two buffers each. The wait
+// count of the kernel's deepest wave stays within the counter's 63. At the
+// 8B MLP widths: 8 KB rows four workgroups with four buffers (the m-wide
+// token gather 0.039 -> 0.034 ms against two with six; more in flight per
+// workgroup, e.g. a full 160 KB ring, measured slower); 28 KB rows over 8192
+// tokens one workgroup with three buffers; the 4096 rows of 28 KB of the
+// weight reframe two with two (0.069 -> 0.065 ms).
 template <typename T>
-void pipe_shape(int64_t ncols, int* per_cu, int* nbuf) {
+void pipe_shape(int64_t ncols, int64_t nrows, int* per_cu, int* nbuf) {
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
   const int64_t ninst = (row_bytes / 16 + 63) / 64;
   const int64_t ld = (ninst + kThreads / 64 - 1) / (kThreads / 64);
@@ -824,6 +826,11 @@ void pipe_shape(int64_t ncols, int* per_cu, int* nbuf) {
     while (d > 2 && (d - 2) * ld + (d - 1) * st > 63) --d;
     return d;
   };
+  if (row_bytes > 8192 && nrows <= 16 * 256 && 4 * row_bytes <= 160 * 1024) {
+    *per_cu = 2;
+    *nbuf = fit(2);
+    return;
+  }
   if (row_bytes <= 8192) {
     *per_cu = 4;
     *nbuf = fit(static_cast<int>(std::min<int64_t>(kPipeMaxBuf, 32768 / row_bytes)));
@@ -850,7 +857,7 @@ void launch_gather(const void* in, int64_t ld_in, const int32_t* rmap_in, void* 
   const int64_t row_bytes = ncols * static_cast<int64_t>(sizeof(T));
   if (pipe_applies<T>(ncols)) {
     int per_cu = 1, nbuf = 2;
-    pipe_shape<T>(ncols, &per_cu, &nbuf);
+    pipe_shape<T>(ncols, nrows, &per_cu, &nbuf);
     const unsigned nwg = static_cast<unsigned>(std::min<int64_t>(nrows, 256 * per_cu));
     hipLaunchKernelGGL(k_gather_rows_pipe<T>, dim3(nwg), dim3(kThreads), static_cast<size_t>(nbuf * row_bytes), s,
                        static_cast<const T*>(in), ld_in, rmap_in, static_cast<T*>(out), ld_out, rmap_out, cidx,
