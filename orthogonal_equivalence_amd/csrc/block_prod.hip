@@ -16,11 +16,12 @@
 // last of which writes the packed gradient straight from its epilogue.
 //
 // gfx950 design: 128 x 128 output tile per workgroup (the tiles of one block
-// on one XCD), 4 waves of 64 x 64
-// (2 x 2 tiles of v_mfma_f32_32x32x16_bf16), K in steps of 64 through two
-// LDS stages filled with global_load_lds_dwordx4 (128-byte rows, XOR
-// swizzle); the epilogue stages each wave's 32 x 64 band through LDS so that
-// row-major and transposed outputs are both written with 16-byte stores.
+// on one XCD), 8 waves of 64 x 32 (2 x 1 tiles of v_mfma_f32_32x32x16_bf16;
+// two waves per SIMD, so that one wave's LDS and MFMA latencies run under
+// the other's work), K in steps of 64 through two LDS stages filled with
+// global_load_lds_dwordx4 (128-byte rows, XOR swizzle); the epilogue stages
+// each wave's 32 x 32 band through LDS so that row-major and transposed
+// outputs are both written with 16-byte stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,12 +32,13 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 
 constexpr int TB = 128;             // output tile
 constexpr int BK = 64;              // K per stage
-constexpr int NT = 256;             // 4 waves
+constexpr int NT = 512;             // 8 waves: 2 along M x 4 along N
+constexpr int WTN = 32;             // wave tile width (columns)
 constexpr int kRowBytes = BK * 2;   // 128
 constexpr int kTileBytes = TB * kRowBytes;  // 16 KB per operand and stage
 constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kInst = kTileBytes / 1024 / (NT / 64);  // loads per wave per operand (4)
-constexpr int kSlab = 64 + 4;       // epilogue slab row stride (floats)
+constexpr int kInst = kTileBytes / 1024 / (NT / 64);  // loads per wave per operand (2)
+constexpr int kSlab = WTN + 4;      // epilogue slab row stride (floats)
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -94,11 +96,12 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
   const int ksteps = d.b / BK;
   const int nk = ksteps * (d.A2 ? 2 : 1);
 
-  f32x16_t acc[2][2];
+  constexpr int TNw = WTN / 32;
+  f32x16_t acc[2][TNw];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TNw; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) koff[kk] = lrow * kRowBytes + (((2 * kk + (lane >> 5)) ^ sw) << 4);
   const int abase = wm * 64 * kRowBytes;
-  const int bbase = kTileBytes + wn * 64 * kRowBytes;
+  const int bbase = kTileBytes + wn * WTN * kRowBytes;
 
   issue(0, smem);
   for (int s = 0; s < nk; ++s) {
@@ -129,22 +132,22 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TNw; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = -acc[i][j][r];
     }
     const char* st = smem + (s & 1) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t af[2], bfr[2];
+      bf16x8_t af[2], bfr[TNw];
 #pragma unroll
       for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
+      for (int j = 0; j < TNw; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TNw; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
@@ -152,41 +155,47 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
   const float sgn = d.neg2 ? -1.f : 1.f;
   const float alpha = d.alpha * sgn, alpha2 = d.alpha2 * sgn;
 
-  // epilogue: per wave and 32-row band, a 32 x 64 slab of v1 (and v2)
+  // epilogue: per wave and 32-row band, a 32 x WTN slab of v1 (and v2)
   __syncthreads();
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * kSlab;
+  constexpr int kCpr = WTN / 8;              // 8-column chunks per slab row
+  constexpr int kCpl = 32 * kCpr / 64;       // chunks per lane
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TNw; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kSlab + j * 32 + lrow] = acc[i][j][r];
     if (pk) {
-      // packed upper triangle: lane -> column, one row per step, so that each
-      // store instruction covers a contiguous run of the row's packed entries
-      const int gn = n0 + wn * 64 + lane;
-      float ef[32];
+      // packed upper triangle: lane -> column (64 / WTN rows at a time), one
+      // row per step, so that each store instruction covers contiguous runs
+      // of the rows' packed entries
+      constexpr int kRowsAtOnce = 64 / WTN;
+      const int lc = lane % WTN, lr = lane / WTN;
+      const int gn = n0 + wn * WTN + lc;
+      float ef[32 / kRowsAtOnce];
 #pragma unroll
-      for (int row = 0; row < 32; ++row) {
-        const int gi = i0 + wm * 64 + i * 32 + row;
-        ef[row] = d.Ef ? d.Ef[zoff + static_cast<int64_t>(gi) * d.b + gn] : 0.f;
+      for (int q = 0; q < 32 / kRowsAtOnce; ++q) {
+        const int gi = i0 + wm * 64 + i * 32 + q * kRowsAtOnce + lr;
+        ef[q] = d.Ef ? d.Ef[zoff + static_cast<int64_t>(gi) * d.b + gn] : 0.f;
       }
 #pragma unroll
-      for (int row = 0; row < 32; ++row) {
+      for (int q = 0; q < 32 / kRowsAtOnce; ++q) {
+        const int row = q * kRowsAtOnce + lr;
         const int gi = i0 + wm * 64 + i * 32 + row;
-        const float v = alpha * slab[row * kSlab + lane] + d.beta * ef[row];
+        const float v = alpha * slab[row * kSlab + lc] + d.beta * ef[q];
         if (gi < gn && gn < pk_r)
           pk[pk_off + static_cast<int64_t>(gi) * pk_r - static_cast<int64_t>(gi) * (gi + 1) / 2 + gn - gi - 1] = v;
       }
       continue;
     }
-    // row pass: lane -> (row, 8 columns); 32 rows x 8 chunks = 4 per lane
+    // row pass: lane -> (row, 8 columns); 32 rows x kCpr chunks
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kCpl; ++c) {
       const int ch = lane + c * 64;
-      const int row = ch >> 3, col = (ch & 7) * 8;
-      const int gi = i0 + wm * 64 + i * 32 + row, gn = n0 + wn * 64 + col;
+      const int row = ch / kCpr, col = (ch % kCpr) * 8;
+      const int gi = i0 + wm * 64 + i * 32 + row, gn = n0 + wn * WTN + col;
       const int64_t roff = static_cast<int64_t>(gi) * d.b + gn;
       const int64_t off = zoff + roff;
       float a[8], v1[8];
@@ -224,15 +233,15 @@ __global__ void __launch_bounds__(NT, 2) k_block_prod(const BlockProdDesc d) {
       }
     }
     if (out1t) {
-      // transposed pass: lane -> (column, 8 rows); 64 columns x 4 row groups = 4 per lane
+      // transposed pass: lane -> (column, 8 rows); WTN columns x 4 row groups
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < WTN * 4 / 64; ++c) {
         const int ch = lane + c * 64;
         const int col = ch >> 2, rg = (ch & 3) * 8;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = slab[(rg + e) * kSlab + col];
-        const int gn = n0 + wn * 64 + col, gi = i0 + wm * 64 + i * 32 + rg;
+        const int gn = n0 + wn * WTN + col, gi = i0 + wm * 64 + i * 32 + rg;
         store8(out1t, zout + static_cast<int64_t>(gn) * d.b + gi, d.out1_f32, v);
       }
     }
