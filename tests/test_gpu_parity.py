@@ -157,6 +157,12 @@ SMALL = [
     # launches of its own; last P blocks of 8 and 16
     _cfg("f32_wide_rows", 8, 64, 16392, 64, 512, "f32", "f32", 60),
     _cfg("bf16_wide_rows", 8, 64, 16400, 64, 256, "bf16", "bf16", 61),
+    # the backward dense product in its persistent form (whole rounds of
+    # 256 x 256 tiles over the 256 CUs): two tiles per workgroup, the second's
+    # first K slice loaded during the first's last step (8192 x 4096 output,
+    # K = 1024), and one tile per workgroup (4096 x 4096, K = 512)
+    _cfg("bf16_persistent_bwd", 8192, 4096, 1024, 256, 256, "bf16", "bf16", 62),
+    _cfg("bf16_persistent_bwd_one", 4096, 4096, 512, 256, 256, "bf16", "bf16", 63),
 ]
 
 
