@@ -38,6 +38,11 @@
 //    scales are applied in the epilogue as for any scaled product.
 //  * Output tiles are ordered so that each XCD works on one contiguous band
 //    of tiles (shared A/B panels stay in that XCD's L2).
+//  * Whole rounds of whole tiles with a K-contiguous B (the backward) run
+//    persistently, one workgroup per CU over its band's tiles, so that each
+//    tile boundary overlaps the next tile's first loads and the epilogue's
+//    stores (k_gemm_dense_persist); with the N-contiguous B of the forward
+//    the same scheme measured slower and is not used.
 //  * When the tiles do not fill a whole number of rounds over the 256 CUs,
 //    the tiles of the last, partial round are split along K into k parts
 //    (k * tail <= 256), so that round runs on (nearly) every CU. Every part
