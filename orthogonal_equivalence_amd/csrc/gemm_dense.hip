@@ -606,16 +606,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense_persist(const GemmDesc d, 
     // the next tile; after the last one, this tile again (a harmless re-load
     // of its first slice into the free buffer)
     int m1 = m0, n1 = n0;
-    int64_t goff1[kInstPerTile];
-#pragma unroll
-    for (int i = 0; i < kInstPerTile; ++i) goff1[i] = goff[i];
-    if (v + stride < ntiles) {
-      coords(v + stride, m1, n1);
-      if constexpr (BNC) {
-#pragma unroll
-        for (int i = 0; i < kInstPerTile; ++i) goff1[i] = nc_offset(d.ldb, n1, d.N, wave, lane, i);
-      }
-    }
+    if (v + stride < ntiles) coords(v + stride, m1, n1);
 
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -638,6 +629,13 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense_persist(const GemmDesc d, 
       const char* st = smem + cur * kStageBytes;
       char* nxt = smem + (cur ^ 1) * kStageBytes;
       const bool last = it == nk - 1;
+      if constexpr (BNC) {
+        // the last step loads the next tile: its B offsets replace this one's
+        if (last) {
+#pragma unroll
+          for (int i = 0; i < kInstPerTile; ++i) goff[i] = nc_offset(d.ldb, n1, d.N, wave, lane, i);
+        }
+      }
       const int kpf = last ? 0 : (it + 1) * BK;
       const int am = last ? m1 : m0, bn = last ? n1 : n0;
       const bf16_t* Bpf = BNC ? B + static_cast<int64_t>(kpf) * d.ldb : B;
@@ -646,8 +644,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense_persist(const GemmDesc d, 
 #pragma unroll
         for (int i = load_first<false>(kk); i < load_first<false>(kk + 1); ++i) {
           if (BNC && i >= kInstPerTile)
-            load_one_nc(Bpf, last ? goff1[i % kInstPerTile] : goff[i % kInstPerTile], nxt + kTileBytes, wave,
-                        i % kInstPerTile);
+            load_one_nc(Bpf, goff[i % kInstPerTile], nxt + kTileBytes, wave, i % kInstPerTile);
           else
             load_one(i < kInstPerTile ? A : B, i < kInstPerTile ? d.lda : d.ldb, i < kInstPerTile ? am : bn,
                      i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
@@ -725,8 +722,6 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense_persist(const GemmDesc d, 
     base = (base + nk) & 1;
     m0 = m1;
     n0 = n1;
-#pragma unroll
-    for (int i = 0; i < kInstPerTile; ++i) goff[i] = goff1[i];
     first = false;
   }
   // the last tile's re-load must land before the workgroup's LDS is released
