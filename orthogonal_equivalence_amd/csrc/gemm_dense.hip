@@ -222,6 +222,44 @@ constexpr int kI8StageBytes = BN * BK;
 constexpr int kI8Chunks = kI8StageBytes / 1024 / (NT / 64);  // 2
 static_assert(NSTAGE * 2 * BM * BK * 2 + 2 * kI8StageBytes <= 160 * 1024, "LDS with int8 staging");
 
+// One K group (16 of the stage's K) of a wave's 128 x 64 outputs: A
+// fragments from the stage's A rows, B fragments from its B rows (K-contiguous)
+// or through transposed reads of its K rows (N-contiguous, inline asm that
+// waits for its own results: as the builtin, the read gets a vmcnt(0) in front
+// of it while direct loads are in flight), then the 4 x 2 MFMAs.
+template <bool BNC>
+__device__ __forceinline__ void kgroup_mfma(const char* st, int kk, const int (&koff)[BK / 16], int abase, int bbase,
+                                            const uint32_t (&bnc_addr)[TN], f32x16_t (&acc)[TM][TN]) {
+  bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
+  if constexpr (BNC) {
+    typedef unsigned long long u64;
+    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+    const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + kk * 16 * kNcRowBytes;
+    const uint32_t a0 = sb + bnc_addr[0], a1 = sb + bnc_addr[1];
+    u64 rb[4];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n ds_read_b64_tr_b16 %1, %4 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %5\n ds_read_b64_tr_b16 %3, %5 offset:2048\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3])
+        : "v"(a0), "v"(a1)
+        : "memory");
+    bfr[0] = __builtin_bit_cast(bf16x8_t, u64x2{rb[0], rb[1]});
+    bfr[1] = __builtin_bit_cast(bf16x8_t, u64x2{rb[2], rb[3]});
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
 // BNC: B is N-contiguous (B[k * ldb + n]) instead of K-contiguous.
 // BI8: B holds int8 codes (ldb in elements = bytes).
 template <bool BNC, bool BI8>
@@ -433,35 +471,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
                    i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
                    i % kInstPerTile);
       }
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
-      if constexpr (BNC) {
-        typedef unsigned long long u64;
-        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-        const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + kk * 16 * kNcRowBytes;
-        const uint32_t a0 = sb + bnc_addr[0], a1 = sb + bnc_addr[1];
-        u64 rb[4];
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %4\n ds_read_b64_tr_b16 %1, %4 offset:2048\n"
-            "ds_read_b64_tr_b16 %2, %5\n ds_read_b64_tr_b16 %3, %5 offset:2048\n"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3])
-            : "v"(a0), "v"(a1)
-            : "memory");
-        bfr[0] = __builtin_bit_cast(bf16x8_t, u64x2{rb[0], rb[1]});
-        bfr[1] = __builtin_bit_cast(bf16x8_t, u64x2{rb[2], rb[3]});
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      kgroup_mfma<BNC>(st, kk, koff, abase, bbase, bnc_addr, acc);
       if constexpr (BI8) {
         // the next stage's codes, loaded one step ago, into its B tile; younger
         // loads are this step's A loads and the codes two stages ahead
@@ -650,35 +660,7 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense_persist(const GemmDesc d, 
                      i < kInstPerTile ? d.M : d.N, kpf, nxt + (i < kInstPerTile ? 0 : kTileBytes), wave, lane,
                      i % kInstPerTile);
         }
-        bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(st + abase + i * 32 * kRowBytes + koff[kk]);
-        if constexpr (BNC) {
-          typedef unsigned long long u64;
-          typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-          const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st)) + kk * 16 * kNcRowBytes;
-          const uint32_t a0 = sb + bnc_addr[0], a1 = sb + bnc_addr[1];
-          u64 rb[4];
-          asm volatile(
-              "ds_read_b64_tr_b16 %0, %4\n ds_read_b64_tr_b16 %1, %4 offset:2048\n"
-              "ds_read_b64_tr_b16 %2, %5\n ds_read_b64_tr_b16 %3, %5 offset:2048\n"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(rb[0]), "=&v"(rb[1]), "=&v"(rb[2]), "=&v"(rb[3])
-              : "v"(a0), "v"(a1)
-              : "memory");
-          bfr[0] = __builtin_bit_cast(bf16x8_t, u64x2{rb[0], rb[1]});
-          bfr[1] = __builtin_bit_cast(bf16x8_t, u64x2{rb[2], rb[3]});
-        } else {
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + bbase + j * 32 * kRowBytes + koff[kk]);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        kgroup_mfma<BNC>(st, kk, koff, abase, bbase, bnc_addr, acc);
       }
     }
 
