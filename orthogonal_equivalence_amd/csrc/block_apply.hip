@@ -8,7 +8,7 @@
 // gfx950 design: one workgroup owns one block and a contiguous run of
 // tokens. Each of its b/32 waves keeps its 32 output columns of B_j resident
 // in registers as MFMA fragments for the whole run, so B_j is read once per
-// workgroup. A 512 x 512 plane would fill a CU's whole register file, so for
+// workgroup (in whole rows through LDS before the first sub-tile). A 512 x 512 plane would fill a CU's whole register file, so for
 // b = 512 two workgroups share a block and a token run, each owning 256 of
 // its output columns (8 waves of 128 fragment registers) and staging the
 // full 512-column input; the two are issued 8 workgroups apart so that they
@@ -28,6 +28,11 @@ namespace {
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
 constexpr int TT = 32;  // tokens per sub-tile
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int B>
 __device__ __forceinline__ int swz_row(int r) {
@@ -79,15 +84,20 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   if (t_begin >= t_end) return;
   const int nsub = static_cast<int>((t_end - t_begin + TT - 1) / TT);
 
-  // this wave's 32 columns of B_j as MFMA B-operand fragments (column n, 8 k's)
-  const int lcol = lane & 31;
-  const int ncol = cofs + wave * 32 + lcol;
-  const bf16_t* brow = plane + static_cast<int64_t>(blk) * B * B + static_cast<int64_t>(ncol) * B + (lane >> 5) * 8;
-  bf16x8_t gfrag[KS];
+  // direct loads: each wave fills LPW x 1 KB of a stage. A stage holds 32
+  // rows of ROWB bytes (16-byte chunk c of row r in slot c ^ swz_row(r)):
+  // either 32 tokens of the input or the 32 plane rows one wave keeps.
+  auto issue_plane = [&](int w, int stage) {
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) gfrag[kk] = *reinterpret_cast<const bf16x8_t*>(brow + kk * 16);
-
-  // direct loads: each wave fills LPW x 1 KB of a stage
+    for (int i = 0; i < LPW; ++i) {
+      const int q = (wave * LPW + i) * 64 + lane;
+      const int row = q / CPR, slot = q % CPR;
+      const int c = slot ^ swz_row<B>(row);
+      const bf16_t* src = plane + (static_cast<int64_t>(blk) * B + cofs + w * 32 + row) * B + c * 8;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                       (lds_void_t)(smem + stage * STAGE + (wave * LPW + i) * 1024), 16, 0, 0);
+    }
+  };
   auto issue = [&](int sub, int stage) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -103,8 +113,52 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
     }
   };
 
-  const int arow = lane & 31;
+  const int arow = lane & 31, lcol = lane & 31;
   const int asw = swz_row<B>(arow);
+
+  // This wave's 32 columns of B_j as MFMA B-operand fragments (lane: column
+  // cofs + 32 wave + lane % 32, k's 16 kk + 8 (lane / 32) .. +7), read from
+  // the plane's rows. Loaded straight into registers, each load instruction
+  // would touch 32 rows for 32 bytes each; staged through LDS in whole rows
+  // (one wave's 32 rows per stage-sized buffer, as many buffers in flight as
+  // the stages and slabs hold), every cache line is fetched once and the
+  // fragments come out like the input's A fragments.
+  constexpr int NBUF = (2 * STAGE + NW * SLAB) / STAGE < NW ? (2 * STAGE + NW * SLAB) / STAGE : NW;
+  static_assert(NBUF >= 2 && NBUF * STAGE <= 2 * STAGE + NW * SLAB, "fragment staging buffers");
+  bf16x8_t gfrag[KS];
+#pragma unroll
+  for (int w = 0; w < NBUF; ++w) issue_plane(w, w);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    // rounds w+1 .. min(w + NBUF, NW) - 1 may still be in flight
+    const int younger = (w + NBUF - 1 < NW - 1 ? w + NBUF - 1 : NW - 1) - w;
+    if (younger >= 3) wait_vmcnt<3 * LPW>();
+    else if (younger == 2) wait_vmcnt<2 * LPW>();
+    else if (younger == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (wave == w) {
+      const char* st = smem + (w % NBUF) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        gfrag[kk] = *reinterpret_cast<const bf16x8_t*>(st + arow * ROWB + ((c ^ asw) << 4));
+      }
+    }
+    if (w + NBUF < NW) {
+      // every wave is past its reads of this buffer before it is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_plane(w + NBUF, w % NBUF);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
   float* slab = reinterpret_cast<float*>(smem + 2 * STAGE + wave * SLAB);
   issue(0, 0);
   for (int s = 0; s < nsub; ++s) {
