@@ -34,6 +34,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+__device__ __forceinline__ void lds_barrier() {
+  // LDS-only barrier: the direct loads in flight are waited for by count
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int B>
 __device__ __forceinline__ int swz_row(int r) {
   // rows of >= 256 bytes: 16-byte slot bank group = slot % 16, spread by r;
@@ -41,6 +48,58 @@ __device__ __forceinline__ int swz_row(int r) {
   if constexpr (B >= 128) return r & 15;
   else return (r >> 1) & 7;
 }
+
+// Per wave, the MFMA fragments frag[kk] (lane: row 32 wave + lane % 32 of a
+// row-major plane of b-element rows, elements 16 kk + 8 (lane / 32) .. +7),
+// for NW waves. Loaded straight into registers, each load instruction would
+// touch 32 rows for 32 bytes each, so every cache line would reach the CU
+// about four times. Instead the rows go through LDS whole: buffer j of
+// NBUF holds one wave's 32 rows (chunk c of row r in slot c ^ swz_row(r),
+// 1 KB direct loads shared by all waves), NBUF of them in flight, and each
+// wave reads its own fragments out of its buffer. Ends with the buffers free.
+template <int b, int NW, int NBUF>
+__device__ __forceinline__ void stage_frags(const bf16_t* __restrict__ rows, char* lds, int wave, int lane,
+                                            bf16x8_t (&frag)[b / 16]) {
+  constexpr int ROWB = 2 * b, CPR = ROWB / 16, BUF = 32 * ROWB, LPW = BUF / 1024 / NW;
+  static_assert(LPW * NW * 1024 == BUF && NBUF >= 2 && NBUF <= 4 && NBUF <= NW, "fragment staging");
+  auto issue = [&](int w, int buf) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int q = (wave * LPW + i) * 64 + lane;
+      const int row = q / CPR, slot = q % CPR;
+      const int c = slot ^ swz_row<b>(row);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(rows + static_cast<int64_t>(w * 32 + row) * b + c * 8),
+                                       (lds_void_t)(lds + buf * BUF + (wave * LPW + i) * 1024), 16, 0, 0);
+    }
+  };
+  const int r = lane & 31, sw = swz_row<b>(r);
+#pragma unroll
+  for (int w = 0; w < NBUF; ++w) issue(w, w);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    // rounds w+1 .. min(w + NBUF, NW) - 1 may still be in flight
+    const int younger = (w + NBUF - 1 < NW - 1 ? w + NBUF - 1 : NW - 1) - w;
+    if (younger >= 3) wait_vmcnt<3 * LPW>();
+    else if (younger == 2) wait_vmcnt<2 * LPW>();
+    else if (younger == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (wave == w) {
+      const char* st = lds + (w % NBUF) * BUF;
+#pragma unroll
+      for (int kk = 0; kk < b / 16; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        frag[kk] = *reinterpret_cast<const bf16x8_t*>(st + r * ROWB + ((c ^ sw) << 4));
+      }
+    }
+    if (w + NBUF < NW) {
+      lds_barrier();  // every wave is past its reads of this buffer
+      issue(w + NBUF, w % NBUF);
+    }
+  }
+  lds_barrier();
+}
+
 
 // workgroups of 8 waves and b <= 256: two per CU, 4 waves per SIMD; b = 512:
 // one per CU (its fragments take 128 registers per lane), 2 waves per SIMD
@@ -84,20 +143,7 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   if (t_begin >= t_end) return;
   const int nsub = static_cast<int>((t_end - t_begin + TT - 1) / TT);
 
-  // direct loads: each wave fills LPW x 1 KB of a stage. A stage holds 32
-  // rows of ROWB bytes (16-byte chunk c of row r in slot c ^ swz_row(r)):
-  // either 32 tokens of the input or the 32 plane rows one wave keeps.
-  auto issue_plane = [&](int w, int stage) {
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int q = (wave * LPW + i) * 64 + lane;
-      const int row = q / CPR, slot = q % CPR;
-      const int c = slot ^ swz_row<B>(row);
-      const bf16_t* src = plane + (static_cast<int64_t>(blk) * B + cofs + w * 32 + row) * B + c * 8;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
-                                       (lds_void_t)(smem + stage * STAGE + (wave * LPW + i) * 1024), 16, 0, 0);
-    }
-  };
+  // direct loads: each wave fills LPW x 1 KB of a stage
   auto issue = [&](int sub, int stage) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -116,48 +162,13 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   const int arow = lane & 31, lcol = lane & 31;
   const int asw = swz_row<B>(arow);
 
-  // This wave's 32 columns of B_j as MFMA B-operand fragments (lane: column
-  // cofs + 32 wave + lane % 32, k's 16 kk + 8 (lane / 32) .. +7), read from
-  // the plane's rows. Loaded straight into registers, each load instruction
-  // would touch 32 rows for 32 bytes each; staged through LDS in whole rows
-  // (one wave's 32 rows per stage-sized buffer, as many buffers in flight as
-  // the stages and slabs hold), every cache line is fetched once and the
-  // fragments come out like the input's A fragments.
+  // this wave's 32 columns of B_j as MFMA B-operand fragments (lane: column
+  // cofs + 32 wave + lane % 32, k's 16 kk + 8 (lane / 32) .. +7): rows of the
+  // plane, staged through the stage and slab space
   constexpr int NBUF = (2 * STAGE + NW * SLAB) / STAGE < NW ? (2 * STAGE + NW * SLAB) / STAGE : NW;
-  static_assert(NBUF >= 2 && NBUF * STAGE <= 2 * STAGE + NW * SLAB, "fragment staging buffers");
+  static_assert(NBUF * STAGE <= 2 * STAGE + NW * SLAB, "fragment staging buffers");
   bf16x8_t gfrag[KS];
-#pragma unroll
-  for (int w = 0; w < NBUF; ++w) issue_plane(w, w);
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    // rounds w+1 .. min(w + NBUF, NW) - 1 may still be in flight
-    const int younger = (w + NBUF - 1 < NW - 1 ? w + NBUF - 1 : NW - 1) - w;
-    if (younger >= 3) wait_vmcnt<3 * LPW>();
-    else if (younger == 2) wait_vmcnt<2 * LPW>();
-    else if (younger == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (wave == w) {
-      const char* st = smem + (w % NBUF) * STAGE;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-        gfrag[kk] = *reinterpret_cast<const bf16x8_t*>(st + arow * ROWB + ((c ^ asw) << 4));
-      }
-    }
-    if (w + NBUF < NW) {
-      // every wave is past its reads of this buffer before it is refilled
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue_plane(w + NBUF, w % NBUF);
-    }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  stage_frags<B, NW, (NBUF < 4 ? NBUF : 4)>(plane + (static_cast<int64_t>(blk) * B + cofs) * B, smem, wave, lane, gfrag);
 
   float* slab = reinterpret_cast<float*>(smem + 2 * STAGE + wave * SLAB);
   issue(0, 0);
@@ -247,13 +258,12 @@ k_block_apply_left(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int6
   if (c_begin >= c_end) return;
   const int nsub = static_cast<int>((c_end - c_begin + TC - 1) / TC);
 
-  // A fragments: rows 32w + (l % 32) of the plane, 8 k's at 16 kk + 8 (l / 32)
+  // A fragments: rows 32w + (l % 32) of the plane, 8 k's at 16 kk + 8 (l / 32),
+  // staged through the stage and slab space
   const int lrow = lane & 31;
-  const bf16_t* arow = plane + static_cast<int64_t>(blk) * B * B + static_cast<int64_t>(wave * 32 + lrow) * B +
-                       (lane >> 5) * 8;
+  static_assert(4 * 32 * B * 2 <= 2 * STAGE + 8 * SLAB * 4, "fragment staging buffers");
   bf16x8_t afrag[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) afrag[kk] = *reinterpret_cast<const bf16x8_t*>(arow + kk * 16);
+  stage_frags<B, 8, 4>(plane + static_cast<int64_t>(blk) * B * B, smem, wave, lane, afrag);
 
   // loads: 32 instructions of 8 rows x 128 bytes per stage, four per wave;
   // lane l lands in slot l % 8 of row 8 q + l / 8 and fetches the chunk that
