@@ -116,7 +116,9 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   constexpr int LPW = STAGE / 1024 / NW;  // 1 KB direct loads per wave and stage
   constexpr int KS = B / 16;
   constexpr int SLAB = 32 * 33 * 4;  // per wave: 32 rows x 32 fp32 columns (+1 pad)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + NW * SLAB];
+  constexpr int NSTG = 2;  // stages
+  constexpr int SMEM = NSTG * STAGE + NW * SLAB;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   run_side_job(job);
   const int lane = threadIdx.x & 63;
@@ -165,19 +167,14 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
   // this wave's 32 columns of B_j as MFMA B-operand fragments (lane: column
   // cofs + 32 wave + lane % 32, k's 16 kk + 8 (lane / 32) .. +7): rows of the
   // plane, staged through the stage and slab space
-  constexpr int NBUF = (2 * STAGE + NW * SLAB) / STAGE < NW ? (2 * STAGE + NW * SLAB) / STAGE : NW;
-  static_assert(NBUF * STAGE <= 2 * STAGE + NW * SLAB, "fragment staging buffers");
+  constexpr int NBUF = SMEM / STAGE < NW ? SMEM / STAGE : NW;
+  static_assert(NBUF * STAGE <= SMEM, "fragment staging buffers");
   bf16x8_t gfrag[KS];
   stage_frags<B, NW, (NBUF < 4 ? NBUF : 4)>(plane + (static_cast<int64_t>(blk) * B + cofs) * B, smem, wave, lane, gfrag);
 
-  float* slab = reinterpret_cast<float*>(smem + 2 * STAGE + wave * SLAB);
-  issue(0, 0);
-  for (int s = 0; s < nsub; ++s) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (s + 1 < nsub) issue(s + 1, (s + 1) & 1);
-    const char* st = smem + (s & 1) * STAGE;
-    f32x16_t acc;
+  float* slab = reinterpret_cast<float*>(smem + NSTG * STAGE + wave * SLAB);
+  // sub-tile s's product into acc: the MFMA chain over the stage st
+  auto product = [&](const char* st, f32x16_t& acc) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
@@ -186,36 +183,61 @@ k_block_apply(const bf16_t* __restrict__ in, bf16_t* __restrict__ out, int64_t l
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(st + arow * ROWB + ((c ^ asw) << 4));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gfrag[kk], acc, 0, 0, 0);
     }
-    // accumulator -> this wave's fp32 slab (32 rows x 32 columns), then per
-    // lane 8 consecutive columns of a row: + residual from the staged input,
-    // * column scale, bfloat16, one 16-byte store
+  };
+  // accumulator -> this wave's fp32 slab (32 rows x 32 columns)
+  auto to_slab = [&](const f32x16_t& acc) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) slab[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 33 + lcol] = acc[r];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // half i of sub-tile s from the slab: per lane 8 consecutive columns of a
+  // row, + residual from the staged input st, * column scale, bfloat16, one
+  // 16-byte store
+  auto store_half = [&](int i, int s, const char* st) {
+    const int q = lane + i * 64;
+    const int row = q >> 2, c4 = q & 3;
+    const int64_t t = t_begin + static_cast<int64_t>(s) * TT + row;
+    const int col = cofs + wave * 32 + c4 * 8;
+    const int chunk = col >> 3;
+    // the residual, read by inline asm that waits for its own result: as an
+    // ordinary LDS load it gets a wait for every direct load in flight, the
+    // next stage's included
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 xr;
+    const uint32_t xa = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>(st + row * ROWB + ((chunk ^ swz_row<B>(row)) << 4)));
+    asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(xr) : "v"(xa) : "memory");
+    const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
+    float v[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = lane + i * 64;
-      const int row = q >> 2, c4 = q & 3;
-      const int64_t t = t_begin + static_cast<int64_t>(s) * TT + row;
-      const int col = cofs + wave * 32 + c4 * 8;
-      const int chunk = col >> 3;
-      const uint4 xr = *reinterpret_cast<const uint4*>(st + row * ROWB + ((chunk ^ swz_row<B>(row)) << 4));
-      const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = slab[row * 33 + c4 * 8 + 2 * e] + __uint_as_float(xw[e] << 16);
-        v[2 * e + 1] = slab[row * 33 + c4 * 8 + 2 * e + 1] + __uint_as_float(xw[e] & 0xffff0000u);
-      }
-      if (scale) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= scale[col0 + (col < width ? col : 0) + e];
-      }
-      if (t < t_end && col < width)
-        *reinterpret_cast<uint4*>(out + t * ld + col0 + col) =
-            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7]));
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = slab[row * 33 + c4 * 8 + 2 * e] + __uint_as_float(xw[e] << 16);
+      v[2 * e + 1] = slab[row * 33 + c4 * 8 + 2 * e + 1] + __uint_as_float(xw[e] & 0xffff0000u);
     }
+    if (scale) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= scale[col0 + (col < width ? col : 0) + e];
+    }
+    if (t < t_end && col < width)
+      *reinterpret_cast<uint4*>(out + t * ld + col0 + col) =
+          make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7]));
+  };
+  auto epilogue = [&](const f32x16_t& acc, int s, const char* st) {
+    to_slab(acc);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    store_half(0, s, st);
+    store_half(1, s, st);
+  };
+
+  issue(0, 0);
+  for (int s = 0; s < nsub; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (s + 1 < nsub) issue(s + 1, (s + 1) & 1);
+    const char* st = smem + (s & 1) * STAGE;
+    f32x16_t acc;
+    product(st, acc);
+    epilogue(acc, s, st);
   }
 }
 
