@@ -41,6 +41,8 @@ __all__ = [
     "dense_block_orthogonal", "dequantize", "permuted_weight", "forward",
     "backward", "backward_blocks", "merge", "weight_centric_forward", "inner",
     "requantize_int8_per_col", "merge_xq", "philox4x64_10", "perm_words",
+    "FP8_MAX", "fp8_e4m3_values", "fp8_e4m3_decode", "fp8_e4m3_encode",
+    "dequantize_fp8", "requantize_fp8_per_col",
     "perm_keys", "sample_perm", "merge_due", "PERM_KEY_BITS",
 ]
 
@@ -361,13 +363,79 @@ def requantize_int8_per_col(W):
     return codes, scale
 
 
-def merge_xq(Wq, scale, q_r, q_p, perm_r, perm_p, b_r, b_p):
-    """Merge of a quantized base weight [XQ], [MG]. The page does not say how
-    the merged weight is stored again; reading: dequantize, W0 <- R W0 P in
-    float64, then store per output column as the input was stored. Returns
-    (codes, scale, merged float64 weight before storage)."""
-    W = merge(dequantize(Wq, scale), q_r, q_p, perm_r, perm_p, b_r, b_p)
-    codes, new_scale = requantize_int8_per_col(W)
+# ----------------------------------------------------------------------------
+# fp8 base weight  ([XQ] extension)
+# ----------------------------------------------------------------------------
+#
+# [XQ] stores the base weight in int8 and expects lower-precision formats such
+# as FP8 to need no quantization-aware training either. The format taken is
+# E4M3 of the OCP 8-bit floating point specification (OFP8): a code byte is a
+# sign bit, a 4-bit exponent field e with bias 7 and a 3-bit mantissa m; e > 0
+# gives (1 + m/8) 2^(e-7), e = 0 gives the subnormal m 2^-9, and e = 15 with
+# m = 7 is NaN (there is no infinity), so the largest finite magnitude is 448.
+# Storage per output column as for int8, a reading: scale[c] = max_r |W[r, c]|
+# / 448 in float32 (1 for a zero column) and the code of W / scale (float32)
+# is the nearest E4M3 value, ties to the even code, magnitudes past 448 kept
+# at 448, and the sign bit that of W / scale.
+
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_values():
+    """Magnitudes of the finite non-negative E4M3 codes 0..126, in code order
+    (increasing)."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def fp8_e4m3_decode(codes):
+    """Value of each E4M3 code byte; NaN for 0x7F and 0xFF."""
+    c = np.asarray(codes).astype(np.uint8).astype(np.int64)
+    low = c & 0x7F
+    v = np.where(low == 0x7F, np.nan, fp8_e4m3_values()[np.minimum(low, 126)])
+    return np.where(c & 0x80, -v, v)
+
+
+def fp8_e4m3_encode(x):
+    """E4M3 code byte of each finite value: the nearest code, ties to the even
+    code, magnitudes past 448 saturated, the sign bit that of x."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = fp8_e4m3_values()
+    a = np.minimum(np.abs(x), FP8_MAX)
+    hi = np.minimum(np.searchsorted(vals, a, side="left"), 126)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    mag = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    return (mag | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def dequantize_fp8(Wq, scale):
+    """Run-time dequantization of a per-output-column E4M3 base weight:
+    W0[r, c] = scale[c] * value(Wq[r, c])."""
+    return fp8_e4m3_decode(Wq) * np.asarray(scale, np.float64)[None, :]
+
+
+def requantize_fp8_per_col(W):
+    """Per-output-column E4M3 storage of a float weight (see above); the
+    division and the decision are taken in float32, the kernels' precision."""
+    W32 = np.asarray(W, dtype=np.float64).astype(np.float32)
+    amax = np.abs(W32).max(axis=0)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    codes = fp8_e4m3_encode((W32 / scale[None, :]).astype(np.float32))
+    return codes, scale
+
+
+def merge_xq(Wq, scale, q_r, q_p, perm_r, perm_p, b_r, b_p, fmt="i8"):
+    """Merge of a quantized base weight [XQ], [MG] (fmt "i8": int8 codes,
+    "f8": E4M3 code bytes). The page does not say how the merged weight is
+    stored again; reading: dequantize, W0 <- R W0 P in float64, then store
+    per output column as the input was stored. Returns (codes, scale, merged
+    float64 weight before storage)."""
+    deq, req = (dequantize_fp8, requantize_fp8_per_col) if fmt == "f8" else (dequantize, requantize_int8_per_col)
+    W = merge(deq(Wq, scale), q_r, q_p, perm_r, perm_p, b_r, b_p)
+    codes, new_scale = req(W)
     return codes, new_scale, W
 
 

@@ -18,14 +18,17 @@ so that each one can be regenerated on its own:
 Values are drawn in float32 and then rounded to the layer's storage type:
 bfloat16 by round-to-nearest-even of the float32 bits; int8 base weights by
 symmetric per-output-column absmax/127 quantisation with round-half-even and a
-clamp to [-127, 127] (the storage format the quantised variant starts from).
+clamp to [-127, 127] (the storage format the quantised variant starts from);
+fp8 base weights likewise per output column, scale absmax/448 and each value
+w / scale converted to the OCP E4M3 byte by torch's float8_e4m3fn conversion
+(round to nearest even).
 """
 
 from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["LayerConfig", "CONFIGS", "bf16_round", "bf16_bits", "from_bf16_bits",
-           "quantize_int8_per_col", "make_layer", "make_activations",
+           "quantize_int8_per_col", "quantize_fp8_per_col", "make_layer", "make_activations",
            "packed_count"]
 
 
@@ -39,7 +42,7 @@ class LayerConfig:
     b_r: int
     b_p: int
     act: str            # "f32" or "bf16"
-    weight: str         # "f32", "bf16" or "i8"
+    weight: str         # "f32", "bf16", "i8" or "f8" (E4M3 byte)
     merge: bool = False
     sigma_w: float = 0.02
     sigma_q: float = 1e-3
@@ -60,6 +63,7 @@ CONFIGS = {
         LayerConfig("llama13b_q_proj", 3, 2 * 2048, 5120, 5120, 512, 512, "bf16", "bf16"),
         LayerConfig("llama13b_down_proj", 4, 2 * 2048, 13824, 5120, 512, 512, "bf16", "bf16"),
         LayerConfig("xq_llama8b_mlp_up", 5, 4 * 2048, 4096, 14336, 256, 256, "bf16", "i8"),
+        LayerConfig("xf8_llama8b_mlp_up", 6, 4 * 2048, 4096, 14336, 256, 256, "bf16", "f8"),
     ]
 }
 
@@ -105,6 +109,21 @@ def quantize_int8_per_col(w):
     return q, scale
 
 
+def quantize_fp8_per_col(w):
+    """Per-column E4M3 storage: scale[c] = max_r |w[r, c]| / 448 in float32,
+    code = the E4M3 byte of w / scale (clamped to +-448 first: the float32
+    division can land just past it)."""
+    import torch
+
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=0)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    x = np.clip(w / scale[None, :], -448.0, 448.0).astype(np.float32)
+    q = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return q, scale
+
+
 def _draw(rng, shape, sigma):
     return (rng.standard_normal(shape, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
 
@@ -124,13 +143,14 @@ def make_layer(cfg, seed=0, m=None, n=None):
 
     Returns a dict. ``W0`` is the float32 value array (exactly representable in
     the storage type), ``W0_raw`` the storage array (float32, uint16 bfloat16
-    bits, or int8), ``w_scale`` the per-column scale for int8 (else None).
+    bits, int8, or uint8 E4M3 bytes), ``w_scale`` the per-column scale of an
+    int8 or fp8 weight (else None).
     """
     m = cfg.m if m is None else m
     n = cfg.n if n is None else n
     w = _draw(_rng(seed, cfg.cfg_id, 0), (m, n), cfg.sigma_w)
-    if cfg.weight == "i8":
-        wq, scale = quantize_int8_per_col(w)
+    if cfg.weight in ("i8", "f8"):
+        wq, scale = (quantize_int8_per_col if cfg.weight == "i8" else quantize_fp8_per_col)(w)
         # values are scale[c] * wq[r, c]; kept as (wq, scale) so that the
         # consumer forms the product in its own precision
         out = dict(W0_raw=wq, w_scale=scale, W0=None)

@@ -445,3 +445,67 @@ def test_merge_schedule_merges_after_every_interval_updates():
     due = [s for s in range(1000) if O.merge_due(s, 200)]
     assert due == [199, 399, 599, 799, 999]
     assert all(O.merge_due(s, 1) for s in range(10))
+
+
+# --- fp8 (E4M3) base weight -------------------------------------------------
+
+def test_fp8_decode_matches_published_values_and_torch():
+    g = _load("fp8_e4m3_published_values.txt")
+    assert np.array_equal(O.fp8_e4m3_decode(g[:, 0].astype(np.uint8)), g[:, 1])
+    assert np.isnan(O.fp8_e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    # every byte against torch's float8_e4m3fn (a library implementation of
+    # the same OCP format)
+    import torch
+
+    c = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    d = O.fp8_e4m3_decode(c)
+    assert np.array_equal(np.isnan(d), np.isnan(t))
+    assert np.array_equal(d[~np.isnan(d)], t[~np.isnan(t)])
+
+
+def test_fp8_encode_rounds_to_nearest_even_and_saturates():
+    import torch
+
+    vals = O.fp8_e4m3_values()
+    # every finite code back to itself; midpoints to the even neighbour
+    assert np.array_equal(O.fp8_e4m3_encode(vals), np.arange(127, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    assert np.array_equal(O.fp8_e4m3_encode(mids), (np.arange(126) + 1) // 2 * 2)
+    # hand-derived ties: 1.0625 halfway 1 (0x38) / 1.125 (0x39) -> 0x38;
+    # 1.1875 halfway 1.125 / 1.25 (0x3A) -> 0x3A; 2^-10 halfway 0 / 2^-9 -> 0
+    assert O.fp8_e4m3_encode([1.0625, 1.1875, 2.0 ** -10]).tolist() == [0x38, 0x3A, 0x00]
+    # saturation and signs
+    assert O.fp8_e4m3_encode([449.0, 1e9, -1e9, -1.0, -0.0]).tolist() == [0x7E, 0x7E, 0xFE, 0xB8, 0x80]
+    # random float32 values within range against torch's conversion
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 0.01,
+                        mids, -mids]).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_e4m3_encode(x), t)
+
+
+def test_fp8_requantize_and_merge():
+    W = np.random.default_rng(12).standard_normal((40, 24)) * 0.02
+    W[:, 3] = 0.0
+    codes, scale = O.requantize_fp8_per_col(W)
+    assert scale[3] == 1.0 and np.all(codes[:, 3] == 0)
+    # the column maximum takes the largest code; every value within half a
+    # code step (relative 2^-4 for normals, 2^-10 absolute on the code scale)
+    big = np.argmax(np.abs(W), axis=0)
+    for c in (0, 1, 5):
+        assert codes[big[c], c] & 0x7F == 0x7E
+    Wd = O.dequantize_fp8(codes, scale)
+    step = np.maximum(np.abs(W) / scale * 2.0 ** -4, 2.0 ** -10) * scale
+    assert np.all(np.abs(Wd - W) <= step * (1 + 1e-6))
+    # the synthetic fp8 weight is that storage of the drawn float weight
+    cfg = synth.CONFIGS["xf8_llama8b_mlp_up"]
+    L = synth.make_layer(cfg, 0, m=32, n=48)
+    c2, s2 = O.requantize_fp8_per_col(O.dequantize_fp8(L["W0_raw"], L["w_scale"]))
+    assert np.array_equal(c2, L["W0_raw"])
+    assert np.allclose(s2, L["w_scale"], rtol=2.0 ** -22, atol=0)
+    # merge with q = 0 keeps every code
+    zr, zp = np.zeros(O.packed_len(32, 16)), np.zeros(O.packed_len(48, 16))
+    pr, pp = np.random.default_rng(13).permutation(32), np.random.default_rng(14).permutation(48)
+    codes, scale, W = O.merge_xq(L["W0_raw"], L["w_scale"], zr, zp, pr, pp, 16, 16, fmt="f8")
+    assert np.array_equal(codes, L["W0_raw"])
