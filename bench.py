@@ -73,7 +73,10 @@ def cpu_baseline(cfg, budget_s=30.0):
     except OSError:  # pragma: no cover - informational only
         pass
     L = synth.make_layer(cfg, 0)
-    W0 = O.dequantize(L["W0_raw"], L["w_scale"]) if cfg.weight == "i8" else L["W0"].astype(np.float64)
+    if cfg.weight in ("i8", "f8"):
+        W0 = (O.dequantize if cfg.weight == "i8" else O.dequantize_fp8)(L["W0_raw"], L["w_scale"])
+    else:
+        W0 = L["W0"].astype(np.float64)
     args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
 
     def fwd_bwd(T):
@@ -89,8 +92,8 @@ def cpu_baseline(cfg, budget_s=30.0):
     t_merge = 0.0
     if cfg.merge:
         t0 = time.perf_counter()
-        if cfg.weight == "i8":
-            O.merge_xq(L["W0_raw"], L["w_scale"], *args[1:])
+        if cfg.weight in ("i8", "f8"):
+            O.merge_xq(L["W0_raw"], L["w_scale"], *args[1:], fmt=cfg.weight)
         else:
             O.merge(*args)
         t_merge = time.perf_counter() - t0
@@ -152,7 +155,7 @@ def algorithmic_work(cfg):
     shape: block-diagonal work only (never dense m x m or n x n rotations),
     one pass over each operand, one G plane per CNP block."""
     es = 4 if cfg.act == "f32" else 2
-    wes = {"f32": 4, "bf16": 2, "i8": 1}[cfg.weight]
+    wes = {"f32": 4, "bf16": 2, "i8": 1, "f8": 1}[cfg.weight]
     T, m, n, br, bp = cfg.T, cfg.m, cfg.n, cfg.b_r, cfg.b_p
     nr, np_ = -(-m // br), -(-n // bp)
     pr = nr * br * (br - 1) // 2
@@ -210,7 +213,8 @@ def kernel_roofline(cfg, per):
 
 # The other single-GPU workloads of the pages' Llama runs, timed as extra
 # lines of the same report (the tiny float32 layer is launch-bound and left out).
-OTHER_WORKLOADS = ("llama3b_proj", "llama13b_q_proj", "llama13b_down_proj", "xq_llama8b_mlp_up")
+OTHER_WORKLOADS = ("llama3b_proj", "llama13b_q_proj", "llama13b_down_proj", "xq_llama8b_mlp_up",
+                   "xf8_llama8b_mlp_up")
 
 
 def time_workload(cfg, steps, warmup):

@@ -28,10 +28,15 @@
  *    launched and no output is touched. POETX_EHIP reports a failed launch.
  *  - Element types: `act_dtype` (x, z, dz, dx, saved activations, the CNP
  *    block buffers) is POETX_F32 or POETX_BF16. `w_dtype` is POETX_F32 with
- *    F32 activations, POETX_BF16 or POETX_I8 with BF16 activations (I8 = int8
- *    weight with one float scale per output column: W0[r][c] = s[c] * q[r][c],
- *    the quantised-base-weight variant POET-XQ of section "POET-XQ").
- *  - Shapes: m, n, b_r, b_p multiples of 8; 8 <= b <= 1024; m, n <= 2^24;
+ *    F32 activations, POETX_BF16, POETX_I8 or POETX_F8 with BF16 activations
+ *    (I8 = int8 weight with one float scale per output column: W0[r][c] =
+ *    s[c] * q[r][c], the quantised-base-weight variant POET-XQ of section
+ *    "POET-XQ"; F8 = the same with q[r][c] an OCP E4M3 fp8 byte (sign, 4-bit
+ *    exponent with bias 7, 3-bit mantissa; largest finite 448; the NaN
+ *    bytes 0x7F / 0xFF are never stored), the lower-precision format the
+ *    section expects to work as well).
+ *  - Shapes: m, n, b_r, b_p multiples of 8 (m, n multiples of 16 for I8 and
+ *    of 64 for F8); 8 <= b <= 1024; m, n <= 2^24;
  *    ceil(m / b_r) + ceil(n / b_p) <= 65535 blocks; 0 <= T <= 2^30 tokens.
  *    Outside these the entry points return POETX_EINVAL and the size queries
  *    return 0.
@@ -66,7 +71,7 @@ enum {
   POETX_EWORKSPACE = 4     /* ws_bytes smaller than poetx_workspace_bytes() */
 };
 
-enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 };
+enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2, POETX_F8 = 3 };
 
 enum { POETX_SIDE_R = 0, POETX_SIDE_P = 1 };
 
@@ -88,7 +93,7 @@ typedef struct poetx_layer {
   int32_t b_r;        /* block size of R: ceil(m / b_r) blocks */
   int32_t b_p;        /* block size of P: ceil(n / b_p) blocks */
   int32_t act_dtype;  /* POETX_F32 or POETX_BF16 */
-  int32_t w_dtype;    /* POETX_F32, POETX_BF16 or POETX_I8 (see above) */
+  int32_t w_dtype;    /* POETX_F32, POETX_BF16, POETX_I8 or POETX_F8 (see above) */
 } poetx_layer;
 
 /* Version of this ABI (POETX_ABI_VERSION). */
@@ -140,7 +145,7 @@ POETX_API int poetx_cnp_build(const poetx_layer* L, const float* q_r, const floa
 
 /* Permuted-frame base weight from W0 in the original frame (loading a
  * weight or a checkpoint): wp = Psi W0 Phi^T, i.e. wp[i][c] =
- * w0[perm_r[i]][perm_p[c]] (m x n, w_dtype); for I8 also wscale_p[c] =
+ * w0[perm_r[i]][perm_p[c]] (m x n, w_dtype); for I8 and F8 also wscale_p[c] =
  * w_scale[perm_p[c]] (n floats; w_scale and wscale_p are ignored otherwise
  * and may be NULL). wp is the weight every other entry point takes: the
  * forward reads it N-contiguous, the backward K-contiguous, and poetx_merge
@@ -151,7 +156,7 @@ POETX_API int poetx_weight_prepare(const poetx_layer* L, const void* w0, const f
                          void* wp, float* wscale_p, hipStream_t stream);
 
 /* The inverse of poetx_weight_prepare, for checkpoints: w0[perm_r[i]][
- * perm_p[c]] = wp[i][c] (m x n, w_dtype) and, for I8, w_scale[perm_p[c]] =
+ * perm_p[c]] = wp[i][c] (m x n, w_dtype) and, for I8 and F8, w_scale[perm_p[c]] =
  * wscale_p[c]. ws: poetx_workspace_bytes(L, 0, POETX_OP_WEIGHT_EXPORT)
  * bytes (n int32). With q = 0 (right after a merge) the layer's function is
  * x -> x w0, whatever the permutations. */
@@ -164,12 +169,13 @@ POETX_API int poetx_weight_export(const poetx_layer* L, const void* wp, const fl
  *   x [T][m], act_dtype. z [T][n], act_dtype, overwritten.
  *   g_r, g_p: CNP block buffers from poetx_cnp_build.
  *   wp: permuted-frame weight (poetx_weight_prepare, poetx_merge);
- *   wscale_p: its column scales (I8 only, else ignored).
+ *   wscale_p: its column scales (I8 and F8 only, else ignored).
  *   saved: poetx_saved_bytes(L, T) bytes, overwritten with X1 and Y1.
- * An int8 weight is dequantised at run time (section "POET-XQ"): the dense
- * product turns its codes into bfloat16 (exact) on their way into on-chip
- * memory and applies the column scales in its epilogue; when m or n is not a
- * multiple of 64 the codes are first copied to bfloat16 in the workspace.
+ * An int8 or fp8 weight is dequantised at run time (section "POET-XQ"): the
+ * dense product turns its codes into bfloat16 (exact for both formats) on
+ * their way into on-chip memory and applies the column scales in its
+ * epilogue; for int8 with m or n not a multiple of 64 the codes are first
+ * copied to bfloat16 in the workspace.
  * T == 0 launches nothing. */
 POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
                   const int32_t* perm_r, const int32_t* perm_p,
@@ -184,10 +190,10 @@ POETX_API int poetx_forward(const poetx_layer* L, int64_t T, const void* x,
  *   q_r, q_p: the packed parameters the CNP buffers were built from.
  *   wp, wscale_p: the forward's permuted-frame weight (m x n).
  * No W0 gradient exists (W0 is frozen). Outputs are overwritten, not
- * accumulated; T == 0 writes zero gradients. When the weight is not int8 and
+ * accumulated; T == 0 writes zero gradients. When the weight is not I8 or F8 and
  * m < T, the P-side product dY1 = dY2 H^T is not formed: the dense product
  * takes dY2 and the weight Wp H (built in the workspace), which is the same
- * dX2 = dY2 H^T Wp^T with fewer bytes moved. For an int8 weight, dY1 takes the
+ * dX2 = dY2 H^T Wp^T with fewer bytes moved. For an I8 or F8 weight, dY1 takes the
  * column scales and the dense product reads Wp's codes, converting them to
  * bfloat16 (exact) itself. */
 POETX_API int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const void* dz,
@@ -233,13 +239,16 @@ POETX_API int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x,
  *   wp [m][n], w_dtype, in-out: in, the permuted-frame weight of perm_r,
  *       perm_p; out, Psi' R W0 P Phi'^T for Psi', Phi' of perm_r_next,
  *       perm_p_next (which may be perm_r, perm_p themselves: no new frame).
- *   wscale_p [n] float, int8 weights only, in-out: the column scales of wp.
- *       The merged weight is stored again the way W0 was (section "POET-XQ：
- *       量化训练的额外红利" stores the base weight quantized; how a merged
- *       weight is stored again is a reading): per column c, scale[c] =
- *       max_r |W0'[r][c]| / 127 (1 for a zero column) and code =
+ *   wscale_p [n] float, I8 and F8 weights only, in-out: the column scales
+ *       of wp. The merged weight is stored again the way W0 was (section
+ *       "POET-XQ：量化训练的额外红利" stores the base weight quantized; how a
+ *       merged weight is stored again is a reading): per column c, I8:
+ *       scale[c] = max_r |W0'[r][c]| / 127 (1 for a zero column) and code =
  *       clamp(rint(W0'[r][c] / scale[c]), -127, 127), rounding half to even
- *       in float32. The merge itself runs in float for int8 weights.
+ *       in float32; F8: scale[c] = max_r |W0'[r][c]| / 448 (1 for a zero
+ *       column) and code = the E4M3 byte nearest W0'[r][c] / scale[c]
+ *       (float32), ties to the even code, magnitudes past 448 saturated.
+ *       The merge itself runs in float for both.
  *   next_ready: NULL, or an event the stream waits for (hipStreamWaitEvent)
  *       after the block products and before perm_r_next / perm_p_next are
  *       read, so that their draw can run on another stream beside the block

@@ -332,12 +332,13 @@ __global__ void k_fill_zero2(float* p0, int64_t n0, float* p1, int64_t n1) {
   }
 }
 
-// ---- int8 base weight around a merge ----------------------------------------
-// out[r][c] = wq[r][c] * scale[cmap[c]] (cmap null: identity), 8 columns per
-// thread: 8-byte loads, 32-byte stores.
+// ---- quantized base weight around a merge ----------------------------------
+// out[r][c] = value(wq[r][c]) * scale[cmap[c]] (cmap null: identity), the
+// byte an int8 code or (fp8) an E4M3 code; 8 columns per thread: 8-byte
+// loads, 32-byte stores.
 __global__ void k_dequant_i8_cols(const int8_t* __restrict__ wq, const float* __restrict__ scale,
                                   const int32_t* __restrict__ cmap, float* __restrict__ out, int64_t rows,
-                                  int64_t cols) {
+                                  int64_t cols, int fp8) {
   const int64_t per_row = cols >> 3;
   POETX_GRID_STRIDE(g, rows * per_row) {  // g: 8-column group
     const int64_t r = g / per_row, c0 = (g % per_row) * 8;
@@ -355,8 +356,10 @@ __global__ void k_dequant_i8_cols(const int8_t* __restrict__ wq, const float* __
     }
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v[e] = static_cast<float>(static_cast<int8_t>((w[e >> 2] >> (8 * (e & 3))) & 0xffu)) * sc[e];
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t byte = (w[e >> 2] >> (8 * (e & 3))) & 0xffu;
+      v[e] = (fp8 ? e4m3_to_f32(byte) : static_cast<float>(static_cast<int8_t>(byte))) * sc[e];
+    }
     float4* o = reinterpret_cast<float4*>(out + r * cols + c0);
     o[0] = make_float4(v[0], v[1], v[2], v[3]);
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -403,11 +406,13 @@ __global__ void k_col_absmax(const float* __restrict__ w, int64_t rows, int64_t 
   atomicMax(amax + c, __float_as_uint(m));
 }
 
-// Per-column int8 storage: scale[c] = amax[c] / 127 (1 for a zero column),
-// wq = clamp(rint(w / scale), -127, 127), rint rounding half to even; the
-// division is the correctly rounded float32 one.
+// Per-column storage. int8: scale[c] = amax[c] / 127 (1 for a zero column),
+// wq = clamp(rint(w / scale), -127, 127), rint rounding half to even. fp8:
+// scale[c] = amax[c] / 448 (1 for a zero column), wq = the E4M3 byte of
+// w / scale. The division is the correctly rounded float32 one.
 __global__ void k_quant_i8_cols(const float* __restrict__ w, const unsigned int* __restrict__ amax,
-                                int8_t* __restrict__ wq, float* __restrict__ scale, int64_t rows, int64_t cols) {
+                                int8_t* __restrict__ wq, float* __restrict__ scale, int64_t rows, int64_t cols,
+                                int fp8) {
   const int64_t per_row = cols >> 3;
   POETX_GRID_STRIDE(g, rows * per_row) {  // g: 8-column group
     const int64_t r = g / per_row, c0 = (g % per_row) * 8;
@@ -415,11 +420,17 @@ __global__ void k_quant_i8_cols(const float* __restrict__ w, const unsigned int*
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int64_t c = c0 + e;
-      float sc = __uint_as_float(amax[c]) / 127.f;
+      float sc = __uint_as_float(amax[c]) / (fp8 ? 448.f : 127.f);
       sc = sc > 0.f ? sc : 1.f;
       if (r == 0) scale[c] = sc;
-      const float q = fminf(fmaxf(rintf(w[r * cols + c] / sc), -127.f), 127.f);
-      out[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu) << (8 * (e & 3));
+      uint32_t byte;
+      if (fp8) {
+        byte = f32_to_e4m3(w[r * cols + c] / sc);
+      } else {
+        const float q = fminf(fmaxf(rintf(w[r * cols + c] / sc), -127.f), 127.f);
+        byte = static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu;
+      }
+      out[e >> 2] |= byte << (8 * (e & 3));
     }
     *reinterpret_cast<uint2*>(wq + r * cols + c0) = make_uint2(out[0], out[1]);
   }
@@ -939,11 +950,11 @@ void gather_f32(const float* in, const int32_t* idx, float* out, int64_t n, hipS
 }
 
 bool dequant_i8_cols(const int8_t* wq, const float* scale, const int32_t* cmap, float* out, int64_t rows,
-                     int64_t cols, hipStream_t s) {
+                     int64_t cols, hipStream_t s, bool fp8) {
   if (rows <= 0 || cols <= 0) return true;
   if (cols % 8 != 0) return false;
   hipLaunchKernelGGL(k_dequant_i8_cols, dim3(grid1(rows * (cols / 8))), dim3(kThreads), 0, s, wq, scale, cmap, out,
-                     rows, cols);
+                     rows, cols, fp8 ? 1 : 0);
   return true;
 }
 
@@ -959,7 +970,7 @@ void bf16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t s) {
 }
 
 bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scale, int64_t rows, int64_t cols,
-                     hipStream_t s) {
+                     hipStream_t s, bool fp8) {
   if (rows <= 0 || cols <= 0) return true;
   if (cols % 8 != 0) return false;
   fill_zero_f32(reinterpret_cast<float*>(amax), cols, s);  // bit pattern 0 = +0.0
@@ -967,7 +978,7 @@ bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scal
   const dim3 g(static_cast<unsigned>((cols + kThreads - 1) / kThreads), grid_yz((rows + band - 1) / band));
   hipLaunchKernelGGL(k_col_absmax, g, dim3(kThreads), 0, s, w, rows, cols, band, amax);
   hipLaunchKernelGGL(k_quant_i8_cols, dim3(grid1(rows * (cols / 8))), dim3(kThreads), 0, s, w, amax, wq, scale,
-                     rows, cols);
+                     rows, cols, fp8 ? 1 : 0);
   return true;
 }
 

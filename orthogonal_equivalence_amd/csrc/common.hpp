@@ -31,6 +31,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// OCP E4M3 fp8 byte (sign, 4-bit exponent with bias 7, 3-bit mantissa; the
+// NaN bytes 0x7F / 0xFF are never stored here) in the low 8 bits of c, as a
+// float: v_cvt_f32_fp8 reads OCP E4M3 on gfx950 (checked against the format's
+// definition for all 256 bytes). Exact, and exact again in bfloat16.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
+}
+
+// float -> E4M3 byte: nearest value, ties to the even code, magnitudes past
+// 448 saturated to 448, the sign bit that of x. Below 2^-6 the steps are
+// 2^-9 (rintf: ties to even; 8 steps is the smallest normal); above, the
+// float's mantissa is rounded to 3 bits on its bits, the carry moving into
+// the exponent.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t mag;
+  if (a < 0x1p-6f) {
+    mag = static_cast<uint32_t>(rintf(a * 512.f));
+  } else {
+    const uint32_t u = __float_as_uint(a);
+    mag = ((u + 0x7ffffu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sgn | mag;
+}
+
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<float> {
   __device__ __forceinline__ static float load(const float* p) { return *p; }

@@ -42,6 +42,8 @@ struct GemmDesc {
   int store_full = 0;
   // 1: the dense W0 product (its own kernel symbol, so profiles separate it)
   int dense = 0;
+  // dense product with 1-byte B codes: 1 = OCP E4M3 fp8 bytes, 0 = int8
+  int b_fp8 = 0;
 };
 
 // Launch on `stream`. a_mode/b_mode/c_type select the kernel; returns false if

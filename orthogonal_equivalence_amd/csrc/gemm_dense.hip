@@ -35,7 +35,10 @@
 //    wave converts the chunks it loaded itself (no barrier needed) exactly to
 //    bfloat16 (|code| <= 127 has at most 8 significant bits) into the same
 //    LDS layouts as a bfloat16 B, K-contiguous or N-contiguous. The column
-//    scales are applied in the epilogue as for any scaled product.
+//    scales are applied in the epilogue as for any scaled product. An fp8 B
+//    (OCP E4M3 bytes, the same storage with 4-bit exponents) takes the same
+//    route with v_cvt_pk_f32_fp8 as the conversion (exact: 4 significant
+//    bits, exponents from 2^-9 to 2^8).
 //  * Output tiles are ordered so that each XCD works on one contiguous band
 //    of tiles (shared A/B panels stay in that XCD's L2).
 //  * Whole rounds of whole tiles with a K-contiguous B (the backward) run
@@ -217,6 +220,23 @@ __device__ __forceinline__ void i8x16_to_bf16(const uint4 raw, uint4& lo, uint4&
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Sixteen E4M3 fp8 codes as sixteen bfloat16 values (exact): v_cvt_pk_f32_fp8
+// turns two bytes of a word into two floats (OCP E4M3 on gfx950), whose low
+// 16 bits are zero.
+__device__ __forceinline__ void f8x16_to_bf16(const uint4 raw, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[q]), false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[q]), true);   // bytes 2, 3
+    o[2 * q] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    o[2 * q + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // int8 B tile: 16 KB of codes per stage, two 1 KB direct loads per wave.
 constexpr int kI8StageBytes = BN * BK;
 constexpr int kI8Chunks = kI8StageBytes / 1024 / (NT / 64);  // 2
@@ -261,8 +281,9 @@ __device__ __forceinline__ void kgroup_mfma(const char* st, int kk, const int (&
 }
 
 // BNC: B is N-contiguous (B[k * ldb + n]) instead of K-contiguous.
-// BI8: B holds int8 codes (ldb in elements = bytes).
-template <bool BNC, bool BI8>
+// BI8: B holds 1-byte codes (ldb in elements = bytes): int8, or with BF8
+// OCP E4M3 fp8 bytes.
+template <bool BNC, bool BI8, bool BF8 = false>
 __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tiles_m, int tiles_n, DenseSplit sp) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * kStageBytes + (BI8 ? 2 * kI8StageBytes : 0)];
   char* const i8st = smem + NSTAGE * kStageBytes;  // int8 staging (BI8 only)
@@ -377,7 +398,8 @@ __global__ void __launch_bounds__(NT, 1) k_gemm_dense(const GemmDesc d, int tile
 #pragma unroll
     for (int u = 0; u < kI8Chunks; ++u) {
       uint4 lo, hi;
-      i8x16_to_bf16(raw[u], lo, hi);
+      if constexpr (BF8) f8x16_to_bf16(raw[u], lo, hi);
+      else i8x16_to_bf16(raw[u], lo, hi);
       cv[u][0] = u32x4_t{lo.x, lo.y, lo.z, lo.w};
       cv[u][1] = u32x4_t{hi.x, hi.y, hi.z, hi.w};
     }
@@ -794,8 +816,13 @@ bool gemm_dense_bf16(const GemmDesc& d, void* split_ws, hipStream_t s, bool b_nc
   const int tail = p.tiles - p.full;
   const dim3 grid(p.full + tail * p.k);
   if (b_int8) {
-    if (b_ncontig) hipLaunchKernelGGL((k_gemm_dense<true, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
-    else hipLaunchKernelGGL((k_gemm_dense<false, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+    if (d.b_fp8) {
+      if (b_ncontig) hipLaunchKernelGGL((k_gemm_dense<true, true, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+      else hipLaunchKernelGGL((k_gemm_dense<false, true, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+    } else {
+      if (b_ncontig) hipLaunchKernelGGL((k_gemm_dense<true, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+      else hipLaunchKernelGGL((k_gemm_dense<false, true>), grid, dim3(NT), 0, s, d, tm, tn, sp);
+    }
   } else {
     if (b_ncontig) hipLaunchKernelGGL((k_gemm_dense<true, false>), grid, dim3(NT), 0, s, d, tm, tn, sp);
     else hipLaunchKernelGGL((k_gemm_dense<false, false>), grid, dim3(NT), 0, s, d, tm, tn, sp);

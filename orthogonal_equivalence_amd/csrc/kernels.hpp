@@ -88,19 +88,22 @@ void fill_zero_f32(float* p, int64_t n, hipStream_t stream);
 // p0[0, n0) and p1[0, n1) set to zero in one launch
 void fill_zero2_f32(float* p0, int64_t n0, float* p1, int64_t n1, hipStream_t stream);
 
-// int8 base weight around a merge (per-output-column scales):
-// out[r][c] = wq[r][c] * scale[cmap ? cmap[c] : c] as float (cols % 8 == 0);
+// Quantized base weight around a merge (per-output-column scales; the byte
+// codes int8, or OCP E4M3 fp8 with fp8):
+// out[r][c] = value(wq[r][c]) * scale[cmap ? cmap[c] : c] as float (cols % 8 == 0);
 bool dequant_i8_cols(const int8_t* wq, const float* scale, const int32_t* cmap, float* out, int64_t rows,
-                     int64_t cols, hipStream_t stream);
+                     int64_t cols, hipStream_t stream, bool fp8 = false);
 // out[i] = in[i] widened from bfloat16;
 void bf16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t stream);
 // out[i] = the int8 code in[i] as bfloat16 (exact), n % 8 == 0 (else false);
 bool i8_to_bf16(const int8_t* in, uint16_t* out, int64_t n, hipStream_t stream);
-// and the storage again: scale[c] = max_r |w[r][c]| / 127 (1 for a zero
-// column), wq = clamp(rint(w / scale), -127, 127); amax: cols words of
+// and the storage again: int8: scale[c] = max_r |w[r][c]| / 127 (1 for a
+// zero column), wq = clamp(rint(w / scale), -127, 127); fp8: scale[c] =
+// max_r |w[r][c]| / 448 (1 for a zero column), wq = the E4M3 byte of w /
+// scale (nearest, ties to even, saturated at 448); amax: cols words of
 // scratch (cols % 8 == 0).
 bool requant_i8_cols(const float* w, unsigned int* amax, int8_t* wq, float* scale, int64_t rows, int64_t cols,
-                     hipStream_t stream);
+                     hipStream_t stream, bool fp8 = false);
 
 // Skew blocks from packed parameters: Qf[z] (b x b, float) if Qf is not null
 // and a bfloat16 copy if Qh is not null. Blocks [0, n0) come from (q0, dim0), blocks

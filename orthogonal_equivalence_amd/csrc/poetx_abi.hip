@@ -69,6 +69,9 @@ bool layer_ok(const poetx_layer* L) {
   if (L->act_dtype == POETX_BF16) {
     if (L->w_dtype == POETX_BF16) return true;
     if (L->w_dtype == POETX_I8) return L->m % 16 == 0 && L->n % 16 == 0;
+    // fp8 codes are only read by the dense kernel, whose shape rules then
+    // hold for both products
+    if (L->w_dtype == POETX_F8) return L->m % 64 == 0 && L->n % 64 == 0;
   }
   return false;
 }
@@ -84,6 +87,9 @@ Side side_of(const poetx_layer* L, int side) {
 bool is_bf16(const poetx_layer* L) { return L->act_dtype == POETX_BF16; }
 int act_size(const poetx_layer* L) { return is_bf16(L) ? 2 : 4; }
 int w_size(const poetx_layer* L) { return L->w_dtype == POETX_F32 ? 4 : (L->w_dtype == POETX_BF16 ? 2 : 1); }
+// a 1-byte base weight with per-column scales: int8 codes or E4M3 fp8 bytes
+bool quantized(const poetx_layer* L) { return L->w_dtype == POETX_I8 || L->w_dtype == POETX_F8; }
+bool fp8_weight(const poetx_layer* L) { return L->w_dtype == POETX_F8; }
 int64_t block_elems(const Side& s) { return static_cast<int64_t>(s.nblk) * s.b * s.b; }
 int64_t packed_len(const Side& s) {
   const int64_t last = s.dim - static_cast<int64_t>(s.nblk - 1) * s.b;
@@ -251,7 +257,7 @@ struct BwdWs {
 // dX2 = dY2 H^T Wp^T = dY2 (Wp H)^T: with a float or bf16 weight and fewer
 // weight rows than tokens it is cheaper to multiply the m x n weight by H once
 // than the T x n gradient by H^T (dH only needs dY2 and Y1, never dY1).
-bool fold_h(const poetx_layer* L, int64_t T) { return L->w_dtype != POETX_I8 && L->m < T; }
+bool fold_h(const poetx_layer* L, int64_t T) { return !quantized(L) && L->m < T; }
 
 BwdWs plan_bwd(const poetx_layer* L, int64_t T, Carve& c) {
   BwdWs w;
@@ -290,7 +296,7 @@ struct MergeWs {
 
 MergeWs plan_merge(const poetx_layer* L, Carve& c) {
   MergeWs w;
-  const bool i8 = L->w_dtype == POETX_I8;
+  const bool i8 = quantized(L);
   const int64_t es = i8 ? 4 : w_size(L);
   w.C1 = c.take<char>(L->m * L->n * es);
   w.C2 = c.take<char>(L->m * L->n * es);
@@ -439,6 +445,7 @@ bool dense_product(const poetx_layer* L, const GemmDesc& d, bool i8, bool b_ncon
                    hipStream_t st) {
   if (i8 ? dense_i8_applies(L, d.N, d.K, d.ldb) : dense_kernel_applies(L, d.N, d.K))
     return gemm_dense_bf16(d, split_ws, st, b_ncontig, i8);
+  if (i8 && d.b_fp8) return false;  // (the layer's shape rules keep fp8 on the dense kernel)
   if (b_ncontig) return !i8 && gemm(L, d, A_KCONTIG, B_NCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
   return gemm(L, d, A_KCONTIG, i8 ? B_KCONTIG_I8 : B_KCONTIG, is_bf16(L) ? C_BF16 : C_F32, st);
 }
@@ -725,7 +732,7 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
                   void* Y1, const FwdWs& w, bool recompute, hipStream_t stream) {
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
   const int es = act_size(L);
-  const bool i8 = L->w_dtype == POETX_I8;
+  const bool i8 = quantized(L);
   bool ok;
   {
     ProfScope p(recompute ? "recompute_gather_x" : "gather_x", stream);
@@ -738,6 +745,7 @@ bool forward_core(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   // Y1 = X2 Wp with Wp read as B[k][n] (N-contiguous)
   GemmDesc d;
   d.dense = 1;
+  d.b_fp8 = fp8_weight(L);
   d.A = w.buf;
   d.lda = L->m;
   d.B = wp;
@@ -776,7 +784,7 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
                    const void* g_r, const void* g_p, const void* wp, const float* wscale_p, float* dq_r,
                    float* dq_p, void* dx, const BwdWs& w, void* cnp_ws, hipStream_t stream) {
   const Side R = side_of(L, POETX_SIDE_R), P = side_of(L, POETX_SIDE_P);
-  const bool i8 = L->w_dtype == POETX_I8;
+  const bool i8 = quantized(L);
   const int es = act_size(L);
   // P side: dY2 = dZ Phi^T, dH = sum_t Y1^T dY2, and either dY1 = dY2 H^T
   // (times the column scales for int8 weights, which belong to Wp's columns)
@@ -798,6 +806,7 @@ bool backward_core(const poetx_layer* L, int64_t T, const void* X1, const void* 
   // the end, and the [T][m] results use bufB and bufC
   GemmDesc d;
   d.dense = 1;
+  d.b_fp8 = fp8_weight(L);
   void* dX1;
   if (fold) {
     ProfScope p("fold_h_bwd", stream);
@@ -999,7 +1008,7 @@ int poetx_weight_prepare(const poetx_layer* L, const void* w0, const float* w_sc
                          const int32_t* perm_p, void* wp, float* wscale_p, hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
   if (!ptrs_ok({w0, perm_r, perm_p, wp})) return POETX_EINVAL;
-  const bool i8 = L->w_dtype == POETX_I8;
+  const bool i8 = quantized(L);
   if (i8 && !ptrs_ok({w_scale, wscale_p})) return POETX_EINVAL;
   clear_pending_error();
   {
@@ -1016,7 +1025,7 @@ int poetx_weight_export(const poetx_layer* L, const void* wp, const float* wscal
                         hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
   if (!ptrs_ok({wp, perm_r, perm_p, w0})) return POETX_EINVAL;
-  const bool i8 = L->w_dtype == POETX_I8;
+  const bool i8 = quantized(L);
   if (i8 && !ptrs_ok({wscale_p, w_scale})) return POETX_EINVAL;
   if (const int e = check_ws(L, 0, POETX_OP_WEIGHT_EXPORT, ws, ws_bytes)) return e;
   clear_pending_error();
@@ -1038,7 +1047,7 @@ int poetx_forward(const poetx_layer* L, int64_t T, const void* x, const int32_t*
   if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
   if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wp, z, saved})) return POETX_EINVAL;
-  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (quantized(L) && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_FORWARD, ws, ws_bytes)) return e;
   clear_pending_error();
   Carve c(ws);
@@ -1056,7 +1065,7 @@ int poetx_forward_mem(const poetx_layer* L, int64_t T, const void* x, const int3
   if (!layer_ok(L) || !tokens_ok(T)) return POETX_EINVAL;
   if (T == 0) return POETX_OK;
   if (!ptrs_ok({x, perm_r, perm_p, g_r, g_p, wp, z})) return POETX_EINVAL;
-  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (quantized(L) && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_FORWARD_MEM, ws, ws_bytes)) return e;
   clear_pending_error();
   Carve c(ws);
@@ -1081,7 +1090,7 @@ int poetx_backward(const poetx_layer* L, int64_t T, const void* saved, const voi
     return launch_status();
   }
   if (!ptrs_ok({saved, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, dx})) return POETX_EINVAL;
-  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (quantized(L) && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_BACKWARD, ws, ws_bytes)) return e;
   Carve c(ws);
   const BwdWs w = plan_bwd(L, T, c);
@@ -1107,7 +1116,7 @@ int poetx_backward_mem(const poetx_layer* L, int64_t T, const void* x, const voi
     return launch_status();
   }
   if (!ptrs_ok({x, dz, perm_r, perm_p, q_r, q_p, g_r, g_p, wp, dx})) return POETX_EINVAL;
-  if (L->w_dtype == POETX_I8 && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
+  if (quantized(L) && (!wscale_p || !aligned16(wscale_p))) return POETX_EINVAL;
   if (const int e = check_ws(L, T, POETX_OP_BACKWARD_MEM, ws, ws_bytes)) return e;
   Carve c(ws);
   char* X1 = c.take<char>(saved_region(L, T));
@@ -1131,7 +1140,7 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
                 const void* g_p, float* q_r, float* q_p, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!layer_ok(L)) return POETX_EINVAL;
   if (!ptrs_ok({wp, perm_r, perm_p, perm_r_next, perm_p_next, g_r, g_p, q_r, q_p})) return POETX_EINVAL;
-  const bool i8 = L->w_dtype == POETX_I8;
+  const bool i8 = quantized(L);
   if (i8 && !ptrs_ok({wscale_p})) return POETX_EINVAL;
   if (const int e = check_ws(L, 0, POETX_OP_MERGE, ws, ws_bytes)) return e;
   clear_pending_error();
@@ -1177,7 +1186,7 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     {
       ProfScope p("merge_dequant", stream);
       ok = dequant_i8_cols(static_cast<const int8_t*>(wp), wscale_p, nullptr, static_cast<float*>(w.C1), L->m,
-                           L->n, stream);
+                           L->n, stream, fp8_weight(L));
       bf16_to_f32(static_cast<const uint16_t*>(g_r), w.gr32, 2 * block_elems(R), stream);
       bf16_to_f32(static_cast<const uint16_t*>(g_p), w.gp32, 2 * block_elems(P), stream);
     }
@@ -1203,7 +1212,7 @@ int poetx_merge(const poetx_layer* L, void* wp, float* wscale_p, const int32_t* 
     {
       ProfScope p("merge_requant", stream);
       ok = ok && requant_i8_cols(static_cast<const float*>(w.C2), w.amax, static_cast<int8_t*>(wp), wscale_p, L->m,
-                                 L->n, stream);
+                                 L->n, stream, fp8_weight(L));
     }
     if (wait_status) return wait_status;
     if (!ok) return POETX_EUNSUPPORTED;

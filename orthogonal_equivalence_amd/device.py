@@ -14,7 +14,8 @@ import torch
 
 from . import poetx as px
 
-_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "f8": torch.uint8}
+_QUANTIZED = ("i8", "f8")  # 1-byte codes with per-column scales
 
 
 def to_device(arr, kind, device="cuda"):
@@ -22,6 +23,8 @@ def to_device(arr, kind, device="cuda"):
     arr = np.ascontiguousarray(arr)
     if kind == "bf16":
         return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    if kind == "f8":
+        return torch.from_numpy(arr.astype(np.uint8)).to(device)
     if kind == "i8":
         return torch.from_numpy(arr.astype(np.int8)).to(device)
     if kind == "i32":
@@ -51,7 +54,7 @@ class DeviceLayer:
         u8 = torch.uint8
         # Psi W0 Phi^T, and for an int8 weight the scales of its columns
         self.wp = torch.empty((m, n), dtype=_TORCH[weight], device=dev)
-        self.wscale_p = torch.ones(n, dtype=torch.float32, device=dev) if weight == "i8" else None
+        self.wscale_p = torch.ones(n, dtype=torch.float32, device=dev) if weight in _QUANTIZED else None
         self.perm_r = torch.arange(m, dtype=torch.int32, device=dev)
         self.perm_p = torch.arange(n, dtype=torch.int32, device=dev)
         self.q_r = torch.zeros(px.poetx_packed_len(self.L, px.POETX_SIDE_R), dtype=torch.float32, device=dev)
@@ -89,19 +92,19 @@ class DeviceLayer:
         self.q_r.copy_(to_device(layer["q_r"], "f32", self.device))
         self.q_p.copy_(to_device(layer["q_p"], "f32", self.device))
         w0 = to_device(layer["W0_raw"], self.weight, self.device)
-        scale = to_device(layer["w_scale"], "f32", self.device) if self.weight == "i8" else None
+        scale = to_device(layer["w_scale"], "f32", self.device) if self.weight in _QUANTIZED else None
         self.set_weight(w0, scale, stream)
 
     def set_weight(self, w0, w_scale=None, stream=None):
         """Permuted-frame weight from W0 [m][n] in the original frame (and its
-        column scales for an int8 weight), for the current permutations."""
+        column scales for an int8 or fp8 weight), for the current permutations."""
         px.poetx_weight_prepare(self.L, w0, w_scale, self.perm_r, self.perm_p, self.wp, self.wscale_p, stream)
 
     def export_w0(self, stream=None):
-        """W0 in the original frame (and, for an int8 weight, its column
+        """W0 in the original frame (and, for an int8 or fp8 weight, its column
         scales), e.g. for a checkpoint. Returns (w0, w_scale or None)."""
         w0 = torch.empty((self.m, self.n), dtype=_TORCH[self.weight], device=self.device)
-        scale = torch.empty(self.n, dtype=torch.float32, device=self.device) if self.weight == "i8" else None
+        scale = torch.empty(self.n, dtype=torch.float32, device=self.device) if self.weight in _QUANTIZED else None
         px.poetx_weight_export(self.L, self.wp, self.wscale_p, self.perm_r, self.perm_p, w0, scale, self.ws, None,
                                stream)
         return w0, scale

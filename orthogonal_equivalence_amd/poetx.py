@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 POETX_OK, POETX_EINVAL, POETX_EUNSUPPORTED, POETX_EHIP, POETX_EWORKSPACE = 0, 1, 2, 3, 4
-POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
+POETX_F32, POETX_BF16, POETX_I8, POETX_F8 = 0, 1, 2, 3
 POETX_SIDE_R, POETX_SIDE_P = 0, 1
 (POETX_OP_CNP_BUILD, POETX_OP_WEIGHT_PREPARE, POETX_OP_FORWARD, POETX_OP_BACKWARD,
  POETX_OP_MERGE, POETX_OP_FORWARD_MEM, POETX_OP_BACKWARD_MEM, POETX_OP_SAMPLE_PERM,
@@ -38,7 +38,7 @@ EXPORTED = [
     "poetx_profile_enable", "poetx_profile_count", "poetx_profile_get",
 ]
 
-_DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
+_DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8, "f8": POETX_F8}
 
 
 class poetx_layer(ctypes.Structure):

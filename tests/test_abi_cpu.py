@@ -65,6 +65,8 @@ def test_sizes_match_block_structure(m, n, b_r, b_p):
     assert px.poetx_saved_bytes(Lf, 3) == 3 * (m + n) * 4
     Lq = px.make_layer(m, n, b_r, b_p, "bf16", "i8")
     assert px.poetx_wbuf_bytes(Lq) == (m * n if m % 16 == 0 and n % 16 == 0 else 0)
+    L8 = px.make_layer(m, n, b_r, b_p, "bf16", "f8")
+    assert px.poetx_wbuf_bytes(L8) == (m * n if m % 64 == 0 and n % 64 == 0 else 0)
     for op in range(5):
         assert px.poetx_workspace_bytes(L, 4096, op) >= 0
     assert px.poetx_workspace_bytes(L, 4096, px.POETX_OP_FORWARD) >= 4096 * max(m, n) * 2
@@ -78,6 +80,8 @@ def test_sizes_match_block_structure(m, n, b_r, b_p):
     dict(m=16, n=16, b_r=8, b_p=8, act="f32", weight="bf16"),
     dict(m=16, n=16, b_r=8, b_p=8, act="f32", weight="i8"),
     dict(m=24, n=32, b_r=8, b_p=8, act="bf16", weight="i8"),   # int8 rows need 16-byte multiples
+    dict(m=16, n=16, b_r=8, b_p=8, act="f32", weight="f8"),
+    dict(m=64, n=96, b_r=8, b_p=8, act="bf16", weight="f8"),   # fp8 widths need multiples of 64
     dict(m=(1 << 24) + 8, n=16, b_r=1024, b_p=8),               # more than 2^24 features
     dict(m=8 * 65535, n=8, b_r=8, b_p=8),                       # 65536 blocks over the two sides
 ])
@@ -180,10 +184,11 @@ def test_argument_errors_before_any_launch():
     with pytest.raises(px.PoetxError) as e:
         px.poetx_merge(Lq, *margs, FAKE, ws_m, stream=0)
     assert e.value.status == px.POETX_EINVAL
-    # int8 weights need their scales
-    with pytest.raises(px.PoetxError) as e:
-        px.poetx_weight_prepare(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
-    assert e.value.status == px.POETX_EINVAL
+    # int8 and fp8 weights need their scales
+    for Lw in (Lq, px.make_layer(64, 64, 16, 16, "bf16", "f8")):
+        with pytest.raises(px.PoetxError) as e:
+            px.poetx_weight_prepare(Lw, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
+        assert e.value.status == px.POETX_EINVAL
     with pytest.raises(px.PoetxError) as e:
         px.poetx_weight_export(Lq, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, stream=0)
     assert e.value.status == px.POETX_EINVAL

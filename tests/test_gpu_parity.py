@@ -43,6 +43,8 @@ def _cfg(name, T, m, n, b_r, b_p, act, weight, cfg_id):
 def _w0_values(cfg, L):
     if cfg.weight == "i8":
         return O.dequantize(L["W0_raw"], L["w_scale"])
+    if cfg.weight == "f8":
+        return O.dequantize_fp8(L["W0_raw"], L["w_scale"])
     return L["W0"].astype(np.float64)
 
 
@@ -106,6 +108,8 @@ SMALL = [
     _cfg("bf16_b32_b64", 130, 256, 192, 32, 64, "bf16", "bf16", 24),
     # int8 base weight with per-column scales
     _cfg("xq_small", 520, 512, 768, 128, 128, "bf16", "i8", 25),
+    # fp8 (E4M3) base weight with per-column scales
+    _cfg("xf8_small", 520, 512, 768, 128, 128, "bf16", "f8", 66),
     # a single token
     _cfg("bf16_one_token", 1, 256, 512, 128, 128, "bf16", "bf16", 26),
     # float32 with more tokens than weight rows: the backward folds H into the weight
@@ -131,6 +135,7 @@ SMALL = [
     # the same with an int8 weight: codes converted to bfloat16 inside the
     # dense kernel, column scales in the split sum's epilogue
     _cfg("xq_split_k", 300, 2048, 2304, 256, 256, "bf16", "i8", 39),
+    _cfg("xf8_split_k", 300, 2048, 2304, 256, 256, "bf16", "f8", 67),
     # one block per side: R's block size exceeds m (a single short block of
     # 64), P is exactly one block
     _cfg("f32_single_block", 50, 64, 128, 128, 128, "f32", "f32", 47),
@@ -168,7 +173,7 @@ SMALL = [
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_layer_parity(cfg):
-    L, A, out, _ = _run(cfg, merge=(cfg.weight != "i8"))
+    L, A, out, _ = _run(cfg, merge=(cfg.weight not in ("i8", "f8")))
     W0 = _w0_values(cfg, L)
     args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
     ref = O.backward(A["X"], A["dZ"], *args)
@@ -409,7 +414,8 @@ def test_token_shard_linearity():
 # full-size workloads, sampled outputs
 # ---------------------------------------------------------------------------
 
-FULL = ["llama3b_proj", "llama8b_mlp_up", "llama13b_q_proj", "llama13b_down_proj", "xq_llama8b_mlp_up"]
+FULL = ["llama3b_proj", "llama8b_mlp_up", "llama13b_q_proj", "llama13b_down_proj", "xq_llama8b_mlp_up",
+        "xf8_llama8b_mlp_up"]
 
 
 @pytest.mark.parametrize("name", FULL)
