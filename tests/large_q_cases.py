@@ -34,4 +34,6 @@ CASES = [
     (_c("q_bf16_b96_strong", 69, 200, 480, 600, 96, "bf16", "bf16", 0.043), "strong"),
     # int8 base weight, fused block products
     (_c("q_xq_b128_strong", 70, 400, 512, 768, 128, "bf16", "i8", 0.037), "strong"),
+    # fp8 (E4M3) base weight, fused block products
+    (_c("q_xf8_b128_strong", 71, 400, 512, 768, 128, "bf16", "f8", 0.037), "strong"),
 ]

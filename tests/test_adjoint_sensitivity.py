@@ -49,6 +49,8 @@ def _recurrence(Q, U, drop=None):
 def _w0(cfg, L):
     if cfg.weight == "i8":
         return O.dequantize(L["W0_raw"], L["w_scale"])
+    if cfg.weight == "f8":
+        return O.dequantize_fp8(L["W0_raw"], L["w_scale"])
     return L["W0"].astype(np.float64)
 
 

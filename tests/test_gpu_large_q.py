@@ -71,7 +71,7 @@ def test_large_rotation_parity(cfg, strength):
           f"sigma_q={cfg.sigma_q}", flush=True)
     L = synth.make_layer(cfg, 0)
     A = synth.make_activations(cfg, 0)
-    merge = cfg.weight != "i8"
+    merge = cfg.weight not in ("i8", "f8")
     dl = DeviceLayer(cfg.m, cfg.n, cfg.b_r, cfg.b_p, cfg.act, cfg.weight, cfg.T)
     dl.load(L)
     dl.cnp_build()
@@ -84,7 +84,10 @@ def test_large_rotation_parity(cfg, strength):
         got["w0"] = to_host_f64(dl.export_w0()[0])
     torch.cuda.synchronize()
 
-    W0 = O.dequantize(L["W0_raw"], L["w_scale"]) if cfg.weight == "i8" else L["W0"].astype(np.float64)
+    if cfg.weight in ("i8", "f8"):
+        W0 = (O.dequantize if cfg.weight == "i8" else O.dequantize_fp8)(L["W0_raw"], L["w_scale"])
+    else:
+        W0 = L["W0"].astype(np.float64)
     args = (W0, L["q_r"], L["q_p"], L["perm_r"], L["perm_p"], cfg.b_r, cfg.b_p)
     ref = O.backward(A["X"], A["dZ"], *args)
     XW = A["X"].astype(np.float64) @ W0

@@ -49,6 +49,8 @@ CASES = [
     _cfg("mem_split_k", 300, 2048, 2304, 256, 256, "bf16", "bf16", 45),
     # the same with an int8 weight (its bfloat16 code copy is workspace too)
     _cfg("mem_xq_split_k", 300, 2048, 2304, 256, 256, "bf16", "i8", 46),
+    # fp8 (E4M3) weight with per-column scales
+    _cfg("mem_xf8", 300, 512, 768, 128, 128, "bf16", "f8", 47),
 ]
 
 
