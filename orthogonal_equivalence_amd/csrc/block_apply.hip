@@ -8,15 +8,17 @@
 // gfx950 design: one workgroup owns one block and a contiguous run of
 // tokens. Each of its b/32 waves keeps its 32 output columns of B_j resident
 // in registers as MFMA fragments for the whole run, so B_j is read once per
-// workgroup (in whole rows through LDS before the first sub-tile). A 512 x 512 plane would fill a CU's whole register file, so for
-// b = 512 two workgroups share a block and a token run, each owning 256 of
-// its output columns (8 waves of 128 fragment registers) and staging the
-// full 512-column input; the two are issued 8 workgroups apart so that they
-// land on the same XCD and the second read of the input hits its L2. 32-token sub-tiles stream global -> LDS with
-// global_load_lds_dwordx4 into two swizzled stages (the next sub-tile is in
-// flight while the current one is multiplied); v_mfma_f32_32x32x16_bf16 does
-// the product; a per-wave LDS slab turns the accumulator into rows, where the
-// residual (from the staged input) is added and 16-byte stores go out.
+// workgroup (in whole rows through LDS before the first sub-tile). A 512 x
+// 512 plane would fill a CU's whole register file, so for b = 512 two
+// workgroups share a block and a token run, each owning 256 of its output
+// columns (8 waves of 128 fragment registers) and staging the full
+// 512-column input; the two are issued 8 workgroups apart so that they land
+// on the same XCD and the second read of the input hits its L2. 32-token
+// sub-tiles stream global -> LDS with global_load_lds_dwordx4 into two
+// swizzled stages (the next sub-tile is in flight while the current one is
+// multiplied); v_mfma_f32_32x32x16_bf16 does the product; a per-wave LDS
+// slab turns the accumulator into rows, where the residual (from the staged
+// input) is added and 16-byte stores go out.
 #include "common.hpp"
 #include "kernels.hpp"
 
